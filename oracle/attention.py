@@ -1,0 +1,162 @@
+"""Reference tree-masked softmax attention in float64.
+
+TEST INFRASTRUCTURE (see ``oracle/__init__``): never imported by the product path.
+
+What is computed ([PTP] attention-mask passage; [AOM] "How do we implement shared
+prefix?": tokens attend to the shared prefix while sibling rollouts stay isolated), for
+query head h, key/value head g = h // (h_q // h_kv), inputs upcast exactly to float64:
+
+  s_ij   = scale * <q[i, h], k[j, g]>                for j in anc*(i)
+  m_i    = max_j s_ij,   l_i = sum_j exp(s_ij - m_i)
+  O[i,h] = sum_j exp(s_ij - m_i) v[j, g] / l_i
+  LSE[h, i] = m_i + ln(l_i)                           (natural log, reading R6)
+
+Pads see nothing: O = 0 and LSE = -inf there (reading R7).  Pad Q/K/V contents never
+enter any result.
+
+Two implementations of the same definition:
+  * ``attention_brute`` / ``attention_at``: token by token over the parent walk anc*(i);
+  * ``attention_segment_blocked``: per segment, the keys are all tokens of the segment's
+    ancestor segments followed by the segment's own tokens under a causal mask — the
+    "one fully visible block per ancestor segment plus a causal triangle over its own
+    segment" decomposition of [PTP]'s mask passage.  It is the fast path used for whole
+    rows and for CPU timing; tests cross-check the two on random forests.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .mask import PAD, ancestors, row_parents
+
+
+def _get(inp, k):
+    return inp[k] if isinstance(inp, dict) else getattr(inp, k)
+
+
+def _f64(inp, name, idx=None):
+    """Rows of Q/K/V upcast exactly to float64 (bf16 bit patterns or float32)."""
+    a = _get(inp, name)
+    if idx is not None:
+        a = a[idx]
+    if _get(inp, "dtype") == "bf16":
+        a = (np.asarray(a, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return np.asarray(a, np.float64)
+
+
+def _softmax_rows(s):
+    """Row softmax pieces over the last axis: (m, l, p) with p = exp(s - m)."""
+    m = s.max(axis=-1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=-1, keepdims=True)
+    return m[..., 0], l[..., 0], p
+
+
+def _attend(qi, kk, vv, scale, G):
+    """One query position, all heads.  qi [Hq, D]; kk, vv [n, Hkv, D]."""
+    Hq, D = qi.shape
+    Hkv = kk.shape[1]
+    q3 = qi.reshape(Hkv, G, D)
+    s = scale * np.einsum("hgd,nhd->hgn", q3, kk)
+    m, l, p = _softmax_rows(s)
+    o = np.einsum("hgn,nhd->hgd", p, vv) / l[..., None]
+    return o.reshape(Hq, D), (m + np.log(l)).reshape(Hq)
+
+
+def attention_at(inp, samples):
+    """O and LSE at chosen (row, position) pairs, all heads, by the token parent walk.
+
+    Returns (O [n, Hq, D], LSE [n, Hq]) in float64.
+    """
+    Hq, Hkv = int(_get(inp, "h_q")), int(_get(inp, "h_kv"))
+    D, scale = int(_get(inp, "head_dim")), float(_get(inp, "scale"))
+    G = Hq // Hkv
+    O = np.zeros((len(samples), Hq, D))
+    L = np.full((len(samples), Hq), -np.inf)
+    cache = {}
+    for n, (r, i) in enumerate(samples):
+        if r not in cache:
+            cache = {r: row_parents(inp, r)}
+        pi = cache[r]
+        anc = ancestors(pi, int(i))
+        if len(anc) == 0:
+            continue
+        qi = _f64(inp, "q", (r, int(i)))
+        kk = _f64(inp, "k", (r, anc))
+        vv = _f64(inp, "v", (r, anc))
+        O[n], L[n] = _attend(qi, kk, vv, scale, G)
+    return O, L
+
+
+def attention_brute(inp):
+    """Whole-input O [R, T, Hq, D] and LSE [R, Hq, T] by the token parent walk (tiny inputs)."""
+    R, T = int(_get(inp, "n_rows")), int(_get(inp, "row_len"))
+    Hq, D = int(_get(inp, "h_q")), int(_get(inp, "head_dim"))
+    samples = [(r, i) for r in range(R) for i in range(T)]
+    O, L = attention_at(inp, samples)
+    return O.reshape(R, T, Hq, D), L.reshape(R, T, Hq).transpose(0, 2, 1).copy()
+
+
+def segment_ancestors(seg_parent, s):
+    """Ancestor segments of s from the root down (excluding s), by walking parents."""
+    chain = []
+    p = int(seg_parent[s])
+    while p >= 0:
+        chain.append(p)
+        p = int(seg_parent[p])
+    return chain[::-1]
+
+
+def attention_segment_blocked(inp, rows=None, dtype=np.float64):
+    """Whole rows by the segment decomposition; returns O [R, T, Hq, D], LSE [R, Hq, T].
+
+    ``dtype`` is the arithmetic type (float64 for parity; the CPU baseline times it as is).
+    """
+    R, T = int(_get(inp, "n_rows")), int(_get(inp, "row_len"))
+    Hq, Hkv = int(_get(inp, "h_q")), int(_get(inp, "h_kv"))
+    D, scale = int(_get(inp, "head_dim")), float(_get(inp, "scale"))
+    G = Hq // Hkv
+    rows = range(R) if rows is None else rows
+    rp = _get(inp, "seg_row_ptr")
+    O = np.zeros((R, T, Hq, D), dtype)
+    L = np.full((R, Hq, T), -np.inf, dtype)
+    for r in rows:
+        a, b = int(rp[r]), int(rp[r + 1])
+        st = _get(inp, "seg_start")[a:b]
+        ln = _get(inp, "seg_len")[a:b]
+        par = _get(inp, "seg_parent")[a:b]
+        if b == a:
+            continue
+        q = _f64(inp, "q", r).astype(dtype)
+        k = _f64(inp, "k", r).astype(dtype)
+        v = _f64(inp, "v", r).astype(dtype)
+        for s in range(b - a):
+            own = np.arange(st[s], st[s] + ln[s])
+            keys = np.concatenate([np.arange(st[p], st[p] + ln[p]) for p in segment_ancestors(par, s)]
+                                  + [own])
+            n_anc = len(keys) - len(own)
+            # visible[a, c]: own query a sees key c if c is an ancestor-segment key or an
+            # own key at or before a.
+            vis = np.ones((len(own), len(keys)), bool)
+            vis[:, n_anc:] = np.tril(np.ones((len(own), len(own)), bool))
+            for g in range(Hkv):
+                qg = q[own][:, g * G:(g + 1) * G, :]                    # [n, G, D]
+                kg = k[keys, g, :]                                       # [m, D]
+                vg = v[keys, g, :]
+                S = scale * np.matmul(qg, kg.T)                          # [n, G, m]
+                S = np.where(vis[:, None, :], S, -np.inf)
+                m = S.max(axis=-1, keepdims=True)
+                P = np.exp(S - m)
+                l = P.sum(axis=-1, keepdims=True)
+                lo, hi = int(st[s]), int(st[s] + ln[s])
+                O[r, lo:hi, g * G:(g + 1) * G, :] = np.matmul(P, vg) / l
+                L[r, g * G:(g + 1) * G, lo:hi] = (m + np.log(l))[..., 0].T
+    return O, L
+
+
+def real_positions(inp):
+    """Boolean [R, T]: True where the position holds a real token (by the parent walk)."""
+    R, T = int(_get(inp, "n_rows")), int(_get(inp, "row_len"))
+    out = np.zeros((R, T), bool)
+    for r in range(R):
+        out[r] = row_parents(inp, r) != PAD
+    return out
