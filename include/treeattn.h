@@ -1,0 +1,202 @@
+/*
+ * treeattn.h — C ABI of libtreeattn.so: prefix-tree packing and tree-masked attention
+ * forward for AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and passage:
+ *   [PTP]   "Prefix tree packing", furtherai.github.io/blog/posts/prefix-tree-packing
+ *   [AReaL] "How to Configure Sequence Packing for Efficient GPU Utilization in AReaL"
+ *   [AOM]   "ART-Optimized Megatron (AOM): 12x higher training throughput" (CoreWeave)
+ *
+ * Two halves:
+ *   1. Host planning over integers only ([PTP] integer-planning passage): tree_pack_plan
+ *      builds the radix segment tree, packs its leaves into fixed-length rows and emits
+ *      the per-row segment/parent table, position ids and a gather map.
+ *   2. Device attention: tree_attn_plan turns a segment table (device copy) into tile
+ *      lists once per batch ([PTP] mask passage: most blocks of a packed row are empty and
+ *      skipped; [AReaL] "Lazy Block Mask Conversion"), and tree_attn_fwd runs the masked
+ *      attention forward on Q/K/V, reusing that plan for every layer.
+ *
+ * Conventions.
+ *   - Every call returns int32: TREE_OK (0) or a negative TREE_E_* code;
+ *     tree_status_str(code) gives a static text.
+ *   - Argument errors are detected and returned synchronously, before any launch.
+ *   - The library never allocates device memory and holds no global mutable state; the
+ *     caller owns every device buffer (inputs, outputs, workspace).  The host plan is
+ *     library-owned until tree_plan_free.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device calls
+ *     are asynchronous on that stream unless stated otherwise.
+ */
+#ifndef TREEATTN_H
+#define TREEATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    TREE_OK = 0,
+    TREE_E_INVAL = -1,        /* bad argument (null pointer, size, shape, unsupported dtype / head_dim) */
+    TREE_E_TOOLONG = -2,      /* a sequence is longer than the row capacity */
+    TREE_E_LAYOUT = -3,       /* the segment table is not a valid pre-order forest layout */
+    TREE_E_NOMEM = -4,        /* host allocation failed */
+    TREE_E_HIP = -5,          /* a HIP runtime call or kernel launch failed */
+    TREE_E_UNSUPPORTED = -6   /* valid arguments this build has no kernel for (e.g. block sizes) */
+};
+
+enum { TREE_DT_BF16 = 1, TREE_DT_F32 = 2 };
+enum { TREE_PLACE_BFD = 0, TREE_PLACE_IN_ORDER = 1 };
+
+/* ------------------------------------------------------------------------------------ *
+ * 1. Host planning
+ * ------------------------------------------------------------------------------------ */
+
+typedef struct {
+    int32_t row_len;       /* row capacity C in tokens, > 0 */
+    int32_t min_shared;    /* minimum shared-segment length, >= 1 ([PTP]: 64 by default) */
+    int32_t pad_multiple;  /* 0: every row is row_len long; m > 0: rows are the longest row's
+                              used length rounded up to a multiple of m */
+    int32_t placement;     /* TREE_PLACE_BFD ([PTP] placement listing) or TREE_PLACE_IN_ORDER
+                              ([PTP] historical section: fill the current row, move on for good
+                              when the next leaf does not fit) */
+} tree_pack_params;
+
+typedef struct tree_plan tree_plan;   /* opaque, host memory, owned by the library */
+
+/*
+ * tree_pack_plan — radix segment build + row packing + row layout ([PTP] tree-building
+ * passage and its refinements, scope passage, bin-packing passage and placement listing,
+ * integer-planning passage).
+ *
+ *   tokens       host int32 [seq_offsets[n_seqs]]: all sequences back to back.
+ *   seq_offsets  host int64 [n_seqs + 1], non-decreasing, seq_offsets[0] = 0; every
+ *                sequence must hold >= 1 token.
+ *   trainable    host uint8 [seq_offsets[n_seqs]] or NULL (nothing trainable).  Trainable
+ *                tokens and the token right before one are never shared, so each branch
+ *                keeps its own copy of the join token ([PTP] off-by-one note).
+ *   group_ids    host int32 [n_seqs] or NULL (each sequence its own group): placement
+ *                groups, placed by their longest sequence, descending.
+ *   p            packing parameters (see tree_pack_params).
+ *   out          receives the plan; free with tree_plan_free.
+ *
+ * The build runs over one global tree of every sequence ([PTP] scope passage).  Segments
+ * are numbered in depth-first pre-order; row r is the r-th bin; inside a row segments are
+ * ordered by that number, laid out back to back from token 0, parents row-local.
+ * Errors: TREE_E_INVAL, TREE_E_TOOLONG (a sequence longer than row_len), TREE_E_NOMEM.
+ * On error *out is set to NULL.  The inputs are only read during the call.
+ */
+int tree_pack_plan(const int32_t *tokens, const int64_t *seq_offsets, int32_t n_seqs,
+                   const uint8_t *trainable, const int32_t *group_ids,
+                   const tree_pack_params *p, tree_plan **out);
+
+/* Read-only views into a plan; valid until tree_plan_free.  All arrays are host memory. */
+typedef struct {
+    int32_t n_rows, row_len, n_segs, n_seqs;
+    int64_t real_tokens;       /* tokens laid out in rows (sum of used lengths) */
+    int64_t unpacked_tokens;   /* sum of sequence lengths; unpacked / real is the
+                                  tree_token_ratio of [AReaL] "Monitoring Packing Efficiency" */
+    int64_t tree_walk_ns, bin_pack_ns;   /* host time of the two planning phases */
+    const int32_t *seg_row_ptr;          /* [n_rows + 1] CSR over segments */
+    const int32_t *seg_start, *seg_len;  /* [n_segs] row-local token offset and length */
+    const int32_t *seg_parent;           /* [n_segs] row-local parent index, -1 = root */
+    const int32_t *seg_pos0;             /* [n_segs] position id of the segment's first token */
+    const int32_t *seg_global_id;        /* [n_segs] global pre-order segment number */
+    const int32_t *seg_src_seq;          /* [n_segs] a sequence holding the segment's tokens */
+    const int32_t *row_used;             /* [n_rows] real tokens per row */
+    const int32_t *pos_ids, *tok_seg;    /* [n_rows * row_len]; pads: 0 and -1 */
+    const int32_t *gather_seq, *gather_pos;  /* [n_rows * row_len] token source; pads: -1 */
+    const int32_t *seq_row, *seq_leaf_seg;   /* [n_seqs] row and row-local leaf segment */
+} tree_plan_view;
+
+int  tree_plan_get(const tree_plan *plan, tree_plan_view *out);
+void tree_plan_free(tree_plan *plan);
+
+/* ------------------------------------------------------------------------------------ *
+ * 2. Device attention
+ * ------------------------------------------------------------------------------------ */
+
+/*
+ * Attention problem description.  The segment arrays are DEVICE copies of a plan's (or any)
+ * segment table: per row, segments in depth-first pre-order, laid out back to back from
+ * token 0 with no gaps, parents row-local and earlier in the row; the rest of the row is
+ * padding.  Tensors (all contiguous, caller-owned, device):
+ *   q    [n_rows, row_len, h_q,  head_dim]  dtype
+ *   k, v [n_rows, row_len, h_kv, head_dim]  dtype
+ *   o    [n_rows, row_len, h_q,  head_dim]  dtype
+ *   lse  [n_rows, h_q, row_len]             float32, natural log
+ * Query head h reads key/value head h / (h_q / h_kv) (grouped-query attention).
+ */
+typedef struct {
+    int32_t n_rows, row_len, h_q, h_kv, head_dim, dtype;
+    int32_t block_q, block_k;   /* tile sizes of the plan; 0 = the forward kernel's sizes */
+    float   scale;              /* softmax scale; 0 = 1/sqrt(head_dim) */
+    int32_t n_segs;
+    const int32_t *seg_row_ptr; /* device [n_rows + 1] */
+    const int32_t *seg_start, *seg_len, *seg_parent;   /* device [n_segs] */
+} tree_attn_desc;
+
+/*
+ * tree_attn_blocks — the tile sizes tree_attn_fwd runs with for this description
+ * (block_q = 256 / the largest power of two <= 8 dividing h_q / h_kv; block_k = 64).
+ * A plan made with other (block_q, block_k) is valid for tree_attn_tiles but not for
+ * tree_attn_fwd.  Host only.  Errors: TREE_E_INVAL.
+ */
+int tree_attn_blocks(const tree_attn_desc *d, int32_t *block_q, int32_t *block_k);
+
+/* Bytes of device workspace tree_attn_plan needs for `d` (resolved tile sizes).  Host only. */
+int tree_attn_workspace_size(const tree_attn_desc *d, size_t *bytes);
+
+/*
+ * tree_attn_plan — tile classification on the device ([PTP] mask passage: one fully visible
+ * block per ancestor segment plus a causal triangle over the own segment; blocks are full,
+ * partial or skipped).  Validates the table into a device status word, computes for every
+ * token the end of its segment's subtree, classifies every (q-tile, k-tile) by its exact
+ * visible-pair count, builds the per-q-tile CSR lists and a longest-first work list.
+ * `ws` must hold tree_attn_workspace_size bytes (256-byte aligned).  Asynchronous.
+ * Errors: TREE_E_INVAL (sizes, tiles not dividing row_len), TREE_E_HIP.
+ */
+int tree_attn_plan(const tree_attn_desc *d, void *ws, void *stream);
+
+/*
+ * tree_attn_plan_status — synchronizes `stream`, then returns TREE_OK or TREE_E_LAYOUT if
+ * the device found the segment table invalid (tree_attn_fwd then writes nothing).
+ */
+int tree_attn_plan_status(const tree_attn_desc *d, const void *ws, void *stream);
+
+/* Device pointers into a planned workspace (for tests and tools). */
+typedef struct {
+    int32_t block_q, block_k, n_qtiles, n_ktiles;   /* per row */
+    const uint8_t *class_map;   /* [n_rows * n_qtiles * n_ktiles] 0 skip, 1 full, 2 partial */
+    const int32_t *qt_ptr;      /* [n_rows * n_qtiles + 1] CSR offsets, row-major (row, q-tile) */
+    const int32_t *kt_idx;      /* [nnz] ascending k-tiles with class != skip */
+    const uint8_t *kt_kind;     /* [nnz] their classes */
+    const int32_t *kend;        /* [n_rows * row_len] token j is visible to exactly the queries
+                                   i with j <= i < kend[j]; pads: kend[j] = j */
+    const int32_t *work;        /* [n_rows * n_qtiles] q-tiles, most non-skip tiles first */
+    const int32_t *status;      /* [1] 0 = table valid */
+} tree_tile_view;
+
+int tree_attn_tiles(const tree_attn_desc *d, const void *ws, tree_tile_view *out);
+
+/*
+ * tree_attn_fwd — tree-masked attention forward ([PTP] attention-mask passage; [AOM] "How do
+ * we implement shared prefix?"): for every real token i and query head h,
+ *   O[i,h] = softmax_j(scale * q[i,h] . k[j,g]) v[j,g] over j in anc*(i)
+ * (itself, earlier tokens of its segment, every token of its ancestor segments), and
+ * LSE[h,i] = log-sum-exp of those scores.  Pads get O = 0 and LSE = -inf; pad Q/K/V
+ * contents never reach a result.  `ws` must come from tree_attn_plan with the same `d`.
+ * bf16: bf16 MFMA with fp32 accumulation, head_dim 64 or 128; f32: fp32 MFMA, head_dim 64.
+ * Asynchronous.  Errors: TREE_E_INVAL, TREE_E_UNSUPPORTED (plan tiles differ from
+ * tree_attn_blocks, or f32 with head_dim 128), TREE_E_HIP.
+ */
+int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const void *k,
+                  const void *v, void *o, float *lse, void *stream);
+
+const char *tree_status_str(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TREEATTN_H */

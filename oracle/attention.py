@@ -15,7 +15,7 @@ Pads see nothing: O = 0 and LSE = -inf there (reading R7).  Pad Q/K/V contents n
 enter any result.
 
 Two implementations of the same definition:
-  * ``attention_brute`` / ``attention_at``: token by token over the parent walk anc*(i);
+  * ``attention_brute`` / ``attention_at``: query by query over anc*(i) from the parent walk;
   * ``attention_segment_blocked``: per segment, the keys are all tokens of the segment's
     ancestor segments followed by the segment's own tokens under a causal mask — the
     "one fully visible block per ancestor segment plus a causal triangle over its own
@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .mask import PAD, ancestors, row_parents
+from .mask import PAD, row_parents, visibility_bits
 
 
 def _get(inp, k):
@@ -51,39 +51,51 @@ def _softmax_rows(s):
     return m[..., 0], l[..., 0], p
 
 
-def _attend(qi, kk, vv, scale, G):
-    """One query position, all heads.  qi [Hq, D]; kk, vv [n, Hkv, D]."""
-    Hq, D = qi.shape
-    Hkv = kk.shape[1]
-    q3 = qi.reshape(Hkv, G, D)
-    s = scale * np.einsum("hgd,nhd->hgn", q3, kk)
-    m, l, p = _softmax_rows(s)
-    o = np.einsum("hgn,nhd->hgd", p, vv) / l[..., None]
-    return o.reshape(Hq, D), (m + np.log(l)).reshape(Hq)
+def attention_at(inp, samples, max_elems: int = 1 << 24):
+    """O and LSE at chosen (row, position) pairs, all heads.
 
-
-def attention_at(inp, samples):
-    """O and LSE at chosen (row, position) pairs, all heads, by the token parent walk.
-
+    Query i's visible set anc*(i) is its row of the parent-walk bit matrix
+    (``mask.visibility_bits``: row i = row pi(i) plus bit i).  For a batch of queries of one
+    row, scores are taken against the union of their visible keys, the keys a query does
+    not see are set to -inf, then the row softmax and PV follow — the definition, batched.
     Returns (O [n, Hq, D], LSE [n, Hq]) in float64.
     """
     Hq, Hkv = int(_get(inp, "h_q")), int(_get(inp, "h_kv"))
     D, scale = int(_get(inp, "head_dim")), float(_get(inp, "scale"))
+    T = int(_get(inp, "row_len"))
     G = Hq // Hkv
     O = np.zeros((len(samples), Hq, D))
     L = np.full((len(samples), Hq), -np.inf)
-    cache = {}
+    by_row: dict = {}
     for n, (r, i) in enumerate(samples):
-        if r not in cache:
-            cache = {r: row_parents(inp, r)}
-        pi = cache[r]
-        anc = ancestors(pi, int(i))
-        if len(anc) == 0:
-            continue
-        qi = _f64(inp, "q", (r, int(i)))
-        kk = _f64(inp, "k", (r, anc))
-        vv = _f64(inp, "v", (r, anc))
-        O[n], L[n] = _attend(qi, kk, vv, scale, G)
+        by_row.setdefault(int(r), []).append((n, int(i)))
+    for r, items in by_row.items():
+        items.sort(key=lambda x: x[1])
+        bits = visibility_bits(row_parents(inp, r))
+        c = 0
+        while c < len(items):
+            m = max(1, min(64, max_elems // (Hq * T)))
+            part = items[c:c + m]
+            c += m
+            idx = np.array([n for n, _ in part])
+            pos = np.array([i for _, i in part])
+            vis = np.unpackbits(bits[pos], axis=1)[:, :T].astype(bool)   # [m, T]
+            live = vis.any(axis=1)
+            if not live.any():
+                continue
+            keys = np.flatnonzero(vis.any(axis=0))
+            vis = vis[live][:, keys]
+            nq, nk = int(live.sum()), len(keys)
+            q = _f64(inp, "q", (r, pos[live]))                                       # [m, Hq, D]
+            k = _f64(inp, "k", (r, keys)).transpose(1, 2, 0)                          # [Hkv, D, nk]
+            v = _f64(inp, "v", (r, keys)).transpose(1, 0, 2)                          # [Hkv, nk, D]
+            q4 = q.reshape(nq, Hkv, G, D).transpose(1, 0, 2, 3).reshape(Hkv, nq * G, D)
+            S = (scale * np.matmul(q4, k)).reshape(Hkv, nq, G, nk)
+            S = np.where(vis[None, :, None, :], S, -np.inf)
+            m_, l_, P = _softmax_rows(S)
+            o = np.matmul(P.reshape(Hkv, nq * G, nk), v).reshape(Hkv, nq, G, D) / l_[..., None]
+            O[idx[live]] = o.transpose(1, 0, 2, 3).reshape(nq, Hq, D)
+            L[idx[live]] = (m_ + np.log(l_)).transpose(1, 0, 2).reshape(nq, Hq)
     return O, L
 
 

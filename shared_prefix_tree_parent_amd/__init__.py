@@ -1,0 +1,266 @@
+"""Python binding of libtreeattn.so (prefix-tree packing + tree-masked attention on MI355X).
+
+Argument marshalling only: every step runs in the C++ planner or the HIP kernels of the
+shared library; torch is used for device memory and the current stream.  The functions
+carry the C names of ``include/treeattn.h``:
+
+  tree_pack_plan(...)            -> dict of numpy arrays (host planner)
+  tree_attn_blocks(desc)         -> (block_q, block_k) of the forward kernel
+  tree_attn_workspace_size(desc) -> bytes
+  tree_attn_plan(desc, ws)       (async on the current stream)
+  tree_attn_plan_status(desc, ws)
+  tree_attn_tiles(desc, ws)      -> dict of device pointers / sizes
+  tree_attn_fwd(desc, ws, q, k, v, o, lse)  (async on the current stream)
+
+plus thin conveniences ``make_desc``, ``attn_plan`` and ``attn_fwd`` that allocate torch
+tensors.  If the library is missing this module raises on first use: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtreeattn.so")
+
+TREE_OK, TREE_E_INVAL, TREE_E_TOOLONG, TREE_E_LAYOUT, TREE_E_NOMEM, TREE_E_HIP, TREE_E_UNSUPPORTED = \
+    0, -1, -2, -3, -4, -5, -6
+TREE_DT_BF16, TREE_DT_F32 = 1, 2
+TREE_PLACE_BFD, TREE_PLACE_IN_ORDER = 0, 1
+
+EXPORTS = ("tree_pack_plan", "tree_plan_get", "tree_plan_free", "tree_attn_blocks",
+           "tree_attn_workspace_size", "tree_attn_plan", "tree_attn_plan_status", "tree_attn_tiles",
+           "tree_attn_fwd", "tree_status_str")
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class TreeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {status_str(code)} ({code})")
+        self.code = code
+
+
+class PackParams(ctypes.Structure):
+    _fields_ = [("row_len", ctypes.c_int32), ("min_shared", ctypes.c_int32),
+                ("pad_multiple", ctypes.c_int32), ("placement", ctypes.c_int32)]
+
+
+class PlanView(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int32), ("row_len", ctypes.c_int32), ("n_segs", ctypes.c_int32),
+                ("n_seqs", ctypes.c_int32), ("real_tokens", ctypes.c_int64),
+                ("unpacked_tokens", ctypes.c_int64), ("tree_walk_ns", ctypes.c_int64),
+                ("bin_pack_ns", ctypes.c_int64)] + \
+               [(n, _i32p) for n in ("seg_row_ptr", "seg_start", "seg_len", "seg_parent", "seg_pos0",
+                                     "seg_global_id", "seg_src_seq", "row_used", "pos_ids", "tok_seg",
+                                     "gather_seq", "gather_pos", "seq_row", "seq_leaf_seg")]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int32), ("row_len", ctypes.c_int32), ("h_q", ctypes.c_int32),
+                ("h_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("n_segs", ctypes.c_int32), ("seg_row_ptr", ctypes.c_void_p),
+                ("seg_start", ctypes.c_void_p), ("seg_len", ctypes.c_void_p),
+                ("seg_parent", ctypes.c_void_p)]
+
+
+class TileView(ctypes.Structure):
+    _fields_ = [("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("n_qtiles", ctypes.c_int32),
+                ("n_ktiles", ctypes.c_int32), ("class_map", ctypes.c_void_p), ("qt_ptr", ctypes.c_void_p),
+                ("kt_idx", ctypes.c_void_p), ("kt_kind", ctypes.c_void_p), ("kend", ctypes.c_void_p),
+                ("work", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtreeattn.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m shared_prefix_tree_parent_amd.build_lib`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.tree_pack_plan.argtypes = [vp, vp, i32, vp, vp, ctypes.POINTER(PackParams), ctypes.POINTER(vp)]
+        L.tree_plan_get.argtypes = [vp, ctypes.POINTER(PlanView)]
+        L.tree_plan_free.argtypes = [vp]
+        L.tree_plan_free.restype = None
+        D = ctypes.POINTER(AttnDesc)
+        L.tree_attn_blocks.argtypes = [D, _i32p, _i32p]
+        L.tree_attn_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+        L.tree_attn_plan.argtypes = [D, vp, vp]
+        L.tree_attn_plan_status.argtypes = [D, vp, vp]
+        L.tree_attn_tiles.argtypes = [D, vp, ctypes.POINTER(TileView)]
+        L.tree_attn_fwd.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
+        L.tree_status_str.argtypes = [ctypes.c_int]
+        L.tree_status_str.restype = ctypes.c_char_p
+        for name in EXPORTS:
+            if name not in ("tree_plan_free", "tree_status_str"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(code: int) -> str:
+    return lib().tree_status_str(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != TREE_OK:
+        raise TreeError(code, what)
+
+
+def _ptr(a) -> int:
+    if a is None:
+        return 0
+    if isinstance(a, np.ndarray):
+        return a.ctypes.data
+    return int(a.data_ptr())
+
+
+# ------------------------------------------------------------------------------ host planning
+
+_PLAN_ARRAYS = {
+    "seg_row_ptr": "n_rows+1", "seg_start": "n_segs", "seg_len": "n_segs", "seg_parent": "n_segs",
+    "seg_pos0": "n_segs", "seg_global_id": "n_segs", "seg_src_seq": "n_segs", "row_used": "n_rows",
+    "pos_ids": "rt", "tok_seg": "rt", "gather_seq": "rt", "gather_pos": "rt", "seq_row": "n_seqs",
+    "seq_leaf_seg": "n_seqs",
+}
+
+
+def tree_pack_plan(tokens, seq_offsets, trainable=None, group_ids=None, row_len=4096, min_shared=64,
+                   pad_multiple=0, placement=TREE_PLACE_BFD) -> dict:
+    """Run the host planner; returns the plan's scalars and copies of its arrays."""
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    off = np.ascontiguousarray(seq_offsets, dtype=np.int64)
+    tr = None if trainable is None else np.ascontiguousarray(trainable, dtype=np.uint8)
+    gr = None if group_ids is None else np.ascontiguousarray(group_ids, dtype=np.int32)
+    n = len(off) - 1
+    p = PackParams(row_len, min_shared, pad_multiple, placement)
+    h = ctypes.c_void_p()
+    _check(lib().tree_pack_plan(_ptr(tok), _ptr(off), n, _ptr(tr), _ptr(gr), ctypes.byref(p),
+                                ctypes.byref(h)), "tree_pack_plan")
+    try:
+        v = PlanView()
+        _check(lib().tree_plan_get(h, ctypes.byref(v)), "tree_plan_get")
+        out = {k: getattr(v, k) for k, _ in PlanView._fields_[:8]}
+        sizes = {"n_rows+1": v.n_rows + 1, "n_segs": v.n_segs, "n_rows": v.n_rows,
+                 "rt": v.n_rows * v.row_len, "n_seqs": v.n_seqs}
+        for name, sz in _PLAN_ARRAYS.items():
+            cnt = sizes[sz]
+            ptr = getattr(v, name)
+            out[name] = np.ctypeslib.as_array(ptr, shape=(cnt,)).copy() if cnt > 0 else np.zeros(0, np.int32)
+        out["n_paths"] = v.n_seqs
+        out["used"] = out["row_used"]
+        return out
+    finally:
+        lib().tree_plan_free(h)
+
+
+def pack_batch(batch, row_len=4096, min_shared=64, pad_multiple=0, use_groups=True,
+               placement=TREE_PLACE_BFD) -> dict:
+    """``tree_pack_plan`` on a ``workloads.SeqBatch``-like object (tokens/offsets/trainable/groups)."""
+    return tree_pack_plan(batch.tokens, batch.offsets, batch.trainable,
+                          batch.groups if use_groups else None, row_len, min_shared, pad_multiple, placement)
+
+
+# ------------------------------------------------------------------------------ device attention
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def make_desc(n_rows, row_len, h_q, h_kv, head_dim, dtype, seg_row_ptr, seg_start, seg_len, seg_parent,
+              scale=0.0, block_q=0, block_k=0) -> AttnDesc:
+    """Build a descriptor; the segment arrays are device tensors (int32) kept alive by the caller."""
+    dt = {"bf16": TREE_DT_BF16, "f32": TREE_DT_F32}.get(dtype, dtype)
+    return AttnDesc(n_rows, row_len, h_q, h_kv, head_dim, dt, block_q, block_k, float(scale),
+                    int(seg_start.numel()) if seg_start is not None else 0,
+                    _ptr(seg_row_ptr), _ptr(seg_start), _ptr(seg_len), _ptr(seg_parent))
+
+
+def tree_attn_blocks(desc: AttnDesc):
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().tree_attn_blocks(ctypes.byref(desc), ctypes.byref(bq), ctypes.byref(bk)), "tree_attn_blocks")
+    return bq.value, bk.value
+
+
+def tree_attn_workspace_size(desc: AttnDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().tree_attn_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "tree_attn_workspace_size")
+    return n.value
+
+
+def tree_attn_plan(desc: AttnDesc, ws, stream=None) -> None:
+    _check(lib().tree_attn_plan(ctypes.byref(desc), _ptr(ws), _stream(stream)), "tree_attn_plan")
+
+
+def tree_attn_plan_status(desc: AttnDesc, ws, stream=None) -> int:
+    """TREE_OK or TREE_E_LAYOUT (synchronizes the stream)."""
+    code = lib().tree_attn_plan_status(ctypes.byref(desc), _ptr(ws), _stream(stream))
+    if code not in (TREE_OK, TREE_E_LAYOUT):
+        _check(code, "tree_attn_plan_status")
+    return code
+
+
+def tree_attn_tiles(desc: AttnDesc, ws) -> dict:
+    t = TileView()
+    _check(lib().tree_attn_tiles(ctypes.byref(desc), _ptr(ws), ctypes.byref(t)), "tree_attn_tiles")
+    return {k: getattr(t, k) for k, _ in TileView._fields_}
+
+
+def tree_attn_fwd(desc: AttnDesc, ws, q, k, v, o, lse, stream=None) -> None:
+    _check(lib().tree_attn_fwd(ctypes.byref(desc), _ptr(ws), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                               _stream(stream)), "tree_attn_fwd")
+
+
+# ------------------------------------------------------------------------------ conveniences
+
+class AttnPlan:
+    """Device segment table + workspace for one batch (reused by every layer)."""
+
+    def __init__(self, seg_row_ptr, seg_start, seg_len, seg_parent, n_rows, row_len, h_q, h_kv,
+                 head_dim, dtype="bf16", scale=0.0, block_q=0, block_k=0, device="cuda"):
+        import torch
+        as_dev = lambda a: torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+        self.seg = [as_dev(seg_row_ptr), as_dev(seg_start), as_dev(seg_len), as_dev(seg_parent)]
+        self.desc = make_desc(n_rows, row_len, h_q, h_kv, head_dim, dtype, *self.seg, scale=scale,
+                              block_q=block_q, block_k=block_k)
+        nbytes = tree_attn_workspace_size(self.desc)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        tree_attn_plan(self.desc, self.ws)
+
+    def status(self) -> int:
+        return tree_attn_plan_status(self.desc, self.ws)
+
+    def tiles(self) -> dict:
+        return tree_attn_tiles(self.desc, self.ws)
+
+
+def attn_plan(inp, dtype=None, block_q=0, block_k=0, device="cuda") -> AttnPlan:
+    """Plan for a workload object with n_rows/row_len/h_q/h_kv/head_dim/dtype/scale and seg_* arrays."""
+    return AttnPlan(inp.seg_row_ptr, inp.seg_start, inp.seg_len, inp.seg_parent, inp.n_rows, inp.row_len,
+                    inp.h_q, inp.h_kv, inp.head_dim, dtype or inp.dtype, getattr(inp, "scale", 0.0),
+                    block_q, block_k, device)
+
+
+def attn_fwd(q, k, v, plan: AttnPlan, o=None, lse=None):
+    """Tree-masked attention forward; returns (o, lse).  q/k/v are contiguous device tensors."""
+    import torch
+    d = plan.desc
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((d.n_rows, d.h_q, d.row_len), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, o, lse):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    tree_attn_fwd(d, plan.ws, q, k, v, o, lse)
+    return o, lse

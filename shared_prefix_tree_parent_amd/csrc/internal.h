@@ -1,0 +1,69 @@
+// Internal declarations shared by the C-ABI glue and the HIP kernels of libtreeattn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "treeattn.h"
+
+namespace treeattn {
+
+constexpr int kTileSkip = 0, kTileFull = 1, kTilePartial = 2;
+constexpr int kFwdBlockK = 64;        // keys per k-tile in the forward kernel
+constexpr int kFwdRowsPerWG = 256;    // (query head, position) rows one forward workgroup owns
+
+// Device workspace layout: every section 256-byte aligned, offsets from the base pointer.
+struct WsLayout {
+    int32_t R = 0, T = 0, BQ = 0, BK = 0, nQ = 0, nK = 0, n_segs = 0;
+    size_t status = 0;    // int32[4]: [0] layout status (0 = ok), [1..3] scratch counters
+    size_t n_real = 0;    // int32[R]   tokens used per row, -1 if the row's table is invalid
+    size_t seg_end = 0;   // int32[n_segs] end (exclusive token offset) of each segment's subtree
+    size_t kend = 0;      // int32[R*T]
+    size_t cmap = 0;      // uint8[R*nQ*nK]
+    size_t qt_ptr = 0;    // int32[R*nQ + 1]
+    size_t kt_idx = 0;    // int32[R*nQ*nK]
+    size_t kt_kind = 0;   // uint8[R*nQ*nK]
+    size_t work = 0;      // int32[R*nQ]
+    size_t hist = 0;      // int32[nK + 2]
+    size_t total = 0;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_t n_segs) {
+    WsLayout w;
+    w.R = R; w.T = T; w.BQ = BQ; w.BK = BK; w.n_segs = n_segs;
+    w.nQ = T / BQ;
+    w.nK = T / BK;
+    const size_t tiles = size_t(R) * w.nQ * w.nK;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    w.status = take(4 * sizeof(int32_t));
+    w.n_real = take(size_t(R) * sizeof(int32_t));
+    w.seg_end = take(size_t(n_segs > 0 ? n_segs : 1) * sizeof(int32_t));
+    w.kend = take(size_t(R) * T * sizeof(int32_t));
+    w.cmap = take(tiles);
+    w.qt_ptr = take((size_t(R) * w.nQ + 1) * sizeof(int32_t));
+    w.kt_idx = take(tiles * sizeof(int32_t));
+    w.kt_kind = take(tiles);
+    w.work = take(size_t(R) * w.nQ * sizeof(int32_t));
+    w.hist = take((size_t(w.nK) + 2) * sizeof(int32_t));
+    w.total = off;
+    return w;
+}
+
+// Launchers (defined in classify.hip / attn_fwd.hip).  Return hipSuccess or the first error.
+hipError_t launch_plan(const tree_attn_desc &d, const WsLayout &w, char *ws, hipStream_t s);
+
+struct FwdShape {
+    int32_t R, T, Hq, Hkv, D, dtype;
+    int32_t G;      // h_q / h_kv
+    int32_t HCH;    // query heads of one KV group handled by one workgroup (1, 2, 4 or 8)
+    int32_t BQ;     // positions per q-tile = kFwdRowsPerWG / HCH
+    float scale;
+};
+hipError_t launch_fwd(const FwdShape &sh, const WsLayout &w, const char *ws, const void *q,
+                      const void *k, const void *v, void *o, float *lse, hipStream_t s);
+
+}  // namespace treeattn

@@ -1,0 +1,98 @@
+"""Helpers for the GPU tests: run the product path through the C-ABI binding and fetch results."""
+import sys
+
+import numpy as np
+
+import shared_prefix_tree_parent_amd as ta
+from workloads import RowInputs
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(inp: RowInputs, name: str):
+    import torch
+    a = getattr(inp, name)
+    if inp.dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to("cuda")
+
+
+def run_fwd(inp: RowInputs, plan=None, repeats: int = 1):
+    """Plan (if not given) and run the forward; returns (O float32 [R,T,Hq,D], LSE [R,Hq,T], plan)."""
+    import torch
+    if plan is None:
+        plan = ta.attn_plan(inp)
+    q, k, v = to_dev(inp, "q"), to_dev(inp, "k"), to_dev(inp, "v")
+    o = lse = None
+    for _ in range(repeats):
+        o, lse = ta.attn_fwd(q, k, v, plan)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy(), plan
+
+
+def fetch_tiles(plan, n_rows):
+    """Copy the classifier's outputs (all inside the plan's workspace tensor) to host arrays."""
+    import torch
+    t = plan.tiles()
+    nq, nk = t["n_qtiles"], t["n_ktiles"]
+    ntile = n_rows * nq
+    torch.cuda.synchronize()
+    base = plan.ws.data_ptr()
+
+    def grab(ptr, count, dtype):
+        nbytes = count * np.dtype(dtype).itemsize
+        if nbytes == 0:
+            return np.zeros(0, dtype)
+        off = ptr - base
+        assert 0 <= off and off + nbytes <= plan.ws.numel()
+        return plan.ws[off:off + nbytes].cpu().numpy().view(dtype).copy()
+
+    qt_ptr = grab(t["qt_ptr"], ntile + 1, np.int32)
+    nnz = int(qt_ptr[-1]) if ntile > 0 else 0
+    return dict(
+        block_q=t["block_q"], block_k=t["block_k"], n_qtiles=nq, n_ktiles=nk,
+        class_map=grab(t["class_map"], ntile * nk, np.uint8).reshape(n_rows, nq, nk),
+        qt_ptr=qt_ptr,
+        kt_idx=grab(t["kt_idx"], nnz, np.int32),
+        kt_kind=grab(t["kt_kind"], nnz, np.uint8),
+        kend=grab(t["kend"], n_rows * plan.desc.row_len, np.int32).reshape(n_rows, plan.desc.row_len),
+        work=grab(t["work"], ntile, np.int32),
+        status=int(grab(t["status"], 1, np.int32)[0]),
+    )
+
+
+def rows_view(O, L):
+    """[R,T,Hq,D], [R,Hq,T] -> [R*T, Hq, D], [R*T, Hq]."""
+    R, T, Hq, D = O.shape
+    return O.reshape(R * T, Hq, D), L.transpose(0, 2, 1).reshape(R * T, Hq)
+
+
+def check_close(o_gpu, l_gpu, o_ref, l_ref, dtype, real_mask, what=""):
+    """Compare [N, Hq, D] outputs and [N, Hq] LSE at N positions (real_mask [N]: real tokens).
+
+    Tolerances: bf16 O max-abs 2e-2, mean-abs 2e-3 (over real tokens x heads x head_dim), LSE
+    max-abs 1e-3; f32 O max-abs 1e-4, mean-abs 1e-5, LSE max-abs 1e-4.  Pads exact: O = 0,
+    LSE = -inf."""
+    tol = dict(bf16=(2e-2, 2e-3, 1e-3), f32=(1e-4, 1e-5, 1e-4))[dtype]
+    real_mask = np.asarray(real_mask, bool)
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite O"
+    err = np.abs(o_gpu - o_ref)
+    real_o = err[real_mask]
+    max_abs = float(real_o.max()) if real_o.size else 0.0
+    mean_abs = float(real_o.mean()) if real_o.size else 0.0
+    lerr = np.abs(l_gpu[real_mask] - l_ref[real_mask])
+    lmax = float(lerr.max()) if lerr.size else 0.0
+    log(f"  {what}: O max-abs {max_abs:.3e} mean-abs {mean_abs:.3e}  LSE max-abs {lmax:.3e}")
+    assert max_abs <= tol[0], f"{what}: O max-abs {max_abs}"
+    assert mean_abs <= tol[1], f"{what}: O mean-abs {mean_abs}"
+    assert lmax <= tol[2], f"{what}: LSE max-abs {lmax}"
+    pad = ~real_mask
+    if pad.any():
+        assert np.all(o_gpu[pad] == 0), f"{what}: pad O not zero"
+        assert np.all(l_gpu[pad] == -np.inf), f"{what}: pad LSE not -inf"
+    return max_abs, mean_abs, lmax

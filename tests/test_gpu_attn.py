@@ -1,0 +1,185 @@
+"""GPU: tree_attn_fwd against the float64 oracle, element by element.
+
+Whole-row comparisons where the oracle finishes in seconds (config 1, config 2, random
+multi-tile forests with ragged tails); at the full sizes of configs 3-5, in the launch
+configuration the benchmark times, on sampled query positions the oracle computes one by
+one (all heads), always including segment starts/ends, the last real token and pads.
+Tolerances (bf16): O max-abs 2e-2 and mean-abs 2e-3, LSE max-abs 1e-3; (f32): O 1e-4 /
+1e-5, LSE 1e-4; pads exact.
+"""
+import numpy as np
+import pytest
+
+import shared_prefix_tree_parent_amd as ta
+from oracle import attention as A
+from oracle import packer as P
+from tests.gpu_util import check_close, log, rows_view, run_fwd
+from workloads import RowInputs, bf16_bits_from_f32, fill_pads, make_config, random_forest_row
+
+pytestmark = pytest.mark.gpu
+
+
+def _real_mask(inp):
+    m = np.zeros((inp.n_rows, inp.row_len), bool)
+    for r in range(inp.n_rows):
+        m[r, :int(inp.real_len[r])] = True
+    return m
+
+
+def _full_check(inp, what, brute=False):
+    O, L, _ = run_fwd(inp)
+    Oref, Lref = A.attention_brute(inp) if brute else A.attention_segment_blocked(inp)
+    o, l = rows_view(O, L)
+    orf, lrf = rows_view(Oref, Lref)
+    return check_close(o, l, orf, lrf, inp.dtype, _real_mask(inp).reshape(-1), what)
+
+
+def _samples(inp, rng, n):
+    """(row, position) pairs: random real tokens plus every segment's first and last token,
+    each row's last real token and a few pads."""
+    out = set()
+    for r in range(inp.n_rows):
+        a, b = int(inp.seg_row_ptr[r]), int(inp.seg_row_ptr[r + 1])
+        for s in range(a, b):
+            out.add((r, int(inp.seg_start[s])))
+            out.add((r, int(inp.seg_start[s] + inp.seg_len[s] - 1)))
+        used = int(inp.real_len[r])
+        if used < inp.row_len:
+            out.add((r, used))
+            out.add((r, inp.row_len - 1))
+    rows = rng.integers(0, inp.n_rows, n)
+    for r in rows:
+        used = int(inp.real_len[r])
+        out.add((int(r), int(rng.integers(0, used))))
+    return sorted(out)
+
+
+def _sampled_check(inp, n_samples, what, seed=0):
+    O, L, _ = run_fwd(inp)
+    smp = _samples(inp, np.random.default_rng(seed), n_samples)
+    log(f"  {what}: {len(smp)} sampled positions")
+    Oref, Lref = A.attention_at(inp, smp)
+    idx_r = np.array([s[0] for s in smp])
+    idx_t = np.array([s[1] for s in smp])
+    o = O[idx_r, idx_t]
+    l = L[idx_r, :, idx_t]
+    real = idx_t < inp.real_len[idx_r]
+    return check_close(o, l, Oref, Lref, inp.dtype, real, what)
+
+
+def test_config1_full_fp32():
+    log("config 1 (fp32) full")
+    _full_check(make_config(1), "config 1", brute=True)
+
+
+def test_config2_full():
+    log("config 2 full")
+    _full_check(make_config(2), "config 2")
+
+
+@pytest.mark.parametrize("cfg,n", [(3, 384), (4, 384), (5, 256)])
+def test_full_size_configs_sampled(cfg, n):
+    log(f"config {cfg} sampled at full size")
+    if cfg == 4:
+        gpu_inp = make_config(4, packer=lambda b, C, m: ta.pack_batch(b, C, m))
+        ref_inp = make_config(4, packer=lambda b, C, m: P.pack_batch(b, C, m), with_qkv=False)
+        for k in ("n_rows", "row_len", "seg_row_ptr", "seg_start", "seg_len", "seg_parent"):
+            assert np.array_equal(getattr(gpu_inp, k), getattr(ref_inp, k))
+        # Q/K/V are the generator's draws for this (R, T); identical plans give identical draws.
+        ref_inp.q, ref_inp.k, ref_inp.v = gpu_inp.q, gpu_inp.k, gpu_inp.v
+        O, L, _ = run_fwd(gpu_inp)
+        smp = _samples(ref_inp, np.random.default_rng(cfg), n)
+        Oref, Lref = A.attention_at(ref_inp, smp)
+        idx_r = np.array([s[0] for s in smp])
+        idx_t = np.array([s[1] for s in smp])
+        real = idx_t < ref_inp.real_len[idx_r]
+        check_close(O[idx_r, idx_t], L[idx_r, :, idx_t], Oref, Lref, "bf16", real, "config 4")
+    else:
+        _sampled_check(make_config(cfg), n, f"config {cfg}", seed=cfg)
+
+
+def test_config3_uniform_variant_sampled():
+    _sampled_check(make_config(3, uniform_lengths=True), 256, "config 3 (uniform lengths)", seed=33)
+
+
+def _random_inputs(rng, R, T, Hq, Hkv, D, dtype, max_segs=14, max_len=160):
+    starts, lens, pars, pos0, rp, used = [], [], [], [], [0], []
+    for _ in range(R):
+        st, ln, par, p0, u = random_forest_row(rng, T, max_segs=max_segs, max_len=max_len,
+                                               fill=float(rng.uniform(0.3, 1.0)))
+        starts.append(st); lens.append(ln); pars.append(par); pos0.append(p0)
+        rp.append(rp[-1] + len(st)); used.append(u)
+    cat = lambda xs: np.concatenate(xs).astype(np.int32)
+    inp = RowInputs("random", R, T, Hq, Hkv, D, dtype, 1 / np.sqrt(D), np.asarray(rp, np.int32), cat(starts),
+                    cat(lens), cat(pars), cat(pos0), 0, real_len=np.asarray(used))
+    for name, H in (("q", Hq), ("k", Hkv), ("v", Hkv)):
+        x = rng.standard_normal((R, T, H, D), dtype=np.float32)
+        setattr(inp, name, bf16_bits_from_f32(x) if dtype == "bf16" else x)
+    return inp
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 128), (8, 4, 128), (8, 2, 128), (16, 2, 128), (32, 2, 128),
+                                      (8, 2, 64), (6, 2, 128), (4, 4, 64)])
+def test_random_forests_bf16(Hq, Hkv, D):
+    rng = np.random.default_rng(Hq * 100 + Hkv * 10 + D)
+    for it in range(3):
+        inp = _random_inputs(rng, R=2, T=512, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16")
+        _full_check(inp, f"random {Hq}/{Hkv} D{D} #{it}")
+
+
+def test_random_forests_fp32():
+    rng = np.random.default_rng(7)
+    for it in range(3):
+        inp = _random_inputs(rng, R=2, T=512, Hq=2, Hkv=2, D=64, dtype="f32")
+        _full_check(inp, f"random fp32 #{it}")
+
+
+def test_one_segment_row_and_singletons():
+    rng = np.random.default_rng(8)
+    # one long segment (plain causal attention) with a ragged tail of pads
+    inp = _random_inputs(rng, 1, 512, 8, 2, 128, "bf16")
+    inp.seg_row_ptr = np.array([0, 1], np.int32)
+    inp.seg_start = np.array([0], np.int32)
+    inp.seg_len = np.array([437], np.int32)
+    inp.seg_parent = np.array([-1], np.int32)
+    inp.seg_pos0 = np.array([0], np.int32)
+    inp.real_len = np.array([437])
+    _full_check(inp, "one segment")
+    # every token its own root: O = v exactly up to bf16 rounding
+    n = 256
+    inp.seg_row_ptr = np.array([0, n], np.int32)
+    inp.seg_start = np.arange(n, dtype=np.int32)
+    inp.seg_len = np.ones(n, np.int32)
+    inp.seg_parent = np.full(n, -1, np.int32)
+    inp.seg_pos0 = np.zeros(n, np.int32)
+    inp.real_len = np.array([n])
+    _full_check(inp, "singleton roots")
+
+
+def test_empty_rows_and_all_pad_batch():
+    rng = np.random.default_rng(9)
+    inp = _random_inputs(rng, 3, 256, 8, 2, 128, "bf16")
+    # make row 1 empty (all pads)
+    rp = inp.seg_row_ptr.copy()
+    n1 = rp[2] - rp[1]
+    keep = np.r_[np.arange(rp[1]), np.arange(rp[2], rp[3])]
+    for k in ("seg_start", "seg_len", "seg_parent", "seg_pos0"):
+        setattr(inp, k, getattr(inp, k)[keep])
+    inp.seg_row_ptr = np.array([0, rp[1], rp[1], rp[3] - n1], np.int32)
+    inp.real_len = np.array([inp.real_len[0], 0, inp.real_len[2]])
+    _full_check(inp, "empty middle row")
+
+
+def test_nan_pads_do_not_leak():
+    inp = make_config(2)
+    O1, L1, _ = run_fwd(inp)
+    fill_pads(inp, np.nan)
+    O2, L2, _ = run_fwd(inp)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_deterministic():
+    inp = make_config(3)
+    O1, L1, plan = run_fwd(inp)
+    O2, L2, _ = run_fwd(inp, plan=plan, repeats=2)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)

@@ -14,6 +14,7 @@ from .gen import (  # noqa: F401
     make_config,
     config4_sequences,
     draw_qkv,
+    fill_pads,
     random_forest_row,
     random_sequences,
 )
