@@ -1,0 +1,239 @@
+"""Benchmark of the tree-attention hot path on one MI355X.
+
+A step = one pass of the device hot path over one batch: tile classification
+(tree_attn_plan) + tree-masked attention forward (tree_attn_fwd), inputs resident in HBM.
+Host planning (radix build + row packing + layout) runs once per batch and is timed
+separately (`host_plan_ms`).  Default workload: the long-prefix row (5000-token shared
+prefix + 16 rollouts, 32/8 heads, head_dim 128, bf16).
+
+Prints ONE JSON line: value = useful TFLOP/s of a step, where useful FLOPs =
+4 * head_dim * h_q * (visible query/key pairs over real tokens); plus % of the bf16 MFMA
+peak, trajectories/s, the forward kernel's roofline point (timed live with HIP events on the
+stream it runs on) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-attn fwd useful TFLOP/s (% bf16 MFMA peak) + trajectories/s per GPU"
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (2.5 PFLOP/s class, 2.4 GHz)
+PEAK_F32_TFLOPS = 157.3      # MI355X dense fp32 MFMA
+HBM_GBS = 8000.0
+
+
+def visible_pairs(inp) -> int:
+    """Sum over rows of sum over segments of (ancestor tokens * len + len (len + 1) / 2): the
+    useful-pair count of the tree mask, from the segment table (host integer arithmetic)."""
+    total = 0
+    rp = inp.seg_row_ptr
+    for r in range(inp.n_rows):
+        a, b = int(rp[r]), int(rp[r + 1])
+        depth_tokens = {}
+        for s in range(a, b):
+            p = int(inp.seg_parent[s])
+            n = int(inp.seg_len[s])
+            anc = 0 if p < 0 else depth_tokens[a + p] + int(inp.seg_len[a + p])
+            depth_tokens[s] = anc
+            total += anc * n + n * (n + 1) // 2
+    return total
+
+
+def host_plan_ms(cfg: int, reps: int = 5) -> float | None:
+    """Median host time of tree_pack_plan on this workload expressed as token sequences."""
+    import shared_prefix_tree_parent_amd as ta
+    from workloads import config4_sequences, make_config
+    if cfg == 4:
+        b, _ = config4_sequences(4)
+        tok, off, tr, gr = b.tokens, b.offsets, b.trainable, b.groups
+        C = 4096
+    else:
+        # The row's tree as sequences: a root of P tokens is a (P + 1)-token prompt whose last
+        # token is the join token each branch keeps; branch tokens after it are trainable.
+        inp = make_config(cfg, with_qkv=False)
+        rng = np.random.default_rng(0)
+        seqs, trains = [], []
+        st, ln, par = inp.seg_start, inp.seg_len, inp.seg_parent
+        kids = {s: [c for c in range(len(st)) if par[c] == s] for s in range(len(st))}
+        toks = [rng.integers(0, 32000, int(n)) for n in ln]
+        for leaf in [s for s in range(len(st)) if not kids[s]]:
+            chain = []
+            s = leaf
+            while s >= 0:
+                chain.append(s)
+                s = int(par[s])
+            chain.reverse()
+            x = np.concatenate([toks[s] for s in chain])
+            t = np.zeros(len(x), np.uint8)
+            t[int(sum(ln[s] for s in chain[:-1])) + 1:] = 1
+            seqs.append(x)
+            trains.append(t)
+        off = np.zeros(len(seqs) + 1, np.int64)
+        off[1:] = np.cumsum([len(x) for x in seqs])
+        tok = np.concatenate(seqs).astype(np.int32)
+        tr = np.concatenate(trains)
+        gr = None
+        C = inp.row_len
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        ta.tree_pack_plan(tok, off, tr, gr, C, 64)
+        times.append((time.perf_counter() - t0) * 1e3)
+    return float(np.median(times))
+
+
+def cpu_baseline(inp, pairs_total: int, budget_s: float = 15.0) -> dict:
+    """The float64 oracle, as it stands, on a bounded sample of query positions of the same
+    workload (all heads); scaled to TFLOP/s by the sample's useful FLOPs."""
+    from oracle import attention as A
+    from oracle import mask as M
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    rng = np.random.default_rng(1234)
+    per_row_bits = {}
+    done_flops, done_q, t_used = 0, 0, 0.0
+    batch = 64
+    while t_used < budget_s and done_q < 1 << 20:
+        r = int(rng.integers(0, inp.n_rows))
+        used = int(inp.real_len[r])
+        if used == 0:
+            continue
+        pos = np.sort(rng.integers(0, used, batch))
+        if r not in per_row_bits:
+            per_row_bits = {r: M.visibility_bits(M.row_parents(inp, r))}
+        cnt = sum(int(np.unpackbits(per_row_bits[r][p])[:inp.row_len].sum()) for p in pos)
+        t0 = time.perf_counter()
+        A.attention_at(inp, [(r, int(p)) for p in pos])
+        t_used += time.perf_counter() - t0
+        done_flops += 4 * inp.head_dim * inp.h_q * cnt
+        done_q += batch
+    return {"value": done_flops / t_used / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done_q} random query positions x all {inp.h_q} heads of the same workload "
+                      f"({done_flops / 1e9:.1f} useful GFLOP, float64, {t_used:.1f} s); the full "
+                      f"workload is {4 * inp.head_dim * inp.h_q * pairs_total / 1e9:.0f} GFLOP"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--uniform-lengths", action="store_true", help="config 3 with literal U[100,1000]")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every row and head of this forward is independent, so "
+              "more GPUs would shard rows/heads with no exchange (see the design notes); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import shared_prefix_tree_parent_amd as ta
+    from workloads import CONFIG_NAMES, make_config
+
+    t0 = time.perf_counter()
+    if args.config == 4:
+        inp = make_config(4, packer=lambda b, C, m: ta.pack_batch(b, C, m))
+    else:
+        inp = make_config(args.config, uniform_lengths=args.uniform_lengths)
+    gen_s = time.perf_counter() - t0
+    pairs = visible_pairs(inp)
+    useful = 4.0 * inp.head_dim * inp.h_q * pairs
+
+    dev = "cuda"
+    conv = (lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)) if inp.dtype == "bf16" \
+        else torch.from_numpy
+    q, k, v = (conv(getattr(inp, n)).to(dev) for n in ("q", "k", "v"))
+    plan = ta.attn_plan(inp, device=dev)
+    if plan.status() != ta.TREE_OK:
+        raise RuntimeError("segment table rejected")
+    o = torch.empty_like(q)
+    lse = torch.empty((inp.n_rows, inp.h_q, inp.row_len), dtype=torch.float32, device=dev)
+    tiles = plan.tiles()
+    qt_ptr = plan.ws[tiles["qt_ptr"] - plan.ws.data_ptr():][: 4 * (inp.n_rows * tiles["n_qtiles"] + 1)]
+    n_tiles = int(qt_ptr.cpu().numpy().view(np.int32)[-1])
+    bq, bk = tiles["block_q"], tiles["block_k"]
+    # every non-skip (q-tile, k-tile) is computed for all h_q heads of its row
+    computed = 4.0 * inp.head_dim * bq * bk * n_tiles * inp.h_q
+
+    def fwd():
+        ta.tree_attn_fwd(plan.desc, plan.ws, q, k, v, o, lse)
+
+    def classify():
+        ta.tree_attn_plan(plan.desc, plan.ws)
+
+    def step():
+        classify()
+        fwd()
+
+    def timed(fn, n):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(n):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps)
+    fwd_ms = timed(fwd, args.steps)
+    cls_ms = timed(classify, args.steps)
+
+    peak = PEAK_BF16_TFLOPS if inp.dtype == "bf16" else PEAK_F32_TFLOPS
+    value = useful / (ms_step * 1e-3) / 1e12
+    fwd_tflops = useful / (fwd_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(fwd_tflops / peak, 4), "traffic": None,
+                "kernel": "tree_attn_fwd_kernel", "algorithmic_flops_per_launch": useful,
+                "avg_launch_us": round(fwd_ms * 1e3, 2)}
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": inp.dtype, "data": "synthetic",
+        "config": {"workload": f"config {args.config}: {CONFIG_NAMES[args.config]}"
+                               + (" [uniform rollout lengths]" if args.uniform_lengths else ""),
+                   "rows": inp.n_rows, "row_len": inp.row_len, "h_q": inp.h_q, "h_kv": inp.h_kv,
+                   "head_dim": inp.head_dim, "paths": inp.n_paths, "real_tokens": int(inp.real_len.sum()),
+                   "visible_pairs": pairs, "useful_gflop": round(useful / 1e9, 3),
+                   "computed_gflop": round(computed / 1e9, 3), "tiles": [bq, bk],
+                   "step": "tree_attn_plan + tree_attn_fwd"},
+        "pct_bf16_peak" if inp.dtype == "bf16" else "pct_f32_peak": round(100 * value / peak, 2),
+        "trajectories_per_s": round(inp.n_paths / (ms_step * 1e-3), 1),
+        "fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_trajectories_per_s": round(inp.n_paths / (fwd_ms * 1e-3), 1),
+        "classify_us": round(cls_ms * 1e3, 2),
+        "host_plan_ms": None,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    try:
+        out["host_plan_ms"] = round(host_plan_ms(args.config), 3)
+    except Exception as e:  # host planning is reported, not required for the device step
+        out["host_plan_ms"] = f"error: {e}"
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, pairs, args.cpu_budget)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 5)
+    print(f"# generated inputs in {gen_s:.1f} s", file=sys.stderr)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
