@@ -216,6 +216,7 @@ hipError_t launch_plan(const tree_attn_desc &d, const WsLayout &w, char *ws, hip
 
     // Cleared with a kernel (not a memset node) so the sequence can be captured in a graph.
     zero_words<<<1, 64, 0, s>>>(status, 4);
+    zero_words<<<1, 128, 0, s>>>(reinterpret_cast<int32_t *>(ws + w.zeros), 128);
     if (w.R == 0) {
         zero_words<<<1, 64, 0, s>>>(qt_ptr, 1);
         return hipGetLastError();
