@@ -133,6 +133,8 @@ def main() -> int:
     ap.add_argument("--uniform-lengths", action="store_true", help="config 3 with literal U[100,1000]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every row and head of this forward is independent, so "
@@ -143,6 +145,17 @@ def main() -> int:
     import torch
     import shared_prefix_tree_parent_amd as ta
     from workloads import CONFIG_NAMES, make_config
+
+    if args.copy_mb:
+        # Known-size reference for the HBM byte counters: each launch reads and writes copy_mb MiB.
+        n = args.copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.copy_mb, "launches": max(args.steps, 1)}))
+        return 0
 
     t0 = time.perf_counter()
     if args.config == 4:

@@ -16,139 +16,213 @@ namespace treeattn {
 namespace {
 
 constexpr int kStatusLayout = 1;
+constexpr int kMaxLdsSegs = 2048;   // segments of one row kept in LDS while validating
 
-// One thread per row: check the table is a pre-order forest laid out from token 0, record the
-// row's used length and every segment's subtree end.
+// One workgroup per row: thread 0 checks that the table is a pre-order forest laid out from
+// token 0 and writes every segment's subtree end (the row's segments are staged in LDS when
+// they fit).  A row that fails the check gets n_real = -1 (then kend[j] = j: all skipped).
 __global__ void validate_rows(int32_t R, int32_t T, int32_t n_segs, const int32_t *__restrict__ rp,
                               const int32_t *__restrict__ st, const int32_t *__restrict__ ln,
                               const int32_t *__restrict__ par, int32_t *__restrict__ n_real,
-                              int32_t *__restrict__ seg_end, int32_t *__restrict__ status) {
-    const int32_t r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= R) return;
-    const int32_t a = rp[r], b = rp[r + 1];
-    bool ok = a >= 0 && a <= b && b <= n_segs;
-    if (r == 0 && a != 0) ok = false;
-    if (r == R - 1 && b != n_segs) ok = false;
+                              int32_t *__restrict__ seg_end) {
+    __shared__ int32_t s_st[kMaxLdsSegs], s_len[kMaxLdsSegs], s_par[kMaxLdsSegs];
+    __shared__ int32_t s_a, s_n;
+    const int32_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        const int32_t a = rp[r], b = rp[r + 1];
+        const bool ok = a >= 0 && a <= b && b <= n_segs && (r != 0 || a == 0) && (r != R - 1 || b == n_segs);
+        s_a = ok ? a : 0;
+        s_n = ok ? b - a : -1;
+    }
+    __syncthreads();
+    const int32_t a = s_a, n = s_n;
+    const bool in_lds = n >= 0 && n <= kMaxLdsSegs;
+    if (in_lds) {
+        for (int32_t i = tid; i < n; i += blockDim.x) {
+            s_st[i] = st[a + i];
+            s_len[i] = ln[a + i];
+            s_par[i] = par[a + i];
+        }
+    }
+    __syncthreads();
+    if (tid != 0) return;
+    auto P = [&](int32_t i) { return in_lds ? s_par[i] : par[a + i]; };
+    bool ok = n >= 0;
     int64_t off = 0;
+    for (int32_t s = 0; s < n && ok; ++s) {
+        const int32_t len = in_lds ? s_len[s] : ln[a + s];
+        const int32_t start = in_lds ? s_st[s] : st[a + s];
+        const int32_t p = P(s);
+        if (len < 1 || start != off) { ok = false; break; }
+        if (p != -1) {
+            if (p < 0 || p >= s) { ok = false; break; }
+            // In pre-order the parent lies on the path from the root to the previous segment:
+            // walk up from s-1 (indices strictly decrease; their parents were checked).
+            int32_t x = s - 1;
+            while (x > p) x = P(x);
+            if (x != p) { ok = false; break; }
+        }
+        off += len;
+        if (off > T) { ok = false; break; }
+    }
     if (ok) {
-        for (int32_t s = a; s < b && ok; ++s) {
-            const int32_t ls = s - a, n = ln[s], p = par[s];
-            if (n < 1 || st[s] != off) { ok = false; break; }
-            if (p != -1) {
-                if (p < 0 || p >= ls) { ok = false; break; }
-                // In pre-order the parent must be on the path from the root to the previous
-                // segment: walk up from ls-1 (indices strictly decrease, parents were checked).
-                int32_t x = ls - 1;
-                while (x > p) x = par[a + x];
-                if (x != p) { ok = false; break; }
-            }
-            off += n;
-            if (off > T) { ok = false; break; }
+        // subtree ends: children come after their parent, so one reverse sweep suffices
+        for (int32_t s = 0; s < n; ++s) {
+            const int32_t e = in_lds ? s_st[s] + s_len[s] : st[a + s] + ln[a + s];
+            if (in_lds) s_len[s] = e; else seg_end[a + s] = e;
         }
+        for (int32_t s = n - 1; s >= 0; --s) {
+            const int32_t p = P(s);
+            if (p < 0) continue;
+            if (in_lds) s_len[p] = max(s_len[p], s_len[s]);
+            else seg_end[a + p] = max(seg_end[a + p], seg_end[a + s]);
+        }
+        if (in_lds)
+            for (int32_t s = 0; s < n; ++s) seg_end[a + s] = s_len[s];
     }
-    if (!ok) {
-        n_real[r] = -1;
-        atomicOr(status, kStatusLayout);
-        return;
-    }
-    n_real[r] = static_cast<int32_t>(off);
-    for (int32_t s = a; s < b; ++s) seg_end[s] = st[s] + ln[s];
-    for (int32_t s = b - 1; s >= a; --s) {
-        const int32_t p = par[s];
-        if (p >= 0) seg_end[a + p] = max(seg_end[a + p], seg_end[s]);
-    }
+    n_real[r] = ok ? static_cast<int32_t>(off) : -1;
 }
 
-// kend[j]: subtree end of j's segment for real tokens, j for pads (and for invalid rows).
-__global__ void token_kend(int32_t T, const int32_t *__restrict__ rp, const int32_t *__restrict__ st,
-                           const int32_t *__restrict__ n_real, const int32_t *__restrict__ seg_end,
-                           int32_t *__restrict__ kend) {
+// Grid (k-tile groups, rows), one wave per k-tile: kend of every token of the tile (its
+// segment's subtree end; j itself for pads) and the tile's (min kend, max kend over real keys).
+__global__ void kend_stats(int32_t T, int32_t BK, int32_t nK, const int32_t *__restrict__ rp,
+                           const int32_t *__restrict__ st, const int32_t *__restrict__ n_real,
+                           const int32_t *__restrict__ seg_end, int32_t *__restrict__ kend,
+                           int2 *__restrict__ kt_stats) {
     const int32_t r = blockIdx.y;
-    const int32_t j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= T) return;
+    const int32_t kt = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (kt >= nK) return;
+    const int lane = threadIdx.x & 63;
     const int32_t nr = n_real[r];
-    int32_t out = j;
-    if (nr >= 0 && j < nr) {
-        int32_t lo = rp[r], hi = rp[r + 1] - 1;   // last segment with start <= j
-        while (lo < hi) {
-            const int32_t mid = (lo + hi + 1) >> 1;
-            if (st[mid] <= j) lo = mid; else hi = mid - 1;
-        }
-        out = seg_end[lo];
-    }
-    kend[int64_t(r) * T + j] = out;
-}
-
-// One workgroup per (row, q-tile): exact visible-pair count of every k-tile, its class, and
-// the number of non-skip tiles (written to qt_ptr[tile + 1] for the scan).
-__global__ void classify_tiles(int32_t T, int32_t BQ, int32_t BK, int32_t nQ, int32_t nK,
-                               const int32_t *__restrict__ kend, uint8_t *__restrict__ cmap,
-                               int32_t *__restrict__ qt_ptr) {
-    const int32_t qt = blockIdx.x, r = blockIdx.y;
-    const int32_t q0 = qt * BQ, q1 = q0 + BQ;
-    const int32_t *kr = kend + int64_t(r) * T;
-    uint8_t *cm = cmap + (int64_t(r) * nQ + qt) * nK;
-    int32_t nz = 0;
-    for (int32_t kt = threadIdx.x; kt < nK; kt += blockDim.x) {
-        const int32_t k0 = kt * BK;
-        int64_t c = 0;
-        if (k0 < q1) {
-            for (int32_t j = k0; j < k0 + BK; ++j) {
-                const int32_t hi = min(kr[j], q1), lo = max(j, q0);
-                if (hi > lo) c += hi - lo;
+    const int32_t a = rp[r], n = nr >= 0 ? rp[r + 1] - a : 0;
+    int32_t *kr = kend + int64_t(r) * T;
+    int32_t mn = INT32_MAX, mx = INT32_MIN;
+    for (int32_t o = lane; o < BK; o += 64) {
+        const int32_t j = kt * BK + o;
+        int32_t ke = j;
+        if (j < nr) {
+            int32_t lo = 0, hi = n - 1;   // last segment with start <= j
+            while (lo < hi) {
+                const int32_t mid = (lo + hi + 1) >> 1;
+                if (st[a + mid] <= j) lo = mid; else hi = mid - 1;
             }
+            ke = seg_end[a + lo];
+            mx = max(mx, ke);
         }
-        const uint8_t cls = c == 0 ? kTileSkip : (c == int64_t(BQ) * BK ? kTileFull : kTilePartial);
-        cm[kt] = cls;
-        nz += cls != kTileSkip;
+        kr[j] = ke;
+        mn = min(mn, ke);
     }
-    __shared__ int32_t red[1024 / 64];
-    for (int off = 32; off > 0; off >>= 1) nz += __shfl_xor(nz, off, 64);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = nz;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t t = 0;
-        for (int i = 0; i < int(blockDim.x >> 6); ++i) t += red[i];
-        qt_ptr[int64_t(r) * nQ + qt + 1] = t;
+    for (int off = 32; off > 0; off >>= 1) {
+        mn = min(mn, __shfl_xor(mn, off, 64));
+        mx = max(mx, __shfl_xor(mx, off, 64));
     }
+    if (lane == 0) kt_stats[int64_t(r) * nK + kt] = make_int2(mn, mx);
 }
 
-// Single workgroup: in-place inclusive scan of qt_ptr[1..n], qt_ptr[0] = 0.
-__global__ void scan_counts(int32_t n, int32_t *__restrict__ qt_ptr) {
-    __shared__ int32_t part[1024 / 64];
-    __shared__ int32_t carry;
-    if (threadIdx.x == 0) { carry = 0; qt_ptr[0] = 0; }
-    __syncthreads();
+// One wave per (row, q-tile).  Classes from the k-tile statistics: with segments in pre-order,
+// consecutive real keys j, j+1 have kend[j] >= j+1, so the queries that see at least one key
+// of a tile form the single interval [first real key, max kend).  Hence, for queries
+// [q0, q1) and keys [k0, k0 + BK):
+//   SKIP <=> no real key in the tile, or k0 >= q1, or max kend <= q0;
+//   FULL <=> k0 + BK - 1 <= q0 and min kend (pads count with kend = j) >= q1;
+//   PARTIAL otherwise.
+// These are exactly the zero / all-pairs cases of the visible-pair count.  Writes the class
+// map and the tile's number of non-skip k-tiles to qt_ptr[tile + 1].
+__global__ void classify_tiles(int32_t R, int32_t BQ, int32_t BK, int32_t nQ, int32_t nK,
+                               const int32_t *__restrict__ n_real, const int2 *__restrict__ kt_stats,
+                               uint8_t *__restrict__ cmap, int32_t *__restrict__ qt_ptr) {
+    const int32_t tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (tile >= R * nQ) return;
+    const int lane = threadIdx.x & 63;
+    const int32_t r = tile / nQ, qt = tile % nQ;
+    const int32_t q0 = qt * BQ, q1 = q0 + BQ, nr = n_real[r];
+    const int2 *stats = kt_stats + int64_t(r) * nK;
+    uint8_t *cm = cmap + int64_t(tile) * nK;
+    int32_t cnt = 0;
+    for (int32_t k00 = 0; k00 < nK; k00 += 64) {
+        const int32_t kt = k00 + lane;
+        uint8_t cls = kTileSkip;
+        if (kt < nK) {
+            const int32_t k0 = kt * BK;
+            const int2 sm = stats[kt];
+            const bool skip = !(k0 < nr) || k0 >= q1 || sm.y <= q0;
+            const bool full = k0 + BK - 1 <= q0 && sm.x >= q1;
+            cls = skip ? kTileSkip : (full ? kTileFull : kTilePartial);
+            cm[kt] = cls;
+        }
+        cnt += __popcll(__ballot(cls != kTileSkip));
+    }
+    if (lane == 0) qt_ptr[tile + 1] = cnt;
+}
+
+// In-place inclusive scan of x[1..n] (x[0] = 0) by one workgroup; `rev` scans x[1..n] as if
+// it were reversed (used for descending buckets).
+__device__ void block_scan(int32_t n, int32_t *x, int32_t *part, int32_t *carry) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if (threadIdx.x == 0) *carry = 0;
+    __syncthreads();
     for (int32_t base = 0; base < n; base += blockDim.x) {
         const int32_t i = base + threadIdx.x;
-        int32_t x = i < n ? qt_ptr[i + 1] : 0;
+        int32_t v = i < n ? x[i + 1] : 0;
         for (int off = 1; off < 64; off <<= 1) {
-            const int32_t y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
+            const int32_t y = __shfl_up(v, off, 64);
+            if (lane >= off) v += y;
         }
-        if (lane == 63) part[wv] = x;
+        if (lane == 63) part[wv] = v;
         __syncthreads();
-        int32_t before = carry;
+        int32_t before = *carry;
         for (int w2 = 0; w2 < wv; ++w2) before += part[w2];
-        if (i < n) qt_ptr[i + 1] = x + before;
+        if (i < n) x[i + 1] = v + before;
         __syncthreads();
         if (threadIdx.x == 0) {
             int32_t t = 0;
             for (int w2 = 0; w2 < nw; ++w2) t += part[w2];
-            carry += t;
+            *carry += t;
         }
         __syncthreads();
     }
+}
+
+// One workgroup: CSR offsets (scan of the per-tile counts), the table status word and the
+// work list: q-tiles ordered by their number of non-skip k-tiles, largest
+// first (a counting sort; the order among equal counts does not affect any result).
+__global__ void finish_plan(int32_t R, int32_t nK, int32_t n_tiles, const int32_t *__restrict__ n_real,
+                            int32_t *__restrict__ qt_ptr, int32_t *__restrict__ hist,
+                            int32_t *__restrict__ work, int32_t *__restrict__ status) {
+    __shared__ int32_t part[1024 / 64];
+    __shared__ int32_t carry, bad;
+    if (threadIdx.x == 0) { bad = 0; qt_ptr[0] = 0; }
+    // counts of cost c go to hist[1 + (nK - c)] so that an inclusive scan yields, at
+    // hist[nK - c], the first slot of cost c in descending order.
+    for (int32_t i = threadIdx.x; i < nK + 2; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int32_t r = threadIdx.x; r < R; r += blockDim.x)
+        if (n_real[r] < 0) atomicOr(&bad, 1);
+    block_scan(n_tiles, qt_ptr, part, &carry);
+    __threadfence_block();
+    __syncthreads();
+    for (int32_t t = threadIdx.x; t < n_tiles; t += blockDim.x)
+        atomicAdd(&hist[1 + nK - (qt_ptr[t + 1] - qt_ptr[t])], 1);
+    __threadfence_block();
+    __syncthreads();
+    block_scan(nK + 1, hist, part, &carry);
+    __threadfence_block();
+    __syncthreads();
+    for (int32_t t = threadIdx.x; t < n_tiles; t += blockDim.x) {
+        const int32_t c = qt_ptr[t + 1] - qt_ptr[t];
+        work[atomicAdd(&hist[nK - c], 1)] = t;
+    }
+    if (threadIdx.x == 0) status[0] = bad ? kStatusLayout : 0;
 }
 
 // One wave per (row, q-tile): compact the non-skip k-tiles in ascending order.
 __global__ void fill_lists(int32_t nK, int32_t n_tiles, const uint8_t *__restrict__ cmap,
                            const int32_t *__restrict__ qt_ptr, int32_t *__restrict__ kt_idx,
                            uint8_t *__restrict__ kt_kind) {
-    const int32_t tile = blockIdx.x;
+    const int32_t tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (tile >= n_tiles) return;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const uint8_t *cm = cmap + int64_t(tile) * nK;
     int32_t pos = qt_ptr[tile];
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -165,40 +239,6 @@ __global__ void fill_lists(int32_t nK, int32_t n_tiles, const uint8_t *__restric
     }
 }
 
-// Single workgroup: order q-tiles by their number of non-skip k-tiles, largest first (a
-// counting sort; the order among equal counts is unspecified and does not affect results).
-__global__ void build_worklist(int32_t n_tiles, int32_t nK, const int32_t *__restrict__ qt_ptr,
-                               int32_t *__restrict__ hist, int32_t *__restrict__ work) {
-    for (int32_t c = threadIdx.x; c <= nK + 1; c += blockDim.x) hist[c] = 0;
-    __threadfence();
-    __syncthreads();
-    for (int32_t t = threadIdx.x; t < n_tiles; t += blockDim.x) {
-        const int32_t c = qt_ptr[t + 1] - qt_ptr[t];
-        atomicAdd(&hist[c], 1);
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t run = 0;
-        for (int32_t c = nK; c >= 0; --c) {   // start offset of each count, descending
-            const int32_t h = hist[c];
-            hist[c] = run;
-            run += h;
-        }
-    }
-    __threadfence();
-    __syncthreads();
-    for (int32_t t = threadIdx.x; t < n_tiles; t += blockDim.x) {
-        const int32_t c = qt_ptr[t + 1] - qt_ptr[t];
-        work[atomicAdd(&hist[c], 1)] = t;
-    }
-}
-
-__global__ void zero_words(int32_t *p, int32_t n) {
-    const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0;
-}
-
 }  // namespace
 
 hipError_t launch_plan(const tree_attn_desc &d, const WsLayout &w, char *ws, hipStream_t s) {
@@ -212,23 +252,21 @@ hipError_t launch_plan(const tree_attn_desc &d, const WsLayout &w, char *ws, hip
     uint8_t *kt_kind = reinterpret_cast<uint8_t *>(ws + w.kt_kind);
     int32_t *work = reinterpret_cast<int32_t *>(ws + w.work);
     int32_t *hist = reinterpret_cast<int32_t *>(ws + w.hist);
+    int2 *kt_stats = reinterpret_cast<int2 *>(ws + w.kt_stats);
     const int32_t n_tiles = w.R * w.nQ;
 
-    // Cleared with a kernel (not a memset node) so the sequence can be captured in a graph.
-    zero_words<<<1, 64, 0, s>>>(status, 4);
-    zero_words<<<1, 128, 0, s>>>(reinterpret_cast<int32_t *>(ws + w.zeros), 128);
-    if (w.R == 0) {
-        zero_words<<<1, 64, 0, s>>>(qt_ptr, 1);
-        return hipGetLastError();
+    // No memset nodes: everything the plan needs cleared is cleared by its own kernels.
+    if (w.R > 0) {
+        validate_rows<<<w.R, 256, 0, s>>>(w.R, w.T, d.n_segs, d.seg_row_ptr, d.seg_start, d.seg_len,
+                                          d.seg_parent, n_real, seg_end);
+        kend_stats<<<dim3((w.nK + 3) / 4, w.R), 256, 0, s>>>(w.T, w.BK, w.nK, d.seg_row_ptr, d.seg_start, n_real,
+                                                             seg_end, kend, kt_stats);
+        classify_tiles<<<(n_tiles + 3) / 4, 256, 0, s>>>(w.R, w.BQ, w.BK, w.nQ, w.nK, n_real, kt_stats, cmap,
+                                                         qt_ptr);
     }
-    validate_rows<<<(w.R + 63) / 64, 64, 0, s>>>(w.R, w.T, d.n_segs, d.seg_row_ptr, d.seg_start,
-                                                 d.seg_len, d.seg_parent, n_real, seg_end, status);
-    token_kend<<<dim3((w.T + 255) / 256, w.R), 256, 0, s>>>(w.T, d.seg_row_ptr, d.seg_start, n_real,
-                                                            seg_end, kend);
-    classify_tiles<<<dim3(w.nQ, w.R), 256, 0, s>>>(w.T, w.BQ, w.BK, w.nQ, w.nK, kend, cmap, qt_ptr);
-    scan_counts<<<1, 1024, 0, s>>>(n_tiles, qt_ptr);
-    fill_lists<<<n_tiles, 64, 0, s>>>(w.nK, n_tiles, cmap, qt_ptr, kt_idx, kt_kind);
-    build_worklist<<<1, 1024, 0, s>>>(n_tiles, w.nK, qt_ptr, hist, work);
+    finish_plan<<<1, 1024, 0, s>>>(w.R, w.nK, n_tiles, n_real, qt_ptr, hist, work, status);
+    if (n_tiles > 0)
+        fill_lists<<<(n_tiles + 3) / 4, 256, 0, s>>>(w.nK, n_tiles, cmap, qt_ptr, kt_idx, kt_kind);
     return hipGetLastError();
 }
 
