@@ -28,6 +28,27 @@ METRIC = "tree-attn fwd useful TFLOP/s (% bf16 MFMA peak) + trajectories/s per G
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (2.5 PFLOP/s class, 2.4 GHz)
 PEAK_F32_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 HBM_GBS = 8000.0
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "tree_attn_fwd_config3_traffic.txt")
+
+
+def recorded_traffic(cfg: int, uniform: bool):
+    """HBM bytes per forward launch from the committed counter summary (FETCH_SIZE x 2 +
+    WRITE_SIZE x 1, calibrated against a copy of known size), or None when the summary is for
+    another workload or the forward kernel's source has changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = {}
+        for line in open(TRAFFIC_RECORD):
+            k, sep, v = line.strip().partition(": ")
+            if sep:
+                rec[k] = v.strip()
+        src = os.path.join(ROOT, rec["source"])
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if digest != rec["source_sha256"] or rec["workload"] != f"config {cfg}" or uniform:
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def visible_pairs(inp) -> int:
@@ -213,8 +234,10 @@ def main() -> int:
     value = useful / (ms_step * 1e-3) / 1e12
     fwd_tflops = useful / (fwd_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(fwd_tflops / peak, 4), "traffic": None,
+                "frac": round(fwd_tflops / peak, 4),
+                "traffic": recorded_traffic(args.config, args.uniform_lengths),
                 "kernel": "tree_attn_fwd_kernel", "algorithmic_flops_per_launch": useful,
+                "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE x1)",
                 "avg_launch_us": round(fwd_ms * 1e3, 2)}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
