@@ -189,7 +189,8 @@ int tree_attn_tiles(const tree_attn_desc *d, const void *ws, tree_tile_view *out
  * contents never reach a result.  `ws` must come from tree_attn_plan with the same `d`.
  * bf16: bf16 MFMA with fp32 accumulation, head_dim 64 or 128; f32: fp32 MFMA, head_dim 64.
  * Asynchronous.  Errors: TREE_E_INVAL, TREE_E_UNSUPPORTED (plan tiles differ from
- * tree_attn_blocks, or f32 with head_dim 128), TREE_E_HIP.
+ * tree_attn_blocks, f32 with head_dim 128, or row_len > 507904: a workgroup keeps its q-tile's
+ * list of row_len/64 k-tiles in LDS), TREE_E_HIP.
  */
 int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const void *k,
                   const void *v, void *o, float *lse, void *stream);

@@ -206,60 +206,110 @@ struct F32Traits {
     static constexpr bool kRoundedP = false;
 };
 
-// LDS buffer layout: [K tile][V tile][kend of the tile's 64 keys]; four buffers rotate.
+// LDS layout: four K tiles, then four V tiles, then the four tiles' kend (64 ints each), then
+// the q-tile's k-tile list.  Tile t lives in buffer slot t % 4.  With K and V in regions of
+// their own, every fragment read inside a 64 KB region is one per-lane base register plus an
+// instruction immediate (slot and block offsets are compile-time), so reads cost no address
+// arithmetic.
 template <class Tr>
 struct Lds {
-    static constexpr int TILE = 64 * Tr::D * Tr::kEsz;
-    static constexpr int K_OFF = 0, V_OFF = TILE, KE_OFF = 2 * TILE;
-    static constexpr int BUF = 2 * TILE + 256;
     static constexpr int NBUF = 4;
+    static constexpr int TILE = 64 * Tr::D * Tr::kEsz;   // one K (or V) tile of 64 keys
+    static constexpr int K_OFF = 0;
+    static constexpr int V_OFF = NBUF * TILE;
+    static constexpr int KE_OFF = 2 * NBUF * TILE;
+    static constexpr int LIST_OFF = KE_OFF + NBUF * 256;
+    static_assert(NBUF * TILE <= 65536, "a region must be reachable by 16-bit LDS offsets");
 };
 
-constexpr int kWaves = 8;           // 256 rows = 8 blocks of 32, one per wave
+#ifndef TREEATTN_FWD_BLOCKS_PER_WAVE
+#define TREEATTN_FWD_BLOCKS_PER_WAVE 1
+#endif
+constexpr int kNBlk = TREEATTN_FWD_BLOCKS_PER_WAVE;   // 32-row blocks per wave
+constexpr int kWaves = 8 / kNBlk;                     // 256 rows per workgroup
 constexpr int kBufFlags = 0x00020000;
 
 // Wait until this wave's loads (including the ones into LDS) have landed, or all but the
 // newest n of them (vmcnt(n); the counter's low 4 bits, lgkmcnt / expcnt not waited for).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 template <int N>
-__device__ __forceinline__ void wait_loads_but() { __builtin_amdgcn_s_waitcnt(0x0f70 | N); }
-
-__device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, char *lds, int voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
+__device__ __forceinline__ void wait_loads_but() {
+    static_assert(N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
 }
-__device__ __forceinline__ void buf_to_lds4(__amdgpu_buffer_rsrc_t r, char *lds, int voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
+// Direct-to-LDS buffer loads (no VGPRs): lane l's 16 (or 4) bytes from rsrc + voff land at LDS
+// address lds + 16 l (4 l).  They are issued from inline asm on purpose: the compiler then
+// does not see an LDS write in flight and does not put a wait for all vector loads in front of
+// every later LDS read; the kernel orders the copies itself with counted vmcnt waits and
+// barriers.  The asm has no register outputs; M0 holds the LDS base (one wait state after
+// writing it).  Offsets past num_records read as zeros.
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int32x4_t buf_rsrc(const void *base, uint32_t num_records) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    int32x4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b)));
+    r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(num_records));
+    r[3] = kBufFlags;
+    return r;
+}
+__device__ __forceinline__ void buf_to_lds16(int32x4_t r, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %0, 0 offen lds"
+                 :: "s"(r), "s"(lds), "v"(voff) : "memory", "m0");
+}
+__device__ __forceinline__ void buf_to_lds4(int32x4_t r, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %0, 0 offen lds"
+                 :: "s"(r), "s"(lds), "v"(voff) : "memory", "m0");
+}
+
+// Maxima use IEEE maximum (NaN-propagating; v_maximum3_f32 on gfx950), which needs no
+// canonicalizing moves in front of each operand, unlike fmaxf in IEEE mode.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float xchg_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xchg_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// Max of elements [8i, 8i+8) of x as a tree (short dependency chains).
+__device__ __forceinline__ float max8(const floatx16 &x, int i) {
+    const float a = vmax(vmax(x[8 * i + 0], x[8 * i + 1]), x[8 * i + 2]);
+    const float b = vmax(vmax(x[8 * i + 3], x[8 * i + 4]), x[8 * i + 5]);
+    return vmax(vmax(a, b), vmax(x[8 * i + 6], x[8 * i + 7]));
+}
 
 // ------------------------------------------------------------------------------------ kernel
 //
-// Each wave's work on tile t is split into a softmax phase V(t) (VALU: mask, max, exp, sums,
-// P^T operands) and a matrix phase M(t) = { O^T += V^T P^T for tile t ; S^T = K Q^T for tile
-// t+1 } (MFMA).  Waves 0-3 (group 0) run the sequence S(0), V(0), M(0), V(1), M(1), ... and
-// waves 4-7 (group 1, one per SIMD beside a group-0 wave) run the same sequence one phase
-// later.  Every phase ends with a workgroup barrier, so at any time one wave of each SIMD is
-// in a matrix phase and the other in a softmax phase: the VALU work hides under the MFMAs.
-// K/V tiles rotate through three LDS buffers: tile t is copied during step 2t-1 (ready at the
-// barrier that ends it), first read by group 0 in step 2t and last read by group 1 in step
-// 2t+3; tile t+3 reuses the buffer from step 2t+5.
+// One workgroup = one item = 256 (query head, position) rows = 8 blocks of 32; 4 waves, one
+// per SIMD, wave w owning blocks 2w and 2w+1.  Every K / V fragment a wave reads from LDS
+// feeds two MFMAs (one per block), which halves the LDS read traffic per MFMA.
+//
+// Software pipeline over 32-key steps.  Step u covers block u % 2 (32 keys) of the u / 2-th
+// k-tile of the q-tile's list.  In step u a wave issues the MFMAs of S(u+1) = K Q^T and of
+// O^T += V^T P^T for step u-1, and, slot by slot between them, the VALU softmax of S(u)
+// (computed in step u-1) that yields the P^T operands of step u: the softmax runs under the
+// wave's own MFMAs.  Two register sets hold S and P (A: even steps, B: odd steps); one loop
+// iteration = one 64-key tile = an even and an odd step, so the sets swap roles without
+// copies.  K/V tiles are copied HBM -> LDS two tiles ahead; one barrier per tile.
 template <class Tr>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void tree_attn_fwd_kernel(FwdArgs a) {
     using elem = typename Tr::elem;
     using frag = typename Tr::frag;
+    using LD = Lds<Tr>;
     constexpr int D = Tr::D;
-    // Grow the reference max only when a tile's max exceeds it by more than 2^8 in the
-    // exponent domain; otherwise keep the stale reference (exp2 values stay <= 256), which
-    // keeps O and the sums exactly consistent and skips the accumulator rescale.
+    constexpr int NB = LD::NBUF;
+    // Grow the reference max only when a block's max exceeds it by more than 2^8 in the
+    // exponent domain; otherwise keep the stale reference (weights stay <= 256), which spares
+    // the accumulator rescale.
     constexpr float kGrow = 8.0f;
 
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -267,9 +317,8 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     if (a.status[0] != 0) return;   // invalid segment table: write nothing
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: phases branch per wave
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
-    const int grp = wave >> 2;
     const int bid = blockIdx.x;
     const int u = bid % a.L, item = bid / a.L;
     const int g = u % a.Hkv, chunk = u / a.Hkv;
@@ -278,28 +327,48 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     const int T = a.T;
     const int n_real = a.n_real[r];
 
-    const int hl = wave % a.HCH, pb = wave / a.HCH;
-    const int head = g * a.G + chunk * a.HCH + hl;
-    const int qpos = qt * a.BQ + pb * 32 + l32;
-
-    // Q fragments (B operand of S^T = K Q^T): lane holds query l32, head_dim chunk (2ds + h).
-    frag qf[Tr::NDS];
-    {
-        const elem *qrow = reinterpret_cast<const elem *>(a.q) + ((int64_t(r) * T + qpos) * a.Hq + head) * D;
+    // The wave's two row blocks: block b -> query head of the group (b % HCH) and 32 positions.
+    int head[kNBlk], qpos[kNBlk];
 #pragma unroll
-        for (int ds = 0; ds < Tr::NDS; ++ds) qf[ds] = Tr::q_frag(qrow, ds, h);
+    for (int j = 0; j < kNBlk; ++j) {
+        const int b = kNBlk * wave + j;
+        head[j] = g * a.G + chunk * a.HCH + b % a.HCH;
+        qpos[j] = qt * a.BQ + (b / a.HCH) * 32 + l32;
     }
 
-    floatx16 acc[Tr::NDB];
+    // Q fragments (B operand of S^T = K Q^T): lane holds query l32, head_dim chunk (2ds + h).
+    frag qf[kNBlk][Tr::NDS];
 #pragma unroll
-    for (int db = 0; db < Tr::NDB; ++db) acc[db] = zero16();
+    for (int j = 0; j < kNBlk; ++j) {
+        const elem *qrow = reinterpret_cast<const elem *>(a.q) + ((int64_t(r) * T + qpos[j]) * a.Hq + head[j]) * D;
+#pragma unroll
+        for (int ds = 0; ds < Tr::NDS; ++ds) qf[j][ds] = Tr::q_frag(qrow, ds, h);
+    }
+
+    floatx16 acc[kNBlk][Tr::NDB];
+#pragma unroll
+    for (int j = 0; j < kNBlk; ++j)
+#pragma unroll
+        for (int db = 0; db < Tr::NDB; ++db) acc[j][db] = zero16();
     // m_run: reference max (raw score units); l_run: fp32 sum of the exponentials (for LSE);
     // w_run: sum of the weights as rounded for the PV product (normalizes O, so the weights
     // applied to V sum to one exactly as used).
-    float m_run = -INFINITY, l_run = 0.f, w_run = 0.f;
+    float m_run[kNBlk], l_run[kNBlk], w_run[kNBlk];
+#pragma unroll
+    for (int j = 0; j < kNBlk; ++j) {
+        m_run[j] = -INFINITY;
+        l_run[j] = 0.f;
+        w_run[j] = 0.f;
+    }
 
     const int32_t t_begin = a.qt_ptr[tile];
     const int N = a.qt_ptr[tile + 1] - t_begin;
+    // The q-tile's k-tile list (index * 4 + kind), staged in LDS: list reads in the loop are
+    // LDS reads, never a vector-memory wait that would also wait for the K/V copies in flight.
+    int32_t *const lst = reinterpret_cast<int32_t *>(smem + LD::LIST_OFF);
+    for (int i = tid; i < N; i += kWaves * 64) lst[i] = a.kt_idx[t_begin + i] * 4 + a.kt_kind[t_begin + i];
+    __syncthreads();
+
     const int row_stride = a.Hkv * D * Tr::kEsz;   // bytes between keys
     const char *kbase0 = reinterpret_cast<const char *>(a.k) + ((int64_t(r) * T) * a.Hkv + g) * D * Tr::kEsz;
     const char *vbase0 = reinterpret_cast<const char *>(a.v) + ((int64_t(r) * T) * a.Hkv + g) * D * Tr::kEsz;
@@ -310,241 +379,305 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     // there after swizzling.  The per-lane source offsets never change; the tile base lives in
     // the buffer descriptor, whose size stops at the row's last real key, so pad keys read as
     // zeros (NaN pads cannot reach PV).
-    constexpr int ROWS = 64 / Tr::CPR, INSTR = Tr::CPR, PER_WAVE = 2 * INSTR / kWaves;
+    constexpr int ROWS = 1024 / (D * Tr::kEsz), INSTR = LD::TILE / 1024, PER_WAVE = 2 * INSTR / kWaves;
     static_assert((2 * INSTR) % kWaves == 0, "waves must split the tile evenly");
-    int voff[PER_WAVE], loff[PER_WAVE];
+    static_assert(PER_WAVE + 1 < 16, "vmcnt field");
+    int voff[PER_WAVE];
 #pragma unroll
     for (int jj = 0; jj < PER_WAVE; ++jj) {
-        const int i = wave + kWaves * jj;
         const bool isv = jj >= INSTR / kWaves;
-        const int blk = isv ? i - INSTR : i;
+        const int blk = isv ? wave + kWaves * (jj - INSTR / kWaves) : wave + kWaves * jj;
         const int row = blk * ROWS + lane / Tr::CPR;
         const int c = (lane % Tr::CPR) ^ (isv ? Tr::vsw(row) : Tr::ksw(row));
         voff[jj] = row * row_stride + c * 16;
-        loff[jj] = (isv ? Lds<Tr>::V_OFF : Lds<Tr>::K_OFF) + blk * 1024;
     }
+    // LDS byte address of smem (the dynamic allocation starts at LDS address 0 in practice;
+    // taken from the pointer to stay correct either way).
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)smem)));
     auto issue = [&](int t) __attribute__((always_inline)) {
-        const int kt = __builtin_amdgcn_readfirstlane(a.kt_idx[t_begin + t]);
-        char *bb = smem + (t % Lds<Tr>::NBUF) * Lds<Tr>::BUF;
+        const int kt = __builtin_amdgcn_readfirstlane(lst[t]) >> 2;
+        const int slot = t & (NB - 1);
         const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - kt * 64, 0), 64));
         const int64_t tb = int64_t(kt) * 64 * row_stride;
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char *>(kbase0 + tb), 0, n_valid * row_stride, kBufFlags);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char *>(vbase0 + tb), 0, n_valid * row_stride, kBufFlags);
+        const int32x4_t rk = buf_rsrc(kbase0 + tb, n_valid * row_stride);
+        const int32x4_t rv = buf_rsrc(vbase0 + tb, n_valid * row_stride);
 #pragma unroll
-        for (int jj = 0; jj < PER_WAVE; ++jj)
-            buf_to_lds16(jj >= INSTR / kWaves ? rv : rk, bb + loff[jj], voff[jj]);
-        if (wave == kWaves - 1) {
-            const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<int32_t *>(kend_row + kt * 64), 0, 256, kBufFlags);
-            buf_to_lds4(re, bb + Lds<Tr>::KE_OFF, lane * 4);
+        for (int jj = 0; jj < PER_WAVE; ++jj) {
+            const bool isv = jj >= INSTR / kWaves;
+            const int blk = isv ? wave + kWaves * (jj - INSTR / kWaves) : wave + kWaves * jj;
+            const uint32_t dst = lds0 + (isv ? LD::V_OFF : LD::K_OFF) + slot * LD::TILE + blk * 1024;
+            buf_to_lds16(isv ? rv : rk, dst, voff[jj]);
         }
+        if (wave == kWaves - 1)
+            buf_to_lds4(buf_rsrc(kend_row + kt * 64, 256), lds0 + LD::KE_OFF + slot * 256, lane * 4);
     };
-
-    floatx16 s[2];                  // S^T of the tile the wave works on (two 32-key blocks)
-    frag pf[2][Tr::NKS];            // its P^T operands
 
     // Lane-dependent byte offsets of the K / V fragments inside a tile (loop invariant).
     int klane[Tr::NDS], vlane[Tr::NDB];
 #pragma unroll
     for (int ds = 0; ds < Tr::NDS; ++ds) klane[ds] = Tr::k_lane(ds, l32, h);
 #pragma unroll
-    for (int db = 0; db < Tr::NDB; ++db) vlane[db] = Tr::v_lane(db, lane);
+    for (int db = 0; db < Tr::NDB; ++db) vlane[db] = LD::V_OFF + Tr::v_lane(db, lane);   // V region base folded in
 
-    // Matrix phase as a fixed pipeline of MFMA slots: S^T = K Q^T for tile ts (16 slots) and/or
-    // O^T += V^T P^T for tile tpv (16 slots), interleaved S, PV, S, PV, ...  Each slot's LDS
-    // operand is read kAhead slots earlier into a small ring; scheduling fences keep this
-    // order, so few fragments are in flight (no register pressure from hoisted reads).
-    constexpr int kAhead = 4;
-    auto matrix_ops = [&](auto with_pv, auto with_s, int tpv, int ts) __attribute__((always_inline)) {
-        constexpr bool PV = decltype(with_pv)::value, S = decltype(with_s)::value;
-        // S op n: 32-key block n % 2, head_dim step n / 2 (the two accumulator chains alternate);
-        // PV op n: d-block n % NDB, key step (n / NDB) % NKS, 32-key block n / (NDB * NKS).
-        constexpr int NS_ALL = 2 * Tr::NDS, NPV_ALL = 2 * Tr::NKS * Tr::NDB;
-        static_assert(!(PV && S) || NS_ALL == NPV_ALL, "interleave needs equal slot counts");
-        constexpr int NPV = PV ? NPV_ALL : 0, NS = S ? NS_ALL : 0, NSLOT = NPV + NS;
-        const int bpv = (tpv % Lds<Tr>::NBUF) * Lds<Tr>::BUF, bs = (ts % Lds<Tr>::NBUF) * Lds<Tr>::BUF;
-        // slot i -> (is S op, index within its kind): S, PV, S, PV, ... when both
-        constexpr auto is_s = [](int i) { return (PV && S) ? (i % 2 == 0) : S; };
-        constexpr auto idx = [](int i) { return (PV && S) ? i / 2 : i; };
-        auto load = [&](auto ic) __attribute__((always_inline)) -> frag {
-            constexpr int i = decltype(ic)::value, n = idx(i);
-            if constexpr (is_s(i)) {
-                return Tr::k_frag_at(smem + (bs + klane[n / 2]) + Lds<Tr>::K_OFF + Tr::K_KB_BYTES * (n % 2));
+    constexpr int NLOAD = 2 * Tr::NDS;          // fragment loads per step: K and V alternate
+    static_assert(Tr::NDS == Tr::NDB * Tr::NKS, "S and PV fragments of a step must pair up");
+    static_assert(NLOAD >= 8, "the softmax needs at least 8 load slots per step");
+    constexpr int EPF = 16 / Tr::NKS;           // accumulator elements per P^T operand
+    constexpr int kAhead = 4;                   // LDS fragment reads issued this many slots early
+    static_assert(NLOAD % kAhead == 0, "the ring carries over steps only when kAhead divides NLOAD");
+    floatx16 sA[kNBlk], sB[kNBlk];
+    frag pA[kNBlk][Tr::NKS], pB[kNBlk][Tr::NKS];
+    bool pending = false;                       // the last step grew the reference max of a lane
+    float alpha_p[kNBlk];                       // ... by these factors (1 where not grown)
+#pragma unroll
+    for (int j = 0; j < kNBlk; ++j) alpha_p[j] = 1.f;
+
+    // Step u-1 of step 0 (the first 32 keys) multiplies zero weights by V block 1 of slot
+    // NB-1; clear that block so it holds finite values.
+    {
+        char *z = smem + LD::V_OFF + (NB - 1) * LD::TILE + 32 * D * Tr::kEsz;
+        for (int off = tid * 16; off < 32 * D * Tr::kEsz; off += kWaves * 64 * 16)
+            *reinterpret_cast<uint4 *>(z + off) = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < kNBlk; ++j)
+#pragma unroll
+        for (int ks = 0; ks < Tr::NKS; ++ks) {
+            if constexpr (Tr::kRoundedP) {
+#pragma unroll
+                for (int e = 0; e < EPF; ++e) pB[j][ks][e] = static_cast<__bf16>(0.f);
             } else {
-                constexpr int db = n % Tr::NDB, kb = n / (Tr::NDB * Tr::NKS), ks = (n / Tr::NDB) % Tr::NKS;
-                return Tr::template v_frag_at<kb, ks>(smem + (bpv + vlane[db]) + Lds<Tr>::V_OFF);
+                pB[j][ks] = frag{};
             }
-        };
-        if constexpr (S) {
-            s[0] = zero16();
-            s[1] = zero16();
         }
-        frag ring[kAhead];
-        static_for<(kAhead < NSLOT ? kAhead : NSLOT)>([&](auto ic) __attribute__((always_inline)) {
-            constexpr int i = decltype(ic)::value;
-            ring[i] = load(ic);
-        });
-        static_for<NSLOT>([&](auto ic) __attribute__((always_inline)) {
-            constexpr int i = decltype(ic)::value, n = idx(i);
-            const frag op = ring[i % kAhead];
-            if constexpr (i + kAhead < NSLOT) ring[i % kAhead] = load(std::integral_constant<int, i + kAhead>{});
-            if constexpr (is_s(i)) s[n % 2] = Tr::mfma(op, qf[n / 2], s[n % 2]);
-            else acc[n % Tr::NDB] = Tr::mfma(op, pf[n / (Tr::NDB * Tr::NKS)][(n / Tr::NDB) % Tr::NKS], acc[n % Tr::NDB]);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-    using yes = std::integral_constant<bool, true>;
-    using no = std::integral_constant<bool, false>;
-    auto softmax = [&](int t) __attribute__((always_inline)) {     // online softmax of tile t -> pf
-        if (a.kt_kind[t_begin + t] == kTilePartial) {
-            // Interval mask: key j visible to query i iff j <= i < kend[j].  Register i of block
-            // kb holds key kbase + 4h + c with c = 32kb + 8(i/4) + i%4, so the first test is
-            // c <= qpos - kbase - 4h against an immediate; kend comes four keys at a time.
-            const int32_t *KEs = reinterpret_cast<const int32_t *>(
-                smem + (t % Lds<Tr>::NBUF) * Lds<Tr>::BUF + Lds<Tr>::KE_OFF) + 4 * h;
-            const int dq = qpos - a.kt_idx[t_begin + t] * 64 - 4 * h;
+
+    // Interval mask of key block KB of tile t on both row blocks: key j is visible to query i
+    // iff j <= i < kend[j].  Register i holds key 32 KB + 4h + 8(i/4) + i%4 of the tile, so the
+    // first test is against an immediate; kend comes four keys at a time.
+    auto mask = [&](auto kbc, int t, int kt, floatx16 (&sc)[kNBlk]) __attribute__((always_inline)) {
+        constexpr int KB = decltype(kbc)::value;
+        const int32_t *KEs = reinterpret_cast<const int32_t *>(smem + LD::KE_OFF + (t & (NB - 1)) * 256) + 4 * h;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int4 ke = *reinterpret_cast<const int4 *>(KEs + 32 * KB + 8 * i4);
+            const int kev[4] = {ke.x, ke.y, ke.z, ke.w};
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const int4 ke = *reinterpret_cast<const int4 *>(KEs + 32 * kb + 8 * i4);
-                    const int kev[4] = {ke.x, ke.y, ke.z, ke.w};
+            for (int j = 0; j < kNBlk; ++j) {
+                const int dq = qpos[j] - kt * 64 - 4 * h;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int c = 32 * kb + 8 * i4 + e;
-                        const bool vis = (c <= dq) & (qpos < kev[e]);
-                        s[kb][4 * i4 + e] = vis ? s[kb][4 * i4 + e] : -INFINITY;
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 32 * KB + 8 * i4 + e;
+                    const bool vis = (c <= dq) & (qpos[j] < kev[e]);
+                    sc[j][4 * i4 + e] = vis ? sc[j][4 * i4 + e] : -INFINITY;
                 }
+            }
         }
-        float mx = s[0][0];
+    };
+    auto rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = xchg_max(mx);
-        const bool grow = mx * a.c > m_run * a.c + kGrow;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float m_new = grow ? mx : m_run;
-            const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * a.c) : 1.f;
-            l_run *= alpha;
-            w_run *= alpha;
+        for (int j = 0; j < kNBlk; ++j)
 #pragma unroll
             for (int db = 0; db < Tr::NDB; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-            m_run = m_new;
+                for (int i = 0; i < 16; ++i) acc[j][db][i] *= alpha_p[j];
+    };
+
+    // LDS offsets of a step's fragments: step (t, KB) computes S(u+1) from block 1-KB of tile
+    // t+KB (past the last tile: stale LDS, never used) and PV(u-1) from block 1-KB of tile
+    // t-1+KB.  V offsets are relative to vlane (which holds the V region base).
+    auto koff = [&](int t, int KB) __attribute__((always_inline)) {
+        return LD::K_OFF + ((t + KB) & (NB - 1)) * LD::TILE + (1 - KB) * Tr::K_KB_BYTES;
+    };
+    auto voff_of = [&](int t, int KB) __attribute__((always_inline)) {
+        return ((t + KB + NB - 1) & (NB - 1)) * LD::TILE;
+    };
+    // Fragment of load slot i of a step whose V block is VB: even slots K, odd slots V.
+    auto load = [&](auto ic, auto vbc, int ko, int vo) __attribute__((always_inline)) -> frag {
+        constexpr int i = decltype(ic)::value, n = i / 2, VB = decltype(vbc)::value;
+        if constexpr (i % 2 == 0) {
+            return Tr::k_frag_at(smem + klane[n] + ko);
+        } else {
+            constexpr int db = n % Tr::NDB, ks = n / Tr::NDB;
+            return Tr::template v_frag_at<VB, ks>(smem + vlane[db] + vo);
         }
-        const float mc = (m_run == -INFINITY ? 0.f : m_run) * a.c;
-        float ls = 0.f;
+    };
+    frag ring[kAhead];              // operand reads in flight, carried from step to step
+
+    // One pipeline step (u = 2t + KB): softmax of sc = S(u) into pc; S(u+1) into sn; PV(u-1)
+    // with weights pp.  VALU work is spread over the load slots: block maxima in slots 0-1,
+    // the reference update in slot 2, the exponentials (with their bf16 operands and weight
+    // sums) over slots 3 .. NLOAD-2.  The last kAhead slots read the first operands of the
+    // next step, so no step starts by waiting for LDS.
+    auto step = [&](auto kbc, int t, int ent, floatx16 (&sc)[kNBlk], floatx16 (&sn)[kNBlk],
+                    frag (&pc)[kNBlk][Tr::NKS], const frag (&pp)[kNBlk][Tr::NKS]) __attribute__((always_inline)) {
+        constexpr int KB = decltype(kbc)::value;
+        using vb_this = std::integral_constant<int, 1 - KB>;
+        using vb_next = std::integral_constant<int, KB>;          // the next step has KB' = 1 - KB
+        const int ko = koff(t, KB), vo = voff_of(t, KB);
+        const int tn = t + KB;                                     // tile of the next step
+        const int ko_n = koff(tn, 1 - KB), vo_n = voff_of(tn, 1 - KB);
+        if (pending) rescale();   // rare: the reference max grew in the previous step
+        if ((ent & 3) == kTilePartial) mask(kbc, t, ent >> 2, sc);
+        float mx[kNBlk][2], alpha[kNBlk], mc[kNBlk];
+        bool grow[kNBlk];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int j = 0; j < kNBlk; ++j) {
+            alpha[j] = 1.f;
+            mc[j] = 0.f;
+            grow[j] = false;
+        }
+        static_for<NLOAD>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value, n = i / 2;
+            const frag op = ring[i % kAhead];
+            if constexpr (i + kAhead < NLOAD) ring[i % kAhead] = load(std::integral_constant<int, i + kAhead>{}, vb_this{}, ko, vo);
+            else ring[i % kAhead] = load(std::integral_constant<int, i + kAhead - NLOAD>{}, vb_next{}, ko_n, vo_n);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.c, -mc));
-                s[kb][i] = e;
-                ls += e;
+            for (int j = 0; j < kNBlk; ++j) {
+                if constexpr (i % 2 == 0) {
+                    if constexpr (n == 0) sn[j] = Tr::mfma(op, qf[j][0], zero16());
+                    else sn[j] = Tr::mfma(op, qf[j][n], sn[j]);
+                } else {
+                    constexpr int db = n % Tr::NDB, ks = n / Tr::NDB;
+                    acc[j][db] = Tr::mfma(op, pp[j][ks], acc[j][db]);
+                }
             }
+            // Block maxima: partial maxima of 8 elements each over slots 0 and 1.
+            if constexpr (i == 0 || i == 1) {
 #pragma unroll
-            for (int ks = 0; ks < Tr::NKS; ++ks) {
-                pf[kb][ks] = Tr::p_frag(s[kb], ks);
-                if constexpr (Tr::kRoundedP) w_run = Tr::wsum(pf[kb][ks], w_run);
+                for (int j = 0; j < kNBlk; ++j) mx[j][i] = max8(sc[j], i);
             }
+            if constexpr (i == 2) {
+                // Grow the reference max only when a block's max exceeds it by more than 2^8 in
+                // the exponent domain; otherwise keep the stale reference (weights stay <= 256),
+                // which spares the accumulator rescale.
+#pragma unroll
+                for (int j = 0; j < kNBlk; ++j) {
+                    const float m = xchg_max(vmax(mx[j][0], mx[j][1]));
+                    grow[j] = m * a.c > m_run[j] * a.c + kGrow;
+                    const float m_new = grow[j] ? m : m_run[j];
+                    alpha[j] = grow[j] ? __builtin_amdgcn_exp2f((m_run[j] - m_new) * a.c) : 1.f;
+                    l_run[j] *= alpha[j];
+                    w_run[j] *= alpha[j];
+                    m_run[j] = m_new;
+                    mc[j] = (m_new == -INFINITY ? 0.f : m_new) * a.c;
+                }
+            }
+            static_for<16 * kNBlk>([&](auto ec) __attribute__((always_inline)) {
+                constexpr int e = decltype(ec)::value, j = e % kNBlk, k = e / kNBlk;
+                if constexpr (3 + (e * (NLOAD - 4)) / (16 * kNBlk) == i) {
+                    const float x = __builtin_amdgcn_exp2f(fmaf(sc[j][k], a.c, -mc[j]));
+                    sc[j][k] = x;
+                    l_run[j] += x;
+                    if constexpr (k % EPF == EPF - 1) {
+                        pc[j][k / EPF] = Tr::p_frag(sc[j], k / EPF);
+                        if constexpr (Tr::kRoundedP) w_run[j] = Tr::wsum(pc[j][k / EPF], w_run[j]);
+                    }
+                }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // Keep this step's P^T operands and sums computed here: without a use at this point
+        // the compiler sinks the exponentials past the next step's rescale branch, out of the
+        // MFMA slots they are meant to fill.
+        bool any_grow = false;
+#pragma unroll
+        for (int j = 0; j < kNBlk; ++j) {
+#pragma unroll
+            for (int ks = 0; ks < Tr::NKS; ++ks) asm volatile("" ::"v"(pc[j][ks]));
+            asm volatile("" ::"v"(l_run[j]), "v"(w_run[j]));
+            any_grow |= grow[j];
+            alpha_p[j] = alpha[j];
         }
-        l_run += ls;
+        pending = __builtin_amdgcn_ballot_w64(any_grow) != 0;
     };
 
-    auto matrix_phase = [&](int t) __attribute__((always_inline)) {   // M(t): PV of tile t and S of tile t+1
-        __builtin_amdgcn_s_setprio(1);
-        // One code path for every tile (two variants in the loop cost ~70 spilled registers);
-        // on the last tile the S slots recompute S of the same tile, which is never used.
-        matrix_ops(yes{}, yes{}, t, t + 1 < N ? t + 1 : t);
-        __builtin_amdgcn_s_setprio(0);
-    };
-    auto first_s = [&]() __attribute__((always_inline)) {
-        __builtin_amdgcn_s_setprio(1);
-        matrix_ops(no{}, yes{}, 0, 0);
-        __builtin_amdgcn_s_setprio(0);
-    };
-
-    // Steps are numbered globally; barrier #n ends step n.  Group 0: step 1 S(0), step 2t+2
-    // V(t), step 2t+3 M(t); group 1 runs one step later.  Tile s is copied in two halves:
-    // group 1's waves issue theirs in step 2s-3, group 0's in step 2s-2 (tiles 0 and 1 in the
-    // prologue), each at the start of a softmax phase.  Tile s is first read in step 2s+1, so
-    // at the end of step 2s every wave waits for its copies of tile s only (the next tile's
-    // may stay in flight: two steps of lead time).  Tile s+4 reuses tile s's buffer from step
-    // 2s+5; tile s is last read in step 2s+4.  Both groups pass 2N+3 barriers.
-    int step = 0, issued = -1;
-    auto issue_tile = [&](int t) __attribute__((always_inline)) {
-        issue(t);
-        issued = t;
-    };
-    auto step_end = [&]() __attribute__((always_inline)) {
-        if ((step & 1) == 0 && (step >> 1) < N) {
-            if (issued <= (step >> 1)) wait_loads_but<0>();
-            else if (wave == kWaves - 1) wait_loads_but<PER_WAVE + 1>();
-            else wait_loads_but<PER_WAVE>();
-        }
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        ++step;
-    };
-
-    if (N > 0) issue_tile(0);
-    if (N > 1) issue_tile(1);
-    step_end();                                   // step 0
-    if (grp == 1) {
-        if (N > 2) issue_tile(2);                 // step 1
-        step_end();
+    // Prologue: tiles 0 and 1 in flight, wait for tile 0, S(0) of both blocks.
+    if (N > 0) issue(0);
+    if (N > 1) {
+        issue(1);
+        if (wave == kWaves - 1) wait_loads_but<PER_WAVE + 1>();
+        else wait_loads_but<PER_WAVE>();
+    } else {
+        wait_loads();
     }
-    if (N > 0) first_s();                         // step 1 (group 0) / 2 (group 1)
-    step_end();
+    block_barrier();
+    if (N > 0) {
+        static_for<Tr::NDS>([&](auto nc) __attribute__((always_inline)) {
+            constexpr int n = decltype(nc)::value;
+            const frag op = Tr::k_frag_at(smem + klane[n] + LD::K_OFF);
+#pragma unroll
+            for (int j = 0; j < kNBlk; ++j) {
+                if constexpr (n == 0) sA[j] = Tr::mfma(op, qf[j][0], zero16());
+                else sA[j] = Tr::mfma(op, qf[j][n], sA[j]);
+            }
+        });
+    }
+    static_for<kAhead>([&](auto ic) __attribute__((always_inline)) {
+        ring[decltype(ic)::value] = load(ic, std::integral_constant<int, 1>{}, koff(0, 0), voff_of(0, 0));
+    });
     for (int t = 0; t < N; ++t) {
-        if (t + 2 + grp < N) issue_tile(t + 2 + grp);
-        softmax(t);
-        step_end();
-        matrix_phase(t);
-        step_end();
+        // Tile t+1 (read from step 2t+1 on) must have landed, and every wave must be done
+        // with tile t-2 (last read in step 2t-2) before its buffer takes tile t+2.
+        if (t + 1 < N) wait_loads();
+        block_barrier();
+        const int ent = __builtin_amdgcn_readfirstlane(lst[t]);
+        if (t + 2 < N) issue(t + 2);
+        step(std::integral_constant<int, 0>{}, t, ent, sA, sB, pA, pB);
+        step(std::integral_constant<int, 1>{}, t, ent, sB, sA, pB, pA);
     }
-    if (grp == 0) step_end();                     // step 2N+2
+    // Drain: PV of the last step (block 1 of tile N-1, weights pB).
+    if (N > 0) {
+        if (pending) rescale();
+        const char *vb = smem + ((N - 1) & (NB - 1)) * LD::TILE;
+        static_for<Tr::NDB * Tr::NKS>([&](auto nc) __attribute__((always_inline)) {
+            constexpr int n = decltype(nc)::value, db = n % Tr::NDB, ks = n / Tr::NDB;
+            const frag op = Tr::template v_frag_at<1, ks>(vb + vlane[db]);
+#pragma unroll
+            for (int j = 0; j < kNBlk; ++j) acc[j][db] = Tr::mfma(op, pB[j][ks], acc[j][db]);
+        });
+    }
 
     // Epilogue: combine the two lane halves' partial sums, normalize, write O and LSE.
-    const float l_tot = xchg_sum(l_run);
-    const float w_tot = Tr::kRoundedP ? xchg_sum(w_run) : l_tot;
-    const float inv = w_tot > 0.f ? 1.f / w_tot : 0.f;
-    elem *op = reinterpret_cast<elem *>(a.o) + ((int64_t(r) * T + qpos) * a.Hq + head) * D;
 #pragma unroll
-    for (int db = 0; db < Tr::NDB; ++db) {
+    for (int j = 0; j < kNBlk; ++j) {
+        const float l_tot = xchg_sum(l_run[j]);
+        const float w_tot = Tr::kRoundedP ? xchg_sum(w_run[j]) : l_tot;
+        const float inv = w_tot > 0.f ? 1.f / w_tot : 0.f;
+        elem *op = reinterpret_cast<elem *>(a.o) + ((int64_t(r) * T + qpos[j]) * a.Hq + head[j]) * D;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            const int d0 = 32 * db + 8 * i4 + 4 * h;
-            float vals[4];
+        for (int db = 0; db < Tr::NDB; ++db) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vals[e] = acc[db][4 * i4 + e] * inv;
-            if constexpr (Tr::kEsz == 2) {
-                uint2 w;
-                w.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[0]))) |
-                      (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[1]))) << 16);
-                w.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[2]))) |
-                      (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[3]))) << 16);
-                *reinterpret_cast<uint2 *>(op + d0) = w;
-            } else {
-                *reinterpret_cast<float4 *>(op + d0) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int d0 = 32 * db + 8 * i4 + 4 * h;
+                float vals[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vals[e] = acc[j][db][4 * i4 + e] * inv;
+                if constexpr (Tr::kEsz == 2) {
+                    uint2 w;
+                    w.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[0]))) |
+                          (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[1]))) << 16);
+                    w.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[2]))) |
+                          (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[3]))) << 16);
+                    *reinterpret_cast<uint2 *>(op + d0) = w;
+                } else {
+                    *reinterpret_cast<float4 *>(op + d0) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+                }
             }
         }
-    }
-    if (h == 0) {
-        const float lse = l_tot > 0.f ? m_run * a.scale + __logf(l_tot) : -INFINITY;
-        a.lse[(int64_t(r) * a.Hq + head) * T + qpos] = lse;
+        if (h == 0) {
+            const float lse = l_tot > 0.f ? m_run[j] * a.scale + __logf(l_tot) : -INFINITY;
+            a.lse[(int64_t(r) * a.Hq + head[j]) * T + qpos[j]] = lse;
+        }
     }
 }
 
 template <class Tr>
 hipError_t launch_tr(const FwdArgs &args, int n_blocks, hipStream_t s) {
-    constexpr int smem = Lds<Tr>::NBUF * Lds<Tr>::BUF;
+    const int max_list = args.T / kFwdBlockK;
+    if (max_list > kFwdMaxKTiles) return hipErrorInvalidValue;
+    const int smem = Lds<Tr>::LIST_OFF + 4 * ((max_list + 3) & ~3);
+    if (smem > 160 * 1024) return hipErrorInvalidValue;
     auto kern = tree_attn_fwd_kernel<Tr>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);

@@ -114,6 +114,7 @@ extern "C" int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void
     fwd_blocks(d, &bq, &bk);
     if (w.BQ != bq || w.BK != bk) return TREE_E_UNSUPPORTED;
     if (d->dtype == TREE_DT_F32 && d->head_dim != 64) return TREE_E_UNSUPPORTED;
+    if (w.nK > kFwdMaxKTiles) return TREE_E_UNSUPPORTED;
     FwdShape sh;
     sh.R = d->n_rows; sh.T = d->row_len; sh.Hq = d->h_q; sh.Hkv = d->h_kv; sh.D = d->head_dim;
     sh.dtype = d->dtype;
@@ -134,7 +135,7 @@ extern "C" const char *tree_status_str(int code) {
         case TREE_E_LAYOUT: return "segment table is not a valid pre-order forest layout";
         case TREE_E_NOMEM: return "out of host memory";
         case TREE_E_HIP: return "HIP runtime or launch error";
-        case TREE_E_UNSUPPORTED: return "no kernel for these arguments (plan tile sizes differ from the forward kernel's)";
+        case TREE_E_UNSUPPORTED: return "no kernel for these arguments (plan tile sizes differ from the forward kernel's, or the row is too long)";
         default: return "unknown status";
     }
 }

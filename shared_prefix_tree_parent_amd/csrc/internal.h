@@ -12,6 +12,9 @@ namespace treeattn {
 constexpr int kTileSkip = 0, kTileFull = 1, kTilePartial = 2;
 constexpr int kFwdBlockK = 64;        // keys per k-tile in the forward kernel
 constexpr int kFwdRowsPerWG = 256;    // (query head, position) rows one forward workgroup owns
+// Longest k-tile list the forward keeps in LDS beside its four 33 KB K/V buffers (160 KB per
+// workgroup): row_len <= 64 * 7936 = 507904.
+constexpr int kFwdMaxKTiles = 7936;
 
 // Device workspace layout: every section 256-byte aligned, offsets from the base pointer.
 struct WsLayout {
