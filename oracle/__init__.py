@@ -3,7 +3,8 @@
 Plain, slow, obviously-correct reference implementations of what the GPU path
 computes: the radix segment build and best-fit-decreasing row packing
 (``oracle.packer``), the token-forest attention mask and tile classes
-(``oracle.mask``) and masked softmax attention in float64 (``oracle.attention``).
+(``oracle.mask``) and masked softmax attention in float64, forward and gradients
+(``oracle.attention``).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path (the C-ABI library and

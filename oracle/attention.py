@@ -172,3 +172,143 @@ def real_positions(inp):
     for r in range(R):
         out[r] = row_parents(inp, r) != PAD
     return out
+
+
+# ------------------------------------------------------------------------------- backward
+#
+# Gradients of the same masked attention for an upstream gradient dO ([PTP]: the packing
+# exists for training, where every layer is differentiated).  With P = softmax(S) over the
+# visible keys of each query (P = 0 elsewhere), O = P V and scale folded into S:
+#
+#   dV = P^T dO                 (summed over the G query heads of a KV head)
+#   dP = dO V^T
+#   D_i = sum_d dO[i,d] O[i,d]  (= sum_j P_ij dP_ij)
+#   dS = P * (dP - D)           (elementwise; rows of the softmax Jacobian)
+#   dQ = scale * dS K
+#   dK = scale * dS^T Q         (summed over the G query heads)
+#
+# Pads: no query sees them and they see nothing, so dQ, dK, dV are 0 there and pad contents
+# of Q/K/V/dO never enter a result.
+
+
+def attention_backward_blocked(inp, dO, rows=None, dtype=np.float64):
+    """Whole-row gradients by the segment decomposition: (dQ [R,T,Hq,D], dK, dV [R,T,Hkv,D]).
+
+    ``dO`` has Q's layout and dtype (bf16 bit patterns or float32).  Per segment and KV head,
+    the keys are all tokens of the ancestor segments followed by the segment's own tokens
+    under a causal mask (as in ``attention_segment_blocked``); gradients of shared keys are
+    summed over every segment whose queries see them.
+    """
+    R, T = int(_get(inp, "n_rows")), int(_get(inp, "row_len"))
+    Hq, Hkv = int(_get(inp, "h_q")), int(_get(inp, "h_kv"))
+    D, scale = int(_get(inp, "head_dim")), float(_get(inp, "scale"))
+    G = Hq // Hkv
+    rows = range(R) if rows is None else rows
+    rp = _get(inp, "seg_row_ptr")
+    bf16 = _get(inp, "dtype") == "bf16"
+    dq = np.zeros((R, T, Hq, D), dtype)
+    dk = np.zeros((R, T, Hkv, D), dtype)
+    dv = np.zeros((R, T, Hkv, D), dtype)
+    for r in rows:
+        a, b = int(rp[r]), int(rp[r + 1])
+        if b == a:
+            continue
+        st = _get(inp, "seg_start")[a:b]
+        ln = _get(inp, "seg_len")[a:b]
+        par = _get(inp, "seg_parent")[a:b]
+        q = _f64(inp, "q", r).astype(dtype)
+        k = _f64(inp, "k", r).astype(dtype)
+        v = _f64(inp, "v", r).astype(dtype)
+        g_o = dO[r]
+        if bf16:
+            g_o = (np.asarray(g_o, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+        g_o = np.asarray(g_o, dtype)
+        for s in range(b - a):
+            own = np.arange(st[s], st[s] + ln[s])
+            keys = np.concatenate([np.arange(st[p], st[p] + ln[p]) for p in segment_ancestors(par, s)]
+                                  + [own])
+            n_anc = len(keys) - len(own)
+            vis = np.ones((len(own), len(keys)), bool)
+            vis[:, n_anc:] = np.tril(np.ones((len(own), len(own)), bool))
+            for g in range(Hkv):
+                hs = slice(g * G, (g + 1) * G)
+                qg = q[own][:, hs, :]                                  # [n, G, D]
+                dog = g_o[own][:, hs, :]                               # [n, G, D]
+                kg = k[keys, g, :]                                     # [m, D]
+                vg = v[keys, g, :]
+                S = scale * np.matmul(qg, kg.T)                        # [n, G, m]
+                S = np.where(vis[:, None, :], S, -np.inf)
+                m = S.max(axis=-1, keepdims=True)
+                P = np.exp(S - m)
+                P /= P.sum(axis=-1, keepdims=True)                     # softmax, 0 where masked
+                O = np.matmul(P, vg)                                   # [n, G, D]
+                Dl = (dog * O).sum(axis=-1, keepdims=True)             # [n, G, 1]
+                dP = np.matmul(dog, vg.T)                              # [n, G, m]
+                dS = P * (dP - Dl)
+                dq[r, own, hs, :] = scale * np.matmul(dS, kg)
+                dk[r, keys, g, :] += scale * np.einsum("ngm,ngd->md", dS, qg)
+                dv[r, keys, g, :] += np.einsum("ngm,ngd->md", P, dog)
+    return dq, dk, dv
+
+
+def attention_grad_at(inp, dO, q_samples=(), k_samples=()):
+    """Gradients at chosen positions, for inputs too large for whole rows.
+
+    dQ at (row, query) pairs: the query's own softmax over anc*(i) (parent walk), then
+    dS and dQ as in the closed form.  dK, dV at (row, key) pairs: every query i whose anc*(i)
+    holds the key (a column of the parent-walk bit matrix) contributes; each such query's O and
+    LSE come from ``attention_at``.  Returns (dQ [nq, Hq, D], dK [nk, Hkv, D], dV [nk, Hkv, D]).
+    """
+    Hq, Hkv = int(_get(inp, "h_q")), int(_get(inp, "h_kv"))
+    D, scale = int(_get(inp, "head_dim")), float(_get(inp, "scale"))
+    T = int(_get(inp, "row_len"))
+    G = Hq // Hkv
+    bf16 = _get(inp, "dtype") == "bf16"
+
+    def g_o(r, idx):
+        a = dO[r][idx]
+        if bf16:
+            a = (np.asarray(a, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+        return np.asarray(a, np.float64)
+
+    dq = np.zeros((len(q_samples), Hq, D))
+    for n, (r, i) in enumerate(q_samples):
+        bits = visibility_bits(row_parents(inp, r))
+        keys = np.flatnonzero(np.unpackbits(bits[i])[:T])
+        if len(keys) == 0:
+            continue
+        qi = _f64(inp, "q", (r, i))                                    # [Hq, D]
+        kk = _f64(inp, "k", (r, keys))                                 # [m, Hkv, D]
+        vv = _f64(inp, "v", (r, keys))
+        do = g_o(r, i)                                                 # [Hq, D]
+        for h in range(Hq):
+            g = h // G
+            s = scale * (kk[:, g, :] @ qi[h])
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o = p @ vv[:, g, :]
+            dp = vv[:, g, :] @ do[h]
+            ds = p * (dp - do[h] @ o)
+            dq[n, h] = scale * (ds @ kk[:, g, :])
+
+    dk = np.zeros((len(k_samples), Hkv, D))
+    dv = np.zeros((len(k_samples), Hkv, D))
+    for n, (r, j) in enumerate(k_samples):
+        bits = visibility_bits(row_parents(inp, r))
+        col = np.unpackbits(bits, axis=1)[:, :T][:, j].astype(bool)
+        queries = np.flatnonzero(col)
+        if len(queries) == 0:
+            continue
+        O, L = attention_at(inp, [(r, int(i)) for i in queries])       # [nq, Hq, D], [nq, Hq]
+        qq = _f64(inp, "q", (r, queries))                              # [nq, Hq, D]
+        do = g_o(r, queries)
+        kj = _f64(inp, "k", (r, j))                                    # [Hkv, D]
+        vj = _f64(inp, "v", (r, j))
+        for h in range(Hq):
+            g = h // G
+            p = np.exp(scale * (qq[:, h, :] @ kj[g]) - L[:, h])          # [nq]
+            dp = do[:, h, :] @ vj[g]
+            ds = p * (dp - (do[:, h, :] * O[:, h, :]).sum(axis=1))
+            dv[n, g] += p @ do[:, h, :]
+            dk[n, g] += scale * (ds @ qq[:, h, :])
+    return dq, dk, dv
