@@ -195,6 +195,34 @@ int tree_attn_tiles(const tree_attn_desc *d, const void *ws, tree_tile_view *out
 int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const void *k,
                   const void *v, void *o, float *lse, void *stream);
 
+/*
+ * Backward of tree_attn_fwd ([PTP]: the packing serves training, so every attention layer is
+ * differentiated).  For an upstream gradient dO of O, with P the softmax of the visible
+ * scores and D_i = sum_d dO[i,h,d] O[i,h,d]:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q,
+ * dK / dV summed over the query heads of each KV head.  Pads get zero gradients; pad contents
+ * of q/k/v/o/dO never reach a result.  bf16 only (TREE_E_UNSUPPORTED otherwise); the plan in
+ * `ws` must use the forward's tile sizes (tree_attn_blocks).
+ *
+ * tree_attn_bwd_workspace_size: bytes of the caller-allocated backward workspace `bws`
+ *   (256-byte aligned): per-token row terms D [R, Hq, T] fp32 plus the per-k-tile lists.
+ * tree_attn_bwd_plan: from the forward plan in `ws`, build into `bws` the lists of q-tiles that
+ *   see each k-tile (the transposed tile lists: ascending q-tile, entry = q_tile * 4 + class)
+ *   and the order of the k-tile work.  Once per batch, like tree_attn_plan; asynchronous.
+ * tree_attn_bwd_tiles: device pointers (into bws) of those lists, for tests:
+ *   kt_ptr[R * n_ktiles + 1] CSR over (row, k-tile), q_list the entries.
+ * tree_attn_bwd: q, k, v as given to tree_attn_fwd; o and lse as it returned them; dout in
+ *   q's layout; writes dq (q's layout), dk and dv (k's layout), bf16.  Uses D in bws (it
+ *   overwrites it).  Asynchronous.  Errors: TREE_E_INVAL, TREE_E_UNSUPPORTED, TREE_E_HIP.
+ */
+int tree_attn_bwd_workspace_size(const tree_attn_desc *d, size_t *bytes);
+int tree_attn_bwd_plan(const tree_attn_desc *d, const void *ws, void *bws, void *stream);
+int tree_attn_bwd_tiles(const tree_attn_desc *d, const void *bws, const int32_t **kt_ptr,
+                        const int32_t **q_list);
+int tree_attn_bwd(const tree_attn_desc *d, const void *ws, void *bws, const void *q, const void *k,
+                  const void *v, const void *o, const float *lse, const void *dout, void *dq,
+                  void *dk, void *dv, void *stream);
+
 const char *tree_status_str(int code);
 
 #ifdef __cplusplus

@@ -246,8 +246,9 @@ def attention_backward_blocked(inp, dO, rows=None, dtype=np.float64):
                 dP = np.matmul(dog, vg.T)                              # [n, G, m]
                 dS = P * (dP - Dl)
                 dq[r, own, hs, :] = scale * np.matmul(dS, kg)
-                dk[r, keys, g, :] += scale * np.einsum("ngm,ngd->md", dS, qg)
-                dv[r, keys, g, :] += np.einsum("ngm,ngd->md", P, dog)
+                n, m_ = len(own), len(keys)                            # sums over (query, head)
+                dk[r, keys, g, :] += scale * (dS.reshape(n * G, m_).T @ qg.reshape(n * G, D))
+                dv[r, keys, g, :] += P.reshape(n * G, m_).T @ dog.reshape(n * G, D)
     return dq, dk, dv
 
 
@@ -272,8 +273,11 @@ def attention_grad_at(inp, dO, q_samples=(), k_samples=()):
         return np.asarray(a, np.float64)
 
     dq = np.zeros((len(q_samples), Hq, D))
+    row_bits: dict = {}
     for n, (r, i) in enumerate(q_samples):
-        bits = visibility_bits(row_parents(inp, r))
+        if r not in row_bits:
+            row_bits[r] = visibility_bits(row_parents(inp, r))
+        bits = row_bits[r]
         keys = np.flatnonzero(np.unpackbits(bits[i])[:T])
         if len(keys) == 0:
             continue
@@ -293,13 +297,21 @@ def attention_grad_at(inp, dO, q_samples=(), k_samples=()):
 
     dk = np.zeros((len(k_samples), Hkv, D))
     dv = np.zeros((len(k_samples), Hkv, D))
-    for n, (r, j) in enumerate(k_samples):
+    cols, fwd = {}, {}                     # per row: visibility columns, O / LSE of the queries needed
+    for r in sorted({int(r) for r, _ in k_samples}):
         bits = visibility_bits(row_parents(inp, r))
-        col = np.unpackbits(bits, axis=1)[:, :T][:, j].astype(bool)
-        queries = np.flatnonzero(col)
+        cols[r] = {int(j): np.flatnonzero(bits[:, int(j) >> 3] & np.uint8(0x80 >> (int(j) & 7)))
+                   for rr, j in k_samples if rr == r}
+        need = np.unique(np.concatenate([np.zeros(0, np.int64)] + list(cols[r].values())))
+        O, L = attention_at(inp, [(r, int(i)) for i in need]) if len(need) else (None, None)
+        fwd[r] = (need, O, L)
+    for n, (r, j) in enumerate(k_samples):
+        queries = cols[int(r)][int(j)]
         if len(queries) == 0:
             continue
-        O, L = attention_at(inp, [(r, int(i)) for i in queries])       # [nq, Hq, D], [nq, Hq]
+        need, O_all, L_all = fwd[int(r)]
+        at = np.searchsorted(need, queries)
+        O, L = O_all[at], L_all[at]                                    # [nq, Hq, D], [nq, Hq]
         qq = _f64(inp, "q", (r, queries))                              # [nq, Hq, D]
         do = g_o(r, queries)
         kj = _f64(inp, "k", (r, j))                                    # [Hkv, D]

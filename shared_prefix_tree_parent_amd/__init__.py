@@ -11,8 +11,12 @@ carry the C names of ``include/treeattn.h``:
   tree_attn_plan_status(desc, ws)
   tree_attn_tiles(desc, ws)      -> dict of device pointers / sizes
   tree_attn_fwd(desc, ws, q, k, v, o, lse)  (async on the current stream)
+  tree_attn_bwd_workspace_size(desc) -> bytes
+  tree_attn_bwd_plan(desc, ws, bws)  (async on the current stream)
+  tree_attn_bwd_tiles(desc, bws)     -> (kt_ptr, q_list) device pointers
+  tree_attn_bwd(desc, ws, bws, q, k, v, o, lse, dout, dq, dk, dv)  (async on the current stream)
 
-plus thin conveniences ``make_desc``, ``attn_plan`` and ``attn_fwd`` that allocate torch
+plus thin conveniences ``make_desc``, ``attn_plan``, ``attn_fwd`` and ``attn_bwd`` that allocate torch
 tensors.  If the library is missing this module raises on first use: there is no fallback.
 """
 from __future__ import annotations
@@ -32,7 +36,8 @@ TREE_PLACE_BFD, TREE_PLACE_IN_ORDER = 0, 1
 
 EXPORTS = ("tree_pack_plan", "tree_plan_get", "tree_plan_free", "tree_attn_blocks",
            "tree_attn_workspace_size", "tree_attn_plan", "tree_attn_plan_status", "tree_attn_tiles",
-           "tree_attn_fwd", "tree_status_str")
+           "tree_attn_fwd", "tree_attn_bwd_workspace_size", "tree_attn_bwd_plan", "tree_attn_bwd_tiles",
+           "tree_attn_bwd", "tree_status_str")
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -97,6 +102,10 @@ def lib() -> ctypes.CDLL:
         L.tree_attn_plan_status.argtypes = [D, vp, vp]
         L.tree_attn_tiles.argtypes = [D, vp, ctypes.POINTER(TileView)]
         L.tree_attn_fwd.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
+        L.tree_attn_bwd_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+        L.tree_attn_bwd_plan.argtypes = [D, vp, vp, vp]
+        L.tree_attn_bwd_tiles.argtypes = [D, vp, ctypes.POINTER(vp), ctypes.POINTER(vp)]
+        L.tree_attn_bwd.argtypes = [D] + [vp] * 12
         L.tree_status_str.argtypes = [ctypes.c_int]
         L.tree_status_str.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -221,6 +230,31 @@ def tree_attn_fwd(desc: AttnDesc, ws, q, k, v, o, lse, stream=None) -> None:
                                _stream(stream)), "tree_attn_fwd")
 
 
+def tree_attn_bwd_workspace_size(desc: AttnDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().tree_attn_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "tree_attn_bwd_workspace_size")
+    return n.value
+
+
+def tree_attn_bwd_plan(desc: AttnDesc, ws, bws, stream=None) -> None:
+    _check(lib().tree_attn_bwd_plan(ctypes.byref(desc), _ptr(ws), _ptr(bws), _stream(stream)),
+           "tree_attn_bwd_plan")
+
+
+def tree_attn_bwd_tiles(desc: AttnDesc, bws):
+    kp, ql = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib().tree_attn_bwd_tiles(ctypes.byref(desc), _ptr(bws), ctypes.byref(kp), ctypes.byref(ql)),
+           "tree_attn_bwd_tiles")
+    return kp.value, ql.value
+
+
+def tree_attn_bwd(desc: AttnDesc, ws, bws, q, k, v, o, lse, dout, dq, dk, dv, stream=None) -> None:
+    _check(lib().tree_attn_bwd(ctypes.byref(desc), _ptr(ws), _ptr(bws), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                               _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
+           "tree_attn_bwd")
+
+
 # ------------------------------------------------------------------------------ conveniences
 
 class AttnPlan:
@@ -243,6 +277,15 @@ class AttnPlan:
     def tiles(self) -> dict:
         return tree_attn_tiles(self.desc, self.ws)
 
+    def bwd_plan(self):
+        """Allocate the backward workspace and build its k-tile lists (once per batch)."""
+        import torch
+        if getattr(self, "bws", None) is None:
+            nbytes = tree_attn_bwd_workspace_size(self.desc)
+            self.bws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.ws.device)
+            tree_attn_bwd_plan(self.desc, self.ws, self.bws)
+        return self.bws
+
 
 def attn_plan(inp, dtype=None, block_q=0, block_k=0, device="cuda") -> AttnPlan:
     """Plan for a workload object with n_rows/row_len/h_q/h_kv/head_dim/dtype/scale and seg_* arrays."""
@@ -264,3 +307,17 @@ def attn_fwd(q, k, v, plan: AttnPlan, o=None, lse=None):
             raise ValueError("tensors must be contiguous")
     tree_attn_fwd(d, plan.ws, q, k, v, o, lse)
     return o, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, plan: AttnPlan, dq=None, dk=None, dv=None):
+    """Gradients of ``attn_fwd`` for upstream ``dout``; returns (dq, dk, dv)."""
+    import torch
+    bws = plan.bwd_plan()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t in (q, k, v, o, lse, dout, dq, dk, dv):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    tree_attn_bwd(plan.desc, plan.ws, bws, q, k, v, o, lse, dout, dq, dk, dv)
+    return dq, dk, dv

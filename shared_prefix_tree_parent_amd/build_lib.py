@@ -26,7 +26,7 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
-HIP_SOURCES = ["classify.hip", "attn_fwd.hip", "capi.hip"]
+HIP_SOURCES = ["classify.hip", "attn_fwd.hip", "attn_bwd.hip", "capi.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 

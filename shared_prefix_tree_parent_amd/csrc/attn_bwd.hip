@@ -1,0 +1,572 @@
+// Tree-masked attention backward for gfx950 (CDNA4): dQ, dK, dV on bf16 MFMA.
+//
+// What is computed ("Prefix tree packing", furtherai.github.io: the packing serves training,
+// so every attention layer is differentiated; the mask is the attention-mask passage's
+// ancestor rule, in its pre-order interval form j <= i < kend[j]).  With P the softmax of the
+// visible scores (recomputed from Q, K and the forward's LSE), D_i = rowsum(dO_i * O_i):
+//   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q.
+//
+// Three launches on the caller's stream:
+//   * row_delta: D per (row, head, token), 0 at pads;
+//   * dq_kernel: one workgroup per forward item (row, q-tile, KV head, chunk of its query
+//     heads), 8 waves of 32 query rows, walking the q-tile's k-tile list with K/V tiles
+//     staged in LDS (direct-to-LDS copies, two tiles ahead);
+//   * dkdv_kernel: one workgroup per (row, k-tile, KV head), 2 waves of 32 keys whose K and V
+//     fragments stay in registers, walking the k-tile's list of q-tiles (the transposed tile
+//     lists) and every query head of the group, with Q / dO / LSE / D of 64 queries at a time
+//     staged in LDS.
+// Every result is written exactly once (no atomics); gradients of pads are zero.
+//
+// Orientation (32x32x16 bf16 MFMA, accumulator element i of lane l at row 8(i/4) + 4(l/32) +
+// i%4, column l%32):
+//   dq_kernel:  S^T = K Q^T and dP^T = V dO^T (keys x queries, a query per lane), then
+//               dQ^T += K^T dS^T with dS^T's accumulator registers as the second operand;
+//   dkdv_kernel: S = Q K^T and dP = dO V^T (queries x keys, a key per lane), then
+//               dV^T += dO^T P and dK^T += Q^T dS.
+// The "transposed" operands (K^T, dO^T, Q^T) are LDS transpose reads of row-major tiles.
+#include <type_traits>
+
+#include "internal.h"
+
+namespace treeattn {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ floatx16 zero16() {
+    floatx16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+constexpr int kBufFlags = 0x00020000;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    void *dq, *dk, *dv;
+    const float *lse;
+    float *delta;
+    const int32_t *qt_ptr, *kt_idx;
+    const uint8_t *kt_kind;
+    const int32_t *kt_ptr, *q_list, *kwork;
+    const int32_t *kend, *work, *n_real, *status;
+    int32_t T, Hq, Hkv, G, HCH, nQ, nK, L, BQ;
+    float c;       // scale * log2(e)
+    float scale;
+};
+
+// ------------------------------------------------------------------------- tiles and operands
+//
+// Tiles are row-major [rows][D] bf16 in LDS with the 16-byte chunk index of each row XOR-ed
+// with the row (mod chunks per row), exactly as the HBM rows are copied in.
+template <int D>
+struct Tile {
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;                // bytes per row
+    static constexpr int NDS = D / 16;                // k-steps over D per 32x32x16 MFMA
+    static constexpr int NDB = D / 32;                // 32-wide column blocks
+    static __device__ __forceinline__ int sw(int row) { return row & (CPR - 1); }
+    // Byte offset of the chunk that holds (row, 8-element column group c).
+    static __device__ __forceinline__ int chunk_at(int row, int c) { return row * ROWB + ((c ^ sw(row)) << 4); }
+    // Operand with row = l%32 of a 32-row block and k = 16 columns starting at 16 ds:
+    // lane l holds columns 16 ds + 8 (l/32) .. +7 of row rb + l%32.
+    static __device__ __forceinline__ bf16x8_t row_frag(const char *tile, int rb, int lane, int ds) {
+        const int row = rb + (lane & 31);
+        return *reinterpret_cast<const bf16x8_t *>(tile + chunk_at(row, 2 * ds + (lane >> 5)));
+    }
+    // Transposed operand of a 32-row block at rb: lane l holds column 32 db + l%32 of the 8
+    // rows rb + 16 ks + 4(l/32) + 0..3 and rb + 16 ks + 8 + 4(l/32) + 0..3 (the row order of
+    // an accumulator's registers 8 ks .. 8 ks + 7).  Two LDS transpose reads: in each 16-lane
+    // group, lane j points at row r0 + j/4, columns 4(j%4) .. +3 of a 16-column group and
+    // receives one column of rows r0 .. r0+3.
+    static __device__ __forceinline__ bf16x8_t tr_frag(const char *tile, int rb, int lane, int ks, int db) {
+        typedef shortx4 __attribute__((address_space(3))) *lds_p;
+        const int grp = lane >> 4, j = lane & 15, h = grp >> 1;
+        const int col = 32 * db + 16 * (grp & 1) + 4 * (j & 3);
+        bf16x4_t y[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int row = rb + 16 * ks + 8 * r + 4 * h + (j >> 2);
+            const char *p = tile + chunk_at(row, col >> 3) + (col & 7) * 2;
+            y[r] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(p)));
+        }
+        return __builtin_shufflevector(y[0], y[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+__device__ __forceinline__ floatx16 mfma(bf16x8_t a, bf16x8_t b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// bf16 operand from accumulator registers 8 ks .. 8 ks + 7.
+__device__ __forceinline__ bf16x8_t acc_frag(const floatx16 &x, int ks) {
+    bf16x8_t f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = static_cast<__bf16>(x[8 * ks + e]);
+    return f;
+}
+
+// Direct-to-LDS buffer loads; see the forward kernel for why they are inline asm.  Offsets
+// past num_records read as zeros.
+__device__ __forceinline__ int32x4_t buf_rsrc(const void *base, uint32_t num_records) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    int32x4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b)));
+    r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(num_records));
+    r[3] = kBufFlags;
+    return r;
+}
+__device__ __forceinline__ void buf_to_lds16(int32x4_t r, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %0, 0 offen lds"
+                 :: "s"(r), "s"(lds), "v"(voff) : "memory", "m0");
+}
+__device__ __forceinline__ void buf_to_lds4(int32x4_t r, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %0, 0 offen lds"
+                 :: "s"(r), "s"(lds), "v"(voff) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_base(const char *p) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)p)));
+}
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+    static_assert(N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Copy `rows` rows of D bf16 (HBM row stride `stride` bytes, rows past n_valid read as zero)
+// into a swizzled LDS tile; the nw waves of the workgroup split the 1 KB instructions.
+template <int D>
+__device__ __forceinline__ void copy_tile(const char *src, int n_valid, int stride, uint32_t dst, int rows,
+                                          int wave, int nw, int lane) {
+    using TL = Tile<D>;
+    constexpr int ROWS_PER_KB = 1024 / (D * 2);
+    const int32x4_t rs = buf_rsrc(src, uint32_t(max(n_valid, 0)) * uint32_t(stride));
+    for (int blk = wave; blk < rows / ROWS_PER_KB; blk += nw) {
+        const int row = blk * ROWS_PER_KB + lane / TL::CPR;
+        const int c = (lane % TL::CPR) ^ TL::sw(row);
+        buf_to_lds16(rs, dst + blk * 1024, row * stride + c * 16);
+    }
+}
+
+// ------------------------------------------------------------------------------ row_delta
+//
+// D[r, h, i] = sum_d dO[r, i, h, d] * O[r, i, h, d] in fp32 for real tokens, 0 at pads (their
+// dO / O contents are never read).  One thread per (row, token, head).
+template <int D, class E>
+__global__ void row_delta(int32_t R, int32_t T, int32_t Hq, const E *__restrict__ o, const E *__restrict__ dout,
+                          const int32_t *__restrict__ n_real, float *__restrict__ delta) {
+    const int64_t id = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (id >= int64_t(R) * T * Hq) return;
+    const int h = int(id % Hq);
+    const int64_t ri = id / Hq;
+    const int r = int(ri / T), i = int(ri % T);
+    float acc = 0.f;
+    if (i < n_real[r]) {
+        const E *po = o + id * D;
+        const E *pd = dout + id * D;
+#pragma unroll 8
+        for (int d = 0; d < D; ++d) acc = fmaf(float(po[d]), float(pd[d]), acc);
+    }
+    delta[(int64_t(r) * Hq + h) * T + i] = acc;
+}
+
+// ------------------------------------------------------------------------------ dq_kernel
+constexpr int kDqWaves = 8;
+constexpr int kBK = 64;                   // keys per k-tile
+
+template <int D>
+struct DqLds {
+    static constexpr int TILE = kBK * D * 2;
+    static constexpr int NB = 3;                       // k-tile buffers (tile t+2 copied under t)
+    static constexpr int K_OFF = 0, V_OFF = NB * TILE, KE_OFF = 2 * NB * TILE;
+    static constexpr int LIST_OFF = KE_OFF + NB * 256;
+    static constexpr int PERW = 2 * (TILE / 1024) / kDqWaves;   // K and V copies per wave per tile
+    static_assert((2 * (TILE / 1024)) % kDqWaves == 0, "waves must split a tile evenly");
+};
+
+template <int D>
+__global__ __launch_bounds__(kDqWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dq_kernel(BwdArgs a) {
+    using TL = Tile<D>;
+    using LD = DqLds<D>;
+    constexpr int NB = LD::NB;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    if (a.status[0] != 0) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int u = blockIdx.x % a.L, item = blockIdx.x / a.L;
+    const int g = u % a.Hkv, chunk = u / a.Hkv;
+    const int tile = a.work[item];
+    const int r = tile / a.nQ, qt = tile % a.nQ;
+    const int T = a.T;
+    const int n_real = a.n_real[r];
+    const int hl = wave % a.HCH, pb = wave / a.HCH;
+    const int head = g * a.G + chunk * a.HCH + hl;
+    const int qpos = qt * a.BQ + pb * 32 + l32;
+    const bool qreal = qpos < n_real;
+
+    // Q and dO fragments of the wave's 32 queries (dO zero at pad queries: its contents never
+    // reach dK / dV / dQ); per-lane log2-domain LSE (+inf at pads so that P = 0) and D.
+    bf16x8_t qf[TL::NDS], dof[TL::NDS];
+    {
+        const int64_t row_off = ((int64_t(r) * T + qpos) * a.Hq + head) * D;
+        const bf16x8_t *pq = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.q) + row_off);
+        const bf16x8_t *pd = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.dout) + row_off);
+#pragma unroll
+        for (int ds = 0; ds < TL::NDS; ++ds) {
+            qf[ds] = pq[2 * ds + h];
+            const bf16x8_t x = pd[2 * ds + h];
+            bf16x8_t z;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] = qreal ? x[e] : static_cast<__bf16>(0.f);
+            dof[ds] = z;
+        }
+    }
+    const float lse_raw = a.lse[(int64_t(r) * a.Hq + head) * T + qpos];
+    const float lse2 = (qreal && lse_raw > -INFINITY) ? lse_raw * kLog2e : INFINITY;
+    const float dlt = a.delta[(int64_t(r) * a.Hq + head) * T + qpos];
+
+    floatx16 acc[TL::NDB];
+#pragma unroll
+    for (int db = 0; db < TL::NDB; ++db) acc[db] = zero16();
+
+    const int32_t t_begin = a.qt_ptr[tile];
+    const int N = a.qt_ptr[tile + 1] - t_begin;
+    int32_t *const lst = reinterpret_cast<int32_t *>(smem + LD::LIST_OFF);
+    for (int i = tid; i < N; i += kDqWaves * 64) lst[i] = a.kt_idx[t_begin + i] * 4 + a.kt_kind[t_begin + i];
+    __syncthreads();
+
+    const int row_stride = a.Hkv * D * 2;
+    const char *kbase0 = reinterpret_cast<const char *>(a.k) + ((int64_t(r) * T) * a.Hkv + g) * D * 2;
+    const char *vbase0 = reinterpret_cast<const char *>(a.v) + ((int64_t(r) * T) * a.Hkv + g) * D * 2;
+    const int32_t *kend_row = a.kend + int64_t(r) * T;
+    const uint32_t lds0 = lds_base(smem);
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const int kt = __builtin_amdgcn_readfirstlane(lst[t]) >> 2;
+        const int slot = t % NB;
+        const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - kt * kBK, 0), kBK));
+        const int64_t tb = int64_t(kt) * kBK * row_stride;
+        copy_tile<D>(kbase0 + tb, n_valid, row_stride, lds0 + LD::K_OFF + slot * LD::TILE, kBK, wave, kDqWaves, lane);
+        copy_tile<D>(vbase0 + tb, n_valid, row_stride, lds0 + LD::V_OFF + slot * LD::TILE, kBK, wave, kDqWaves, lane);
+        if (wave == kDqWaves - 1) buf_to_lds4(buf_rsrc(kend_row + kt * kBK, 256), lds0 + LD::KE_OFF + slot * 256, lane * 4);
+    };
+
+    if (N > 0) issue(0);
+    if (N > 1) issue(1);
+    for (int t = 0; t < N; ++t) {
+        // Tile t has landed for every wave once each waited for its own copies of t (only
+        // t+1's may still be in flight), and every wave is past tile t-1 before its buffer
+        // slot takes tile t+2.
+        if (t + 1 < N) {
+            // leave tile t+1's copies (the newest) in flight
+            if (wave == kDqWaves - 1) wait_loads_but<DqLds<D>::PERW + 1>();
+            else wait_loads_but<DqLds<D>::PERW>();
+        } else {
+            wait_loads();
+        }
+        block_barrier();
+        if (t + 2 < N) issue(t + 2);
+        const int ent = __builtin_amdgcn_readfirstlane(lst[t]);
+        const int kt = ent >> 2;
+        const bool partial = (ent & 3) == kTilePartial;
+        const int slot = t % NB;
+        const char *Kt = smem + LD::K_OFF + slot * LD::TILE;
+        const char *Vt = smem + LD::V_OFF + slot * LD::TILE;
+        const int32_t *KEs = reinterpret_cast<const int32_t *>(smem + LD::KE_OFF + slot * 256) + 4 * h;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            floatx16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int ds = 0; ds < TL::NDS; ++ds) {
+                s = mfma(TL::row_frag(Kt, 32 * kb, lane, ds), qf[ds], s);
+                dp = mfma(TL::row_frag(Vt, 32 * kb, lane, ds), dof[ds], dp);
+            }
+            // P^T and dS^T; element i is key 32 kb + 8(i/4) + 4h + i%4 of the tile.
+            const int dq_ = qpos - kt * kBK - 4 * h;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                int4 ke = make_int4(INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX);
+                if (partial) ke = *reinterpret_cast<const int4 *>(KEs + 32 * kb + 8 * i4);
+                const int kev[4] = {ke.x, ke.y, ke.z, ke.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * i4 + e, c = 32 * kb + 8 * i4 + e;
+                    const bool vis = !partial || ((c <= dq_) & (qpos < kev[e]));
+                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.c, -lse2)) : 0.f;
+                    s[i] = p * (dp[i] - dlt);
+                }
+            }
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8_t dsf = acc_frag(s, ks);
+#pragma unroll
+                for (int db = 0; db < TL::NDB; ++db)
+                    acc[db] = mfma(TL::tr_frag(Kt, 32 * kb, lane, ks, db), dsf, acc[db]);
+            }
+        }
+    }
+
+    // dQ = scale * (dQ^T)^T; lane holds query qpos, 4 consecutive d per register group.
+    __bf16 *op = reinterpret_cast<__bf16 *>(a.dq) + ((int64_t(r) * T + qpos) * a.Hq + head) * D;
+#pragma unroll
+    for (int db = 0; db < TL::NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int d0 = 32 * db + 8 * i4 + 4 * h;
+            uint2 w;
+            w.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[db][4 * i4 + 0] * a.scale))) |
+                  (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[db][4 * i4 + 1] * a.scale))) << 16);
+            w.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[db][4 * i4 + 2] * a.scale))) |
+                  (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[db][4 * i4 + 3] * a.scale))) << 16);
+            *reinterpret_cast<uint2 *>(op + d0) = w;
+        }
+}
+
+// ---------------------------------------------------------------------------- dkdv_kernel
+constexpr int kKvWaves = 2;               // 32 keys each: one 64-key tile per workgroup
+constexpr int kQB = 64;                   // queries staged per unit
+
+template <int D>
+struct KvLds {
+    static constexpr int TILE = kQB * D * 2;
+    static constexpr int STAGE = 2 * TILE + 2 * kQB * 4;   // Q, dO, LSE, D
+    static constexpr int Q_OFF = 0, DO_OFF = TILE, LSE_OFF = 2 * TILE, DL_OFF = 2 * TILE + kQB * 4;
+    static constexpr int NSTAGE = 2;
+};
+
+template <int D>
+__global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
+    using TL = Tile<D>;
+    using LD = KvLds<D>;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    if (a.status[0] != 0) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int g = blockIdx.x % a.Hkv, item = blockIdx.x / a.Hkv;
+    const int ktile = a.kwork[item];
+    const int r = ktile / a.nK, kt = ktile % a.nK;
+    const int T = a.T;
+    const int n_real = a.n_real[r];
+    const int key = kt * kBK + 32 * wave + l32;         // this lane's key (column of S / dP)
+    const bool kreal = key < n_real;
+    const int kend_k = a.kend[int64_t(r) * T + key];
+
+    // K and V fragments of the wave's 32 keys (B operands of S = Q K^T and dP = dO V^T):
+    // lane holds columns 16 ds + 8h .. +7 of its key; zero at pad keys.
+    bf16x8_t kf[TL::NDS], vf[TL::NDS];
+    {
+        const int64_t off = ((int64_t(r) * T + key) * a.Hkv + g) * D;
+        const bf16x8_t *pk = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.k) + off);
+        const bf16x8_t *pv = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.v) + off);
+#pragma unroll
+        for (int ds = 0; ds < TL::NDS; ++ds) {
+            const bf16x8_t x = pk[2 * ds + h], y = pv[2 * ds + h];
+            bf16x8_t zx, zy;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                zx[e] = kreal ? x[e] : static_cast<__bf16>(0.f);
+                zy[e] = kreal ? y[e] : static_cast<__bf16>(0.f);
+            }
+            kf[ds] = zx;
+            vf[ds] = zy;
+        }
+    }
+    floatx16 dk[TL::NDB], dv[TL::NDB];       // dK^T, dV^T: rows d, a key per lane
+#pragma unroll
+    for (int db = 0; db < TL::NDB; ++db) {
+        dk[db] = zero16();
+        dv[db] = zero16();
+    }
+
+    // Units: (q-tile of the k-tile's list, query head of the group, 64-query chunk).
+    const int32_t l_begin = a.kt_ptr[ktile];
+    const int NL = a.kt_ptr[ktile + 1] - l_begin;
+    const int QB = min(a.BQ, kQB), n_chunks = a.BQ / QB;
+    const int per_tile = a.G * n_chunks;
+    const int NU = NL * per_tile;
+    const int q_stride = a.Hq * D * 2;
+    const uint32_t lds0 = lds_base(smem);
+    auto unit = [&](int n, int &q0, int &head, bool &partial) __attribute__((always_inline)) {
+        const int ent = __builtin_amdgcn_readfirstlane(a.q_list[l_begin + n / per_tile]);
+        const int rem = n % per_tile;
+        head = g * a.G + rem / n_chunks;
+        q0 = (ent >> 2) * a.BQ + (rem % n_chunks) * QB;
+        partial = (ent & 3) == kTilePartial;
+    };
+    auto issue = [&](int n) __attribute__((always_inline)) {
+        int q0, head;
+        bool partial;
+        unit(n, q0, head, partial);
+        const uint32_t st = lds0 + (n % LD::NSTAGE) * LD::STAGE;
+        const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - q0, 0), QB));
+        const int64_t roff = ((int64_t(r) * T + q0) * a.Hq + head) * D * 2;
+        copy_tile<D>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, st + LD::Q_OFF, QB, wave, kKvWaves, lane);
+        copy_tile<D>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride, st + LD::DO_OFF, QB, wave, kKvWaves, lane);
+        const int64_t loff = (int64_t(r) * a.Hq + head) * T + q0;
+        if (wave == 0 && lane < QB) {
+            buf_to_lds4(buf_rsrc(a.lse + loff, uint32_t(QB) * 4), st + LD::LSE_OFF, lane * 4);
+            buf_to_lds4(buf_rsrc(a.delta + loff, uint32_t(QB) * 4), st + LD::DL_OFF, lane * 4);
+        }
+    };
+
+    if (NU > 0) issue(0);
+    for (int n = 0; n < NU; ++n) {
+        wait_loads();
+        block_barrier();
+        if (n + 1 < NU) issue(n + 1);
+        int q0, head;
+        bool partial;
+        unit(n, q0, head, partial);
+        const char *st = smem + (n % LD::NSTAGE) * LD::STAGE;
+        const char *Qt = st + LD::Q_OFF;
+        const char *Ot = st + LD::DO_OFF;
+        const float *LS = reinterpret_cast<const float *>(st + LD::LSE_OFF);
+        const float *DL = reinterpret_cast<const float *>(st + LD::DL_OFF);
+        for (int qb = 0; qb < QB / 32; ++qb) {
+            floatx16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int ds = 0; ds < TL::NDS; ++ds) {
+                s = mfma(TL::row_frag(Qt, 32 * qb, lane, ds), kf[ds], s);
+                dp = mfma(TL::row_frag(Ot, 32 * qb, lane, ds), vf[ds], dp);
+            }
+            // Element i is query q0 + 32 qb + 8(i/4) + 4h + i%4; LSE and D four at a time.
+            floatx16 pm;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int qi = 32 * qb + 8 * i4 + 4 * h;
+                const float4 l4 = *reinterpret_cast<const float4 *>(LS + qi);
+                const float4 d4 = *reinterpret_cast<const float4 *>(DL + qi);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * i4 + e, q = q0 + qi + e;
+                    const bool vis = kreal & (!partial || ((key <= q) & (q < kend_k))) & (lv[e] > -INFINITY);
+                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.c, -lv[e] * kLog2e)) : 0.f;
+                    pm[i] = p;
+                    s[i] = p * (dp[i] - dv4[e]);
+                }
+            }
+            // dV^T += dO^T P ;  dK^T += Q^T dS
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8_t pf = acc_frag(pm, ks), sf = acc_frag(s, ks);
+#pragma unroll
+                for (int db = 0; db < TL::NDB; ++db) {
+                    dv[db] = mfma(TL::tr_frag(Ot, 32 * qb, lane, ks, db), pf, dv[db]);
+                    dk[db] = mfma(TL::tr_frag(Qt, 32 * qb, lane, ks, db), sf, dk[db]);
+                }
+            }
+        }
+    }
+
+    // dK = scale dS^T Q, dV = P^T dO: lane holds its key, 4 consecutive d per register group.
+    const int64_t off = ((int64_t(r) * T + key) * a.Hkv + g) * D;
+    __bf16 *pk = reinterpret_cast<__bf16 *>(a.dk) + off;
+    __bf16 *pv = reinterpret_cast<__bf16 *>(a.dv) + off;
+#pragma unroll
+    for (int db = 0; db < TL::NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int d0 = 32 * db + 8 * i4 + 4 * h;
+            uint2 wk, wv;
+            wk.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(dk[db][4 * i4 + 0] * a.scale))) |
+                   (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(dk[db][4 * i4 + 1] * a.scale))) << 16);
+            wk.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(dk[db][4 * i4 + 2] * a.scale))) |
+                   (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(dk[db][4 * i4 + 3] * a.scale))) << 16);
+            wv.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(dv[db][4 * i4 + 0]))) |
+                   (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(dv[db][4 * i4 + 1]))) << 16);
+            wv.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(dv[db][4 * i4 + 2]))) |
+                   (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(dv[db][4 * i4 + 3]))) << 16);
+            *reinterpret_cast<uint2 *>(pk + d0) = wk;
+            *reinterpret_cast<uint2 *>(pv + d0) = wv;
+        }
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, hipStream_t s) {
+    const int64_t n_rows = int64_t(R) * a.T * a.Hq;
+    if (n_rows > 0) {
+        row_delta<D, __bf16><<<int((n_rows + 255) / 256), 256, 0, s>>>(
+            R, a.T, a.Hq, reinterpret_cast<const __bf16 *>(a.o), reinterpret_cast<const __bf16 *>(a.dout),
+            a.n_real, a.delta);
+    }
+    if (n_items_q > 0) {
+        const int smem = DqLds<D>::LIST_OFF + 4 * ((a.nK + 3) & ~3);
+        if (smem > 160 * 1024) return hipErrorInvalidValue;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(dq_kernel<D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+        if (e != hipSuccess) return e;
+        dq_kernel<D><<<n_items_q, kDqWaves * 64, smem, s>>>(a);
+    }
+    if (n_items_k > 0) {
+        const int smem = KvLds<D>::NSTAGE * KvLds<D>::STAGE;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(dkdv_kernel<D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+        if (e != hipSuccess) return e;
+        dkdv_kernel<D><<<n_items_k, kKvWaves * 64, smem, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b, const char *ws, char *bws,
+                      const void *q, const void *k, const void *v, const void *o, const float *lse,
+                      const void *dout, void *dq, void *dk, void *dv, hipStream_t s) {
+    BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.lse = lse;
+    a.delta = reinterpret_cast<float *>(bws + b.delta);
+    a.qt_ptr = reinterpret_cast<const int32_t *>(ws + w.qt_ptr);
+    a.kt_idx = reinterpret_cast<const int32_t *>(ws + w.kt_idx);
+    a.kt_kind = reinterpret_cast<const uint8_t *>(ws + w.kt_kind);
+    a.kt_ptr = reinterpret_cast<const int32_t *>(bws + b.kt_ptr);
+    a.q_list = reinterpret_cast<const int32_t *>(bws + b.q_list);
+    a.kwork = reinterpret_cast<const int32_t *>(bws + b.kwork);
+    a.kend = reinterpret_cast<const int32_t *>(ws + w.kend);
+    a.work = reinterpret_cast<const int32_t *>(ws + w.work);
+    a.n_real = reinterpret_cast<const int32_t *>(ws + w.n_real);
+    a.status = reinterpret_cast<const int32_t *>(ws + w.status);
+    a.T = sh.T; a.Hq = sh.Hq; a.Hkv = sh.Hkv; a.G = sh.G; a.HCH = sh.HCH;
+    a.nQ = w.nQ; a.nK = w.nK; a.BQ = sh.BQ;
+    a.L = sh.Hkv * (sh.G / sh.HCH);
+    a.scale = sh.scale;
+    a.c = sh.scale * kLog2e;
+    const int64_t n_q = int64_t(sh.R) * w.nQ * a.L;
+    const int64_t n_k = int64_t(sh.R) * w.nK * sh.Hkv;
+    if (n_q > INT32_MAX || n_k > INT32_MAX) return hipErrorInvalidValue;
+    if (sh.dtype != TREE_DT_BF16) return hipErrorInvalidValue;
+    if (sh.D == 128) return launch_d<128>(a, sh.R, int(n_q), int(n_k), s);
+    if (sh.D == 64) return launch_d<64>(a, sh.R, int(n_q), int(n_k), s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace treeattn

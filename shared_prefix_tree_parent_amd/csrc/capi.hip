@@ -127,6 +127,78 @@ extern "C" int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void
     return e == hipSuccess ? TREE_OK : TREE_E_HIP;
 }
 
+// ----------------------------------------------------------------------------- backward
+
+namespace {
+// The backward runs on the forward's plan (same tile sizes) and needs bf16.
+int bwd_check(const tree_attn_desc *d, WsLayout *w, BwdLayout *b) {
+    if (!layout_of(d, w)) return TREE_E_INVAL;
+    int32_t bq, bk;
+    fwd_blocks(d, &bq, &bk);
+    if (w->BQ != bq || w->BK != bk) return TREE_E_UNSUPPORTED;
+    if (d->dtype != TREE_DT_BF16) return TREE_E_UNSUPPORTED;
+    if (w->nK > kFwdMaxKTiles) return TREE_E_UNSUPPORTED;
+    *b = make_bwd_layout(*w, d->h_q);
+    return TREE_OK;
+}
+}  // namespace
+
+extern "C" int tree_attn_bwd_workspace_size(const tree_attn_desc *d, size_t *bytes) {
+    WsLayout w;
+    BwdLayout b;
+    if (bytes == nullptr) return TREE_E_INVAL;
+    const int rc = bwd_check(d, &w, &b);
+    if (rc != TREE_OK) return rc;
+    *bytes = b.total;
+    return TREE_OK;
+}
+
+extern "C" int tree_attn_bwd_plan(const tree_attn_desc *d, const void *ws, void *bws, void *stream) {
+    WsLayout w;
+    BwdLayout b;
+    const int rc = bwd_check(d, &w, &b);
+    if (rc != TREE_OK) return rc;
+    if (ws == nullptr || bws == nullptr || (reinterpret_cast<uintptr_t>(bws) & 255) != 0) return TREE_E_INVAL;
+    const hipError_t e = launch_bwd_plan(w, b, static_cast<const char *>(ws), static_cast<char *>(bws),
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TREE_OK : TREE_E_HIP;
+}
+
+extern "C" int tree_attn_bwd_tiles(const tree_attn_desc *d, const void *bws, const int32_t **kt_ptr,
+                                   const int32_t **q_list) {
+    WsLayout w;
+    BwdLayout b;
+    const int rc = bwd_check(d, &w, &b);
+    if (rc != TREE_OK) return rc;
+    if (bws == nullptr || kt_ptr == nullptr || q_list == nullptr) return TREE_E_INVAL;
+    *kt_ptr = reinterpret_cast<const int32_t *>(static_cast<const char *>(bws) + b.kt_ptr);
+    *q_list = reinterpret_cast<const int32_t *>(static_cast<const char *>(bws) + b.q_list);
+    return TREE_OK;
+}
+
+extern "C" int tree_attn_bwd(const tree_attn_desc *d, const void *ws, void *bws, const void *q, const void *k,
+                             const void *v, const void *o, const float *lse, const void *dout, void *dq,
+                             void *dk, void *dv, void *stream) {
+    WsLayout w;
+    BwdLayout b;
+    const int rc = bwd_check(d, &w, &b);
+    if (rc != TREE_OK) return rc;
+    if (ws == nullptr || bws == nullptr) return TREE_E_INVAL;
+    if (d->n_rows > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
+                          dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr))
+        return TREE_E_INVAL;
+    FwdShape sh;
+    sh.R = d->n_rows; sh.T = d->row_len; sh.Hq = d->h_q; sh.Hkv = d->h_kv; sh.D = d->head_dim;
+    sh.dtype = d->dtype;
+    sh.G = d->h_q / d->h_kv;
+    sh.HCH = heads_per_wg(sh.G);
+    sh.BQ = w.BQ;
+    sh.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->head_dim));
+    const hipError_t e = launch_bwd(sh, w, b, static_cast<const char *>(ws), static_cast<char *>(bws), q, k, v,
+                                    o, lse, dout, dq, dk, dv, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TREE_OK : TREE_E_HIP;
+}
+
 extern "C" const char *tree_status_str(int code) {
     switch (code) {
         case TREE_OK: return "ok";
@@ -135,7 +207,7 @@ extern "C" const char *tree_status_str(int code) {
         case TREE_E_LAYOUT: return "segment table is not a valid pre-order forest layout";
         case TREE_E_NOMEM: return "out of host memory";
         case TREE_E_HIP: return "HIP runtime or launch error";
-        case TREE_E_UNSUPPORTED: return "no kernel for these arguments (plan tile sizes differ from the forward kernel's, or the row is too long)";
+        case TREE_E_UNSUPPORTED: return "no kernel for these arguments (plan tile sizes differ from the forward kernel's, the row is too long, or no backward for this dtype)";
         default: return "unknown status";
     }
 }

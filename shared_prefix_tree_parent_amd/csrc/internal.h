@@ -58,8 +58,33 @@ inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_
     return w;
 }
 
-// Launchers (defined in classify.hip / attn_fwd.hip).  Return hipSuccess or the first error.
+// Backward workspace layout (caller-allocated, filled by tree_attn_bwd_plan / tree_attn_bwd).
+struct BwdLayout {
+    size_t delta = 0;     // float[R*Hq*T]: rowsum(dO * O) per (row, head, token); 0 at pads
+    size_t kt_ptr = 0;    // int32[R*nK + 1]: CSR over (row, k-tile) of the q-tiles that see it
+    size_t q_list = 0;    // int32[R*nQ*nK]: q-tile * 4 + class, ascending q-tile per k-tile
+    size_t kwork = 0;     // int32[R*nK]: (row, k-tile) items, longest list first
+    size_t khist = 0;     // int32[nQ + 2]
+    size_t total = 0;
+};
+
+inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq) {
+    BwdLayout b;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    b.delta = take(size_t(w.R) * Hq * w.T * sizeof(float));
+    b.kt_ptr = take((size_t(w.R) * w.nK + 1) * sizeof(int32_t));
+    b.q_list = take(size_t(w.R) * w.nQ * w.nK * sizeof(int32_t));
+    b.kwork = take(size_t(w.R) * w.nK * sizeof(int32_t));
+    b.khist = take((size_t(w.nQ) + 2) * sizeof(int32_t));
+    b.total = off;
+    return b;
+}
+
+// Launchers (defined in classify.hip / attn_fwd.hip / attn_bwd.hip).  Return hipSuccess or the
+// first error.
 hipError_t launch_plan(const tree_attn_desc &d, const WsLayout &w, char *ws, hipStream_t s);
+hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, const char *ws, char *bws, hipStream_t s);
 
 struct FwdShape {
     int32_t R, T, Hq, Hkv, D, dtype;
@@ -70,5 +95,8 @@ struct FwdShape {
 };
 hipError_t launch_fwd(const FwdShape &sh, const WsLayout &w, const char *ws, const void *q,
                       const void *k, const void *v, void *o, float *lse, hipStream_t s);
+hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b, const char *ws, char *bws,
+                      const void *q, const void *k, const void *v, const void *o, const float *lse,
+                      const void *dout, void *dq, void *dk, void *dv, hipStream_t s);
 
 }  // namespace treeattn

@@ -96,3 +96,73 @@ def check_close(o_gpu, l_gpu, o_ref, l_ref, dtype, real_mask, what=""):
         assert np.all(o_gpu[pad] == 0), f"{what}: pad O not zero"
         assert np.all(l_gpu[pad] == -np.inf), f"{what}: pad LSE not -inf"
     return max_abs, mean_abs, lmax
+
+
+def bf16_dev(bits):
+    """bf16 bit patterns (uint16 numpy) -> device bfloat16 tensor."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def run_bwd(inp: RowInputs, dO, plan=None, repeats: int = 1):
+    """Forward then backward through the C-ABI; returns (dq, dk, dv) float32 numpy, plan."""
+    import torch
+    if plan is None:
+        plan = ta.attn_plan(inp)
+    q, k, v = to_dev(inp, "q"), to_dev(inp, "k"), to_dev(inp, "v")
+    do = bf16_dev(dO)
+    o, lse = ta.attn_fwd(q, k, v, plan)
+    g = None
+    for _ in range(repeats):
+        g = ta.attn_bwd(q, k, v, o, lse, do, plan)
+    torch.cuda.synchronize()
+    return tuple(x.float().cpu().numpy() for x in g), plan
+
+
+# Gradient tolerance.  Every product of the backward takes bf16 operands (Q, K, V, dO, and P
+# and dS rounded to bf16) with fp32 accumulation, and each gradient is rounded to bf16 once:
+# per element that is a relative error of about 2^-9 of the size of that token's gradient
+# vector (cancellation inside one sum can make a single element much smaller than its terms,
+# so the scale is the vector's RMS over head_dim, not the element).  Bound:
+#   |err| <= 2^-5 * rms_d(ref[token, head]) + 2^-7 * rms(ref) + extra,
+# 16x the expected error with a floor for vectors that are themselves near zero, and
+# mean |err| <= 2^-7 mean |ref| + mean(extra).
+# `extra` covers the row term D_i = sum_d dO_id O_id, which the backward takes from the
+# forward's bf16 O: |bf16(x) - x| <= 2^-9 |x| gives |dD_i| <= c_i = 2^-9 sum_d |dO_id O_id|,
+# which moves dQ_i by scale * dD_i * sum_j P_ij k_j and dK_j by scale * sum_i P_ij dD_i q_i.
+# Where attention is concentrated on a few keys the true gradients nearly cancel and this term
+# dominates.  It is bounded with a factor 2 from oracle quantities: the attention-averaged keys
+# (the forward with V replaced by K) for dQ, and for dK the oracle's dV for the upstream
+# gradient c_i |q_i| (dV_j = sum_i P_ij dO_i).
+GRAD_VEC_TOL, GRAD_FLOOR_TOL, GRAD_MEAN_TOL = 2.0 ** -5, 2.0 ** -7, 2.0 ** -7
+
+
+def row_term_bound(dO, O):
+    """c_i = 2^-9 sum_d |dO_id O_id| per (position, head), shape [..., H, 1]."""
+    return 2.0 ** -9 * np.abs(np.asarray(dO, np.float64) * O).sum(axis=-1, keepdims=True)
+
+
+def check_grad(got, ref, real_mask, what, extra=None):
+    """got / ref [N, H, D] at N positions; real_mask [N].  Pads must be exactly zero."""
+    real_mask = np.asarray(real_mask, bool)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    g, r = got[real_mask], ref[real_mask]
+    worst = mean_rel = 0.0
+    if r.size:
+        err = np.abs(g - r)
+        vec = np.sqrt((r ** 2).mean(axis=-1, keepdims=True))
+        glob = float(np.sqrt((r ** 2).mean()))
+        bound = GRAD_VEC_TOL * vec + GRAD_FLOOR_TOL * glob + 1e-30
+        if extra is not None:
+            bound = bound + extra[real_mask]
+        worst = float((err / bound).max())
+        mean_bound = GRAD_MEAN_TOL * np.abs(r).mean() + (0.0 if extra is None else extra[real_mask].mean())
+        mean_rel = float(err.mean() / max(mean_bound, 1e-30))
+        log(f"  {what}: max-abs {err.max():.3e} (rms {glob:.3e}), worst/bound {worst:.3f}, "
+            f"mean-abs/bound {mean_rel:.3f}")
+        assert worst <= 1.0, f"{what}: error above bound ({worst})"
+        assert mean_rel <= 1.0, f"{what}: mean error above bound ({mean_rel})"
+    pad = ~real_mask
+    if pad.any():
+        assert np.all(got[pad] == 0), f"{what}: pad gradient not zero"
+    return worst, mean_rel

@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     f32_from_bf16_bits,
     make_config,
     config4_sequences,
+    draw_grad,
     draw_qkv,
     fill_pads,
     random_forest_row,

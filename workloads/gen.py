@@ -122,6 +122,14 @@ def draw_qkv(rng: np.random.Generator, R: int, T: int, h_q: int, h_kv: int, D: i
     return out
 
 
+def draw_grad(inp: RowInputs, seed: int = 0) -> np.ndarray:
+    """Upstream gradient dO ~ N(0, 1) in Q's layout and dtype, from its own generator
+    (``default_rng(seed)``) so that the Q/K/V draws are unchanged."""
+    x = np.random.default_rng(seed).standard_normal(
+        (inp.n_rows, inp.row_len, inp.h_q, inp.head_dim), dtype=np.float32)
+    return bf16_bits_from_f32(x) if inp.dtype == "bf16" else x
+
+
 def fill_pads(inp: RowInputs, value: float) -> None:
     """Overwrite Q/K/V at pad positions (token index >= real_len of the row)."""
     for name in ("q", "k", "v"):
