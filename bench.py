@@ -10,6 +10,10 @@ Prints ONE JSON line: value = useful TFLOP/s of a step, where useful FLOPs =
 4 * head_dim * h_q * (visible query/key pairs over real tokens); plus % of the bf16 MFMA
 peak, trajectories/s, the forward kernel's roofline point (timed live with HIP events on the
 stream it runs on) and the CPU oracle timed on a bounded sample of the same workload.
+Beside it, the backward (tree_attn_bwd: dQ, dK, dV for a seeded upstream gradient, bf16
+workloads) is timed on the same inputs and reported as `bwd`, with its FLOPs counted the
+FlashAttention way: 2.5 x the forward's useful FLOPs (S recomputed once, dP, dV, dK and dQ,
+each 2 * head_dim per visible pair and query head).
 """
 from __future__ import annotations
 
@@ -170,6 +174,7 @@ def main() -> int:
     ap.add_argument("--uniform-lengths", action="store_true", help="config 3 with literal U[100,1000]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -181,7 +186,7 @@ def main() -> int:
 
     import torch
     import shared_prefix_tree_parent_amd as ta
-    from workloads import CONFIG_NAMES, make_config
+    from workloads import CONFIG_NAMES, draw_grad, make_config
 
     if args.copy_mb:
         # Known-size reference for the HBM byte counters: each launch reads and writes copy_mb MiB.
@@ -246,6 +251,33 @@ def main() -> int:
     fwd_ms = timed(fwd, args.steps)
     cls_ms = timed(classify, args.steps)
 
+    bwd = None
+    if inp.dtype == "bf16" and not args.no_bwd:
+        do = torch.from_numpy(draw_grad(inp, args.config).view(np.int16)).view(torch.bfloat16).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = plan.bwd_plan()
+        fwd()
+
+        def bwd_step():
+            ta.tree_attn_bwd(plan.desc, plan.ws, bws, q, k, v, o, lse, do, dq, dk, dv)
+
+        def bwd_plan():
+            ta.tree_attn_bwd_plan(plan.desc, plan.ws, bws)
+
+        for _ in range(args.warmup):
+            bwd_step()
+        bwd_ms = timed(bwd_step, args.steps)
+        bwd_plan_ms = timed(bwd_plan, args.steps)
+        bwd_flops = 2.5 * useful
+        bwd_tflops = bwd_flops / (bwd_ms * 1e-3) / 1e12
+        bwd = {"ms": round(bwd_ms, 4), "tflops": round(bwd_tflops, 2),
+               "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS,
+               "flops_per_call": bwd_flops, "flops": "2.5 x forward useful (S, dP, dV, dK, dQ)",
+               "mfma_flops_per_call": 3.5 * useful,
+               "plan_us": round(bwd_plan_ms * 1e3, 2),
+               "fwd_plus_bwd_ms": round(fwd_ms + bwd_ms, 4),
+               "calls": "tree_attn_bwd (row terms + dQ kernel + dK/dV kernel); plan once per batch"}
+
     peak = PEAK_BF16_TFLOPS if inp.dtype == "bf16" else PEAK_F32_TFLOPS
     value = useful / (ms_step * 1e-3) / 1e12
     fwd_tflops = useful / (fwd_ms * 1e-3) / 1e12
@@ -274,6 +306,7 @@ def main() -> int:
         "host_plan_ms": None,
         "roofline": roofline,
         "clock_adjusted": None,
+        "bwd": bwd,
         "cpu_baseline": None,
     }
     clk = recorded_clock_ghz(args.config, args.uniform_lengths)
