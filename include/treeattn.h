@@ -205,15 +205,16 @@ int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const 
  * `ws` must use the forward's tile sizes (tree_attn_blocks).
  *
  * tree_attn_bwd_workspace_size: bytes of the caller-allocated backward workspace `bws`
- *   (256-byte aligned): per-token row terms D [R, Hq, T] fp32 plus the per-k-tile lists.
+ *   (256-byte aligned): per-token row terms D and log2-scaled LSE ([R, Hq, T] fp32 each)
+ *   plus the per-k-tile lists.
  * tree_attn_bwd_plan: from the forward plan in `ws`, build into `bws` the lists of q-tiles that
  *   see each k-tile (the transposed tile lists: ascending q-tile, entry = q_tile * 4 + class)
  *   and the order of the k-tile work.  Once per batch, like tree_attn_plan; asynchronous.
  * tree_attn_bwd_tiles: device pointers (into bws) of those lists, for tests:
  *   kt_ptr[R * n_ktiles + 1] CSR over (row, k-tile), q_list the entries.
  * tree_attn_bwd: q, k, v as given to tree_attn_fwd; o and lse as it returned them; dout in
- *   q's layout; writes dq (q's layout), dk and dv (k's layout), bf16.  Uses D in bws (it
- *   overwrites it).  Asynchronous.  Errors: TREE_E_INVAL, TREE_E_UNSUPPORTED, TREE_E_HIP.
+ *   q's layout; writes dq (q's layout), dk and dv (k's layout), bf16.  Overwrites the row
+ *   terms in bws (the lists are kept).  Asynchronous.  Errors: TREE_E_INVAL, TREE_E_UNSUPPORTED, TREE_E_HIP.
  */
 int tree_attn_bwd_workspace_size(const tree_attn_desc *d, size_t *bytes);
 int tree_attn_bwd_plan(const tree_attn_desc *d, const void *ws, void *bws, void *stream);

@@ -7,14 +7,14 @@
 //   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q.
 //
 // Three launches on the caller's stream:
-//   * row_delta: D per (row, head, token), 0 at pads;
+//   * row_terms: D and the forward's LSE in log2 units per (row, head, token), 0 / -inf at pads;
 //   * dq_kernel: one workgroup per forward item (row, q-tile, KV head, chunk of its query
 //     heads), 8 waves of 32 query rows, walking the q-tile's k-tile list with K/V tiles
 //     staged in LDS (direct-to-LDS copies, two tiles ahead);
 //   * dkdv_kernel: one workgroup per (row, k-tile, KV head), 2 waves of 32 keys whose K and V
 //     fragments stay in registers, walking the k-tile's list of q-tiles (the transposed tile
-//     lists) and every query head of the group, with Q / dO / LSE / D of 64 queries at a time
-//     staged in LDS.
+//     lists) and every query head of the group in blocks of 32 queries, two blocks per
+//     LDS stage (Q, dO, LSE, D), the next stage copied while the current one is used.
 // Every result is written exactly once (no atomics); gradients of pads are zero.
 //
 // Orientation (32x32x16 bf16 MFMA, accumulator element i of lane l at row 8(i/4) + 4(l/32) +
@@ -24,6 +24,8 @@
 //   dkdv_kernel: S = Q K^T and dP = dO V^T (queries x keys, a key per lane), then
 //               dV^T += dO^T P and dK^T += Q^T dS.
 // The "transposed" operands (K^T, dO^T, Q^T) are LDS transpose reads of row-major tiles.
+// The softmax takes the LSE in log2 units (one FMA and one exp per element); the mask of a
+// PARTIAL tile is applied in its own uniform branch, so FULL tiles do no mask arithmetic.
 #include <type_traits>
 
 #include "internal.h"
@@ -36,15 +38,6 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
-
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 __device__ __forceinline__ floatx16 zero16() {
     floatx16 z;
@@ -60,7 +53,7 @@ struct BwdArgs {
     const void *q, *k, *v, *o, *dout;
     void *dq, *dk, *dv;
     const float *lse;
-    float *delta;
+    float *delta, *lse2;
     const int32_t *qt_ptr, *kt_idx;
     const uint8_t *kt_kind;
     const int32_t *kt_ptr, *q_list, *kwork;
@@ -72,40 +65,64 @@ struct BwdArgs {
 
 // ------------------------------------------------------------------------- tiles and operands
 //
-// Tiles are row-major [rows][D] bf16 in LDS with the 16-byte chunk index of each row XOR-ed
-// with the row (mod chunks per row), exactly as the HBM rows are copied in.
+// Tiles are row-major [rows][D] bf16 in LDS; the 16-byte chunks of each row are permuted by
+// XOR with sw(row), exactly as the HBM rows are copied in.  sw is chosen so that both kinds of
+// fragment read below hit distinct LDS banks (a row read: 32 rows, one chunk each; a transposed
+// read: 4 rows x 64 bytes per half-wave), and so that it repeats every 16 rows: row offsets that
+// are multiples of 16 then become instruction immediates while the lane part of every address
+// is computed once per kernel.
 template <int D>
 struct Tile {
     static constexpr int CPR = D / 8;                 // 16-byte chunks per row
     static constexpr int ROWB = D * 2;                // bytes per row
     static constexpr int NDS = D / 16;                // k-steps over D per 32x32x16 MFMA
     static constexpr int NDB = D / 32;                // 32-wide column blocks
-    static __device__ __forceinline__ int sw(int row) { return row & (CPR - 1); }
+    static __device__ __forceinline__ int sw(int row) {
+        if constexpr (CPR == 16) return (row & 15) ^ ((row & 3) << 2);
+        else return ((row >> 1) & 7) ^ (((row >> 1) & 1) << 2);
+    }
     // Byte offset of the chunk that holds (row, 8-element column group c).
     static __device__ __forceinline__ int chunk_at(int row, int c) { return row * ROWB + ((c ^ sw(row)) << 4); }
-    // Operand with row = l%32 of a 32-row block and k = 16 columns starting at 16 ds:
-    // lane l holds columns 16 ds + 8 (l/32) .. +7 of row rb + l%32.
-    static __device__ __forceinline__ bf16x8_t row_frag(const char *tile, int rb, int lane, int ds) {
-        const int row = rb + (lane & 31);
-        return *reinterpret_cast<const bf16x8_t *>(tile + chunk_at(row, 2 * ds + (lane >> 5)));
+    // Row operand (row = l%32 of a 32-row block, k = 16 columns from 16 ds): lane l holds
+    // columns 16 ds + 8 (l/32) .. +7.  Lane part for block row 0; add 32 * block * ROWB.
+    static __device__ __forceinline__ int row_lane(int lane, int ds) {
+        return chunk_at(lane & 31, 2 * ds + (lane >> 5));
     }
-    // Transposed operand of a 32-row block at rb: lane l holds column 32 db + l%32 of the 8
-    // rows rb + 16 ks + 4(l/32) + 0..3 and rb + 16 ks + 8 + 4(l/32) + 0..3 (the row order of
-    // an accumulator's registers 8 ks .. 8 ks + 7).  Two LDS transpose reads: in each 16-lane
-    // group, lane j points at row r0 + j/4, columns 4(j%4) .. +3 of a 16-column group and
-    // receives one column of rows r0 .. r0+3.
-    static __device__ __forceinline__ bf16x8_t tr_frag(const char *tile, int rb, int lane, int ks, int db) {
-        typedef shortx4 __attribute__((address_space(3))) *lds_p;
+    // Transposed operand of a 32-row block: lane l holds column 32 db + l%32 of rows
+    // 16 ks + 4(l/32) + 0..3 and 16 ks + 8 + 4(l/32) + 0..3 (the row order of an accumulator's
+    // registers 8 ks .. 8 ks + 7).  Two LDS transpose reads (r = 0, 1): in each 16-lane group,
+    // lane j points at row 8 r + 4 h + j/4, columns 4(j%4) .. +3 of a 16-column group and
+    // receives one column of 4 rows.  Lane part for block row 0, ks = 0; add
+    // (32 * block + 16 ks) * ROWB.
+    static __device__ __forceinline__ int tr_lane(int lane, int db, int r) {
         const int grp = lane >> 4, j = lane & 15, h = grp >> 1;
         const int col = 32 * db + 16 * (grp & 1) + 4 * (j & 3);
-        bf16x4_t y[2];
+        return chunk_at(8 * r + 4 * h + (j >> 2), col >> 3) + (col & 7) * 2;
+    }
+    static __device__ __forceinline__ bf16x8_t row_at(const char *p) {
+        return *reinterpret_cast<const bf16x8_t *>(p);
+    }
+    static __device__ __forceinline__ bf16x8_t tr_at(const char *p0, const char *p1) {
+        typedef shortx4 __attribute__((address_space(3))) *lds_p;
+        const bf16x4_t y0 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(p0)));
+        const bf16x4_t y1 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(p1)));
+        return __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+// Per-lane parts of the fragment addresses (computed once).
+template <int D>
+struct LaneOffsets {
+    int row[Tile<D>::NDS];
+    int tr[Tile<D>::NDB][2];
+    __device__ __forceinline__ explicit LaneOffsets(int lane) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int row = rb + 16 * ks + 8 * r + 4 * h + (j >> 2);
-            const char *p = tile + chunk_at(row, col >> 3) + (col & 7) * 2;
-            y[r] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(p)));
+        for (int ds = 0; ds < Tile<D>::NDS; ++ds) row[ds] = Tile<D>::row_lane(lane, ds);
+#pragma unroll
+        for (int db = 0; db < Tile<D>::NDB; ++db) {
+            tr[db][0] = Tile<D>::tr_lane(lane, db, 0);
+            tr[db][1] = Tile<D>::tr_lane(lane, db, 1);
         }
-        return __builtin_shufflevector(y[0], y[1], 0, 1, 2, 3, 4, 5, 6, 7);
     }
 };
 
@@ -120,8 +137,9 @@ __device__ __forceinline__ bf16x8_t acc_frag(const floatx16 &x, int ks) {
     return f;
 }
 
-// Direct-to-LDS buffer loads; see the forward kernel for why they are inline asm.  Offsets
-// past num_records read as zeros.
+// Direct-to-LDS buffer loads, issued as inline asm so that the compiler does not wait for them
+// before unrelated LDS reads (it cannot tell which LDS bytes they write).  Offsets past
+// num_records read as zeros.
 __device__ __forceinline__ int32x4_t buf_rsrc(const void *base, uint32_t num_records) {
     const uint64_t b = reinterpret_cast<uint64_t>(base);
     int32x4_t r;
@@ -170,26 +188,38 @@ __device__ __forceinline__ void copy_tile(const char *src, int n_valid, int stri
     }
 }
 
-// ------------------------------------------------------------------------------ row_delta
+// ------------------------------------------------------------------------------ row_terms
 //
 // D[r, h, i] = sum_d dO[r, i, h, d] * O[r, i, h, d] in fp32 for real tokens, 0 at pads (their
-// dO / O contents are never read).  One thread per (row, token, head).
-template <int D, class E>
-__global__ void row_delta(int32_t R, int32_t T, int32_t Hq, const E *__restrict__ o, const E *__restrict__ dout,
-                          const int32_t *__restrict__ n_real, float *__restrict__ delta) {
-    const int64_t id = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (id >= int64_t(R) * T * Hq) return;
-    const int h = int(id % Hq);
-    const int64_t ri = id / Hq;
+// dO / O contents are never read), and LSE2[r, h, i] = LSE[r, h, i] * log2(e).  D / 8 lanes
+// per (token, head) row, 16 bytes each, summed across the lanes.
+template <int D>
+__global__ void row_terms(int32_t R, int32_t T, int32_t Hq, const __bf16 *__restrict__ o,
+                          const __bf16 *__restrict__ dout, const float *__restrict__ lse,
+                          const int32_t *__restrict__ n_real, float *__restrict__ delta,
+                          float *__restrict__ lse2) {
+    constexpr int LPR = D / 8;
+    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t row = gid / LPR;                       // (r, i, h) in o's row order
+    const int part = int(gid % LPR);
+    if (row >= int64_t(R) * T * Hq) return;              // whole groups of LPR lanes
+    const int h = int(row % Hq);
+    const int64_t ri = row / Hq;
     const int r = int(ri / T), i = int(ri % T);
     float acc = 0.f;
     if (i < n_real[r]) {
-        const E *po = o + id * D;
-        const E *pd = dout + id * D;
-#pragma unroll 8
-        for (int d = 0; d < D; ++d) acc = fmaf(float(po[d]), float(pd[d]), acc);
+        const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(o + row * D + part * 8);
+        const bf16x8_t y = *reinterpret_cast<const bf16x8_t *>(dout + row * D + part * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(float(x[e]), float(y[e]), acc);
     }
-    delta[(int64_t(r) * Hq + h) * T + i] = acc;
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+    if (part == 0) {
+        const int64_t idx = (int64_t(r) * Hq + h) * T + i;
+        delta[idx] = acc;
+        lse2[idx] = lse[idx] * kLog2e;
+    }
 }
 
 // ------------------------------------------------------------------------------ dq_kernel
@@ -205,6 +235,49 @@ struct DqLds {
     static constexpr int PERW = 2 * (TILE / 1024) / kDqWaves;   // K and V copies per wave per tile
     static_assert((2 * (TILE / 1024)) % kDqWaves == 0, "waves must split a tile evenly");
 };
+
+// One k-tile of the dq pass for a wave's 32 queries: P^T, dS^T of both 32-key blocks, then
+// dQ^T += K^T dS^T.  Element i of the score accumulators is key 32 kb + 8(i/4) + 4h + i%4.
+template <int D>
+__device__ __forceinline__ void dq_tile(const char *Kt, const char *Vt, const int32_t *KEs, const LaneOffsets<D> &lo,
+                                        const bf16x8_t (&qf)[D / 16], const bf16x8_t (&dof)[D / 16], float c,
+                                        float lse2, float dlt, bool partial, int dq_, int qpos,
+                                        floatx16 (&acc)[D / 32]) {
+    using TL = Tile<D>;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        floatx16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ds = 0; ds < TL::NDS; ++ds) {
+            s = mfma(TL::row_at(Kt + lo.row[ds] + 32 * kb * TL::ROWB), qf[ds], s);
+            dp = mfma(TL::row_at(Vt + lo.row[ds] + 32 * kb * TL::ROWB), dof[ds], dp);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
+        if (partial) {             // uniform: FULL tiles skip the mask
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int4 ke = *reinterpret_cast<const int4 *>(KEs + 32 * kb + 8 * i4);
+                const int kev[4] = {ke.x, ke.y, ke.z, ke.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int cc = 32 * kb + 8 * i4 + e;
+                    s[4 * i4 + e] = ((cc <= dq_) & (qpos < kev[e])) ? s[4 * i4 + e] : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = s[i] * (dp[i] - dlt);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8_t dsf = acc_frag(s, ks);
+            const int rofs = (32 * kb + 16 * ks) * TL::ROWB;
+#pragma unroll
+            for (int db = 0; db < TL::NDB; ++db)
+                acc[db] = mfma(TL::tr_at(Kt + lo.tr[db][0] + rofs, Kt + lo.tr[db][1] + rofs), dsf, acc[db]);
+        }
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(kDqWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -246,9 +319,10 @@ void dq_kernel(BwdArgs a) {
             dof[ds] = z;
         }
     }
-    const float lse_raw = a.lse[(int64_t(r) * a.Hq + head) * T + qpos];
-    const float lse2 = (qreal && lse_raw > -INFINITY) ? lse_raw * kLog2e : INFINITY;
+    const float lse2_raw = a.lse2[(int64_t(r) * a.Hq + head) * T + qpos];
+    const float lse2 = (qreal && lse2_raw > -INFINITY) ? lse2_raw : INFINITY;
     const float dlt = a.delta[(int64_t(r) * a.Hq + head) * T + qpos];
+    const LaneOffsets<D> lo(lane);
 
     floatx16 acc[TL::NDB];
 #pragma unroll
@@ -292,43 +366,12 @@ void dq_kernel(BwdArgs a) {
         if (t + 2 < N) issue(t + 2);
         const int ent = __builtin_amdgcn_readfirstlane(lst[t]);
         const int kt = ent >> 2;
-        const bool partial = (ent & 3) == kTilePartial;
         const int slot = t % NB;
         const char *Kt = smem + LD::K_OFF + slot * LD::TILE;
         const char *Vt = smem + LD::V_OFF + slot * LD::TILE;
         const int32_t *KEs = reinterpret_cast<const int32_t *>(smem + LD::KE_OFF + slot * 256) + 4 * h;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            floatx16 s = zero16(), dp = zero16();
-#pragma unroll
-            for (int ds = 0; ds < TL::NDS; ++ds) {
-                s = mfma(TL::row_frag(Kt, 32 * kb, lane, ds), qf[ds], s);
-                dp = mfma(TL::row_frag(Vt, 32 * kb, lane, ds), dof[ds], dp);
-            }
-            // P^T and dS^T; element i is key 32 kb + 8(i/4) + 4h + i%4 of the tile.
-            const int dq_ = qpos - kt * kBK - 4 * h;
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                int4 ke = make_int4(INT32_MAX, INT32_MAX, INT32_MAX, INT32_MAX);
-                if (partial) ke = *reinterpret_cast<const int4 *>(KEs + 32 * kb + 8 * i4);
-                const int kev[4] = {ke.x, ke.y, ke.z, ke.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * i4 + e, c = 32 * kb + 8 * i4 + e;
-                    const bool vis = !partial || ((c <= dq_) & (qpos < kev[e]));
-                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.c, -lse2)) : 0.f;
-                    s[i] = p * (dp[i] - dlt);
-                }
-            }
-            // dQ^T += K^T dS^T
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8_t dsf = acc_frag(s, ks);
-#pragma unroll
-                for (int db = 0; db < TL::NDB; ++db)
-                    acc[db] = mfma(TL::tr_frag(Kt, 32 * kb, lane, ks, db), dsf, acc[db]);
-            }
-        }
+        const int dq_ = qpos - kt * kBK - 4 * h;
+        dq_tile<D>(Kt, Vt, KEs, lo, qf, dof, a.c, lse2, dlt, (ent & 3) == kTilePartial, dq_, qpos, acc);
     }
 
     // dQ = scale * (dQ^T)^T; lane holds query qpos, 4 consecutive d per register group.
@@ -349,14 +392,104 @@ void dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------- dkdv_kernel
 constexpr int kKvWaves = 2;               // 32 keys each: one 64-key tile per workgroup
-constexpr int kQB = 64;                   // queries staged per unit
+constexpr int kQBlk = 32;                 // queries per block; two blocks per LDS stage
 
 template <int D>
 struct KvLds {
-    static constexpr int TILE = kQB * D * 2;
-    static constexpr int STAGE = 2 * TILE + 2 * kQB * 4;   // Q, dO, LSE, D
-    static constexpr int Q_OFF = 0, DO_OFF = TILE, LSE_OFF = 2 * TILE, DL_OFF = 2 * TILE + kQB * 4;
+    static constexpr int TILE = kQBlk * D * 2;                  // Q or dO of one block
+    static constexpr int BLK = 2 * TILE + 2 * kQBlk * 4;       // Q, dO, LSE2, D of one block
+    static constexpr int Q_OFF = 0, DO_OFF = TILE, LSE_OFF = 2 * TILE, DL_OFF = 2 * TILE + kQBlk * 4;
+    static constexpr int STAGE = 2 * BLK;
     static constexpr int NSTAGE = 2;
+};
+
+// Softmax of one block for a wave's 32 keys: P and dS as bf16 operands (accumulator register
+// order).  Element i is query q0 + 8(i/4) + 4h + i%4 of the block.
+template <int D>
+__device__ __forceinline__ void kv_softmax(const floatx16 &s, const floatx16 &dp, const char *blk, int h, float c,
+                                           bool partial, int key, int kend_k, int qh, bf16x8_t (&pf)[2],
+                                           bf16x8_t (&sf)[2]) {
+    using LD = KvLds<D>;
+    const float *LS = reinterpret_cast<const float *>(blk + LD::LSE_OFF) + 4 * h;
+    const float *DL = reinterpret_cast<const float *>(blk + LD::DL_OFF) + 4 * h;
+    floatx16 pm, dsm;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 l4 = *reinterpret_cast<const float4 *>(LS + 8 * i4);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pm[4 * i4 + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * i4 + e], c, -lv[e]));
+    }
+    if (partial) {                 // uniform: stages of FULL blocks skip the mask
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int q = qh + 8 * i4 + e;
+                pm[4 * i4 + e] = ((key <= q) & (q < kend_k)) ? pm[4 * i4 + e] : 0.f;
+            }
+    }
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 d4 = *reinterpret_cast<const float4 *>(DL + 8 * i4);
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsm[4 * i4 + e] = pm[4 * i4 + e] * (dp[4 * i4 + e] - dv4[e]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        pf[ks] = acc_frag(pm, ks);
+        sf[ks] = acc_frag(dsm, ks);
+    }
+}
+
+// One LDS stage (blocks A and B) for a wave: S and dP of both blocks, then the softmax and
+// the dV / dK updates of A, then of B.
+template <int D>
+__device__ __forceinline__ void kv_stage(const char *st, const LaneOffsets<D> &lo, const bf16x8_t (&kf)[D / 16],
+                                         const bf16x8_t (&vf)[D / 16], float c, int h, int key, int kend_k,
+                                         int qa, int qb, bool pa, bool pb, floatx16 (&dk)[D / 32],
+                                         floatx16 (&dv)[D / 32]) {
+    using TL = Tile<D>;
+    using LD = KvLds<D>;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const char *blk = st + b * LD::BLK;
+        const char *Qt = blk + LD::Q_OFF;
+        const char *Ot = blk + LD::DO_OFF;
+        floatx16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ds = 0; ds < TL::NDS; ++ds) {
+            s = mfma(TL::row_at(Qt + lo.row[ds]), kf[ds], s);
+            dp = mfma(TL::row_at(Ot + lo.row[ds]), vf[ds], dp);
+        }
+        bf16x8_t pf[2], sf[2];
+        kv_softmax<D>(s, dp, blk, h, c, b == 0 ? pa : pb, key, kend_k, (b == 0 ? qa : qb) + 4 * h, pf, sf);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int rofs = 16 * ks * TL::ROWB;
+#pragma unroll
+            for (int db = 0; db < TL::NDB; ++db) {
+                dv[db] = mfma(TL::tr_at(Ot + lo.tr[db][0] + rofs, Ot + lo.tr[db][1] + rofs), pf[ks], dv[db]);
+                dk[db] = mfma(TL::tr_at(Qt + lo.tr[db][0] + rofs, Qt + lo.tr[db][1] + rofs), sf[ks], dk[db]);
+            }
+        }
+    }
+}
+
+// Position in a k-tile's sequence of 32-query blocks: list entry, query head of the group,
+// 32-query chunk of the q-tile.
+struct BlockCursor {
+    int e = 0, hd = 0, ch = 0;
+    __device__ __forceinline__ void next(int G, int CH) {
+        if (++ch == CH) {
+            ch = 0;
+            if (++hd == G) {
+                hd = 0;
+                ++e;
+            }
+        }
+    }
 };
 
 template <int D>
@@ -376,7 +509,7 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     const int n_real = a.n_real[r];
     const int key = kt * kBK + 32 * wave + l32;         // this lane's key (column of S / dP)
     const bool kreal = key < n_real;
-    const int kend_k = a.kend[int64_t(r) * T + key];
+    const int kend_k = a.kend[int64_t(r) * T + key];    // == key at pads: never visible
 
     // K and V fragments of the wave's 32 keys (B operands of S = Q K^T and dP = dO V^T):
     // lane holds columns 16 ds + 8h .. +7 of its key; zero at pad keys.
@@ -398,6 +531,7 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
             vf[ds] = zy;
         }
     }
+    const LaneOffsets<D> lo(lane);
     floatx16 dk[TL::NDB], dv[TL::NDB];       // dK^T, dV^T: rows d, a key per lane
 #pragma unroll
     for (int db = 0; db < TL::NDB; ++db) {
@@ -405,34 +539,49 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
         dv[db] = zero16();
     }
 
-    // Units: (q-tile of the k-tile's list, query head of the group, 64-query chunk).
+    // Blocks: (entry of the k-tile's q-tile list, query head, 32-query chunk); two per stage.
+    // An odd count is padded with an empty block (no rows copied, so Q = dO = LSE2 = D = 0,
+    // and a query position past every kend so that its P is 0).
     const int32_t l_begin = a.kt_ptr[ktile];
     const int NL = a.kt_ptr[ktile + 1] - l_begin;
-    const int QB = min(a.BQ, kQB), n_chunks = a.BQ / QB;
-    const int per_tile = a.G * n_chunks;
-    const int NU = NL * per_tile;
+    const int CH = a.BQ / kQBlk;
+    const int NBLK = NL * a.G * CH;
+    const int NU = (NBLK + 1) / 2;
     const int q_stride = a.Hq * D * 2;
     const uint32_t lds0 = lds_base(smem);
-    auto unit = [&](int n, int &q0, int &head, bool &partial) __attribute__((always_inline)) {
-        const int ent = __builtin_amdgcn_readfirstlane(a.q_list[l_begin + n / per_tile]);
-        const int rem = n % per_tile;
-        head = g * a.G + rem / n_chunks;
-        q0 = (ent >> 2) * a.BQ + (rem % n_chunks) * QB;
+    constexpr int kNoQuery = 1 << 30;
+    auto block_at = [&](const BlockCursor &cu, int b, int &q0, int &head, bool &partial) __attribute__((always_inline)) {
+        if (b >= NBLK) {
+            q0 = kNoQuery;
+            head = g * a.G;
+            partial = true;
+            return;
+        }
+        const int ent = __builtin_amdgcn_readfirstlane(a.q_list[l_begin + cu.e]);
+        q0 = (ent >> 2) * a.BQ + cu.ch * kQBlk;
+        head = g * a.G + cu.hd;
         partial = (ent & 3) == kTilePartial;
     };
+    BlockCursor ci, cc;            // next block to copy / to compute
     auto issue = [&](int n) __attribute__((always_inline)) {
-        int q0, head;
-        bool partial;
-        unit(n, q0, head, partial);
         const uint32_t st = lds0 + (n % LD::NSTAGE) * LD::STAGE;
-        const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - q0, 0), QB));
-        const int64_t roff = ((int64_t(r) * T + q0) * a.Hq + head) * D * 2;
-        copy_tile<D>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, st + LD::Q_OFF, QB, wave, kKvWaves, lane);
-        copy_tile<D>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride, st + LD::DO_OFF, QB, wave, kKvWaves, lane);
-        const int64_t loff = (int64_t(r) * a.Hq + head) * T + q0;
-        if (wave == 0 && lane < QB) {
-            buf_to_lds4(buf_rsrc(a.lse + loff, uint32_t(QB) * 4), st + LD::LSE_OFF, lane * 4);
-            buf_to_lds4(buf_rsrc(a.delta + loff, uint32_t(QB) * 4), st + LD::DL_OFF, lane * 4);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            int q0, head;
+            bool partial;
+            block_at(ci, 2 * n + b, q0, head, partial);
+            ci.next(a.G, CH);
+            const int n_valid = q0 == kNoQuery ? 0 : __builtin_amdgcn_readfirstlane(min(max(n_real - q0, 0), kQBlk));
+            const int q0c = q0 == kNoQuery ? 0 : q0;
+            const int64_t roff = ((int64_t(r) * T + q0c) * a.Hq + head) * D * 2;
+            const uint32_t bl = st + b * LD::BLK;
+            copy_tile<D>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, bl + LD::Q_OFF, kQBlk, wave, kKvWaves, lane);
+            copy_tile<D>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride, bl + LD::DO_OFF, kQBlk, wave, kKvWaves, lane);
+            if (wave == b && lane < kQBlk) {
+                const int64_t loff = (int64_t(r) * a.Hq + head) * T + q0c;
+                buf_to_lds4(buf_rsrc(a.lse2 + loff, uint32_t(n_valid) * 4), bl + LD::LSE_OFF, lane * 4);
+                buf_to_lds4(buf_rsrc(a.delta + loff, uint32_t(n_valid) * 4), bl + LD::DL_OFF, lane * 4);
+            }
         }
     };
 
@@ -441,49 +590,14 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
         wait_loads();
         block_barrier();
         if (n + 1 < NU) issue(n + 1);
-        int q0, head;
-        bool partial;
-        unit(n, q0, head, partial);
+        int qa, qb, ha, hb;
+        bool pa, pb;
+        block_at(cc, 2 * n, qa, ha, pa);
+        cc.next(a.G, CH);
+        block_at(cc, 2 * n + 1, qb, hb, pb);
+        cc.next(a.G, CH);
         const char *st = smem + (n % LD::NSTAGE) * LD::STAGE;
-        const char *Qt = st + LD::Q_OFF;
-        const char *Ot = st + LD::DO_OFF;
-        const float *LS = reinterpret_cast<const float *>(st + LD::LSE_OFF);
-        const float *DL = reinterpret_cast<const float *>(st + LD::DL_OFF);
-        for (int qb = 0; qb < QB / 32; ++qb) {
-            floatx16 s = zero16(), dp = zero16();
-#pragma unroll
-            for (int ds = 0; ds < TL::NDS; ++ds) {
-                s = mfma(TL::row_frag(Qt, 32 * qb, lane, ds), kf[ds], s);
-                dp = mfma(TL::row_frag(Ot, 32 * qb, lane, ds), vf[ds], dp);
-            }
-            // Element i is query q0 + 32 qb + 8(i/4) + 4h + i%4; LSE and D four at a time.
-            floatx16 pm;
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int qi = 32 * qb + 8 * i4 + 4 * h;
-                const float4 l4 = *reinterpret_cast<const float4 *>(LS + qi);
-                const float4 d4 = *reinterpret_cast<const float4 *>(DL + qi);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * i4 + e, q = q0 + qi + e;
-                    const bool vis = kreal & (!partial || ((key <= q) & (q < kend_k))) & (lv[e] > -INFINITY);
-                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.c, -lv[e] * kLog2e)) : 0.f;
-                    pm[i] = p;
-                    s[i] = p * (dp[i] - dv4[e]);
-                }
-            }
-            // dV^T += dO^T P ;  dK^T += Q^T dS
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8_t pf = acc_frag(pm, ks), sf = acc_frag(s, ks);
-#pragma unroll
-                for (int db = 0; db < TL::NDB; ++db) {
-                    dv[db] = mfma(TL::tr_frag(Ot, 32 * qb, lane, ks, db), pf, dv[db]);
-                    dk[db] = mfma(TL::tr_frag(Qt, 32 * qb, lane, ks, db), sf, dk[db]);
-                }
-            }
-        }
+        kv_stage<D>(st, lo, kf, vf, a.c, h, key, kend_k, qa, qb, pa, pb, dk, dv);
     }
 
     // dK = scale dS^T Q, dV = P^T dO: lane holds its key, 4 consecutive d per register group.
@@ -511,11 +625,11 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
 
 template <int D>
 hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, hipStream_t s) {
-    const int64_t n_rows = int64_t(R) * a.T * a.Hq;
-    if (n_rows > 0) {
-        row_delta<D, __bf16><<<int((n_rows + 255) / 256), 256, 0, s>>>(
-            R, a.T, a.Hq, reinterpret_cast<const __bf16 *>(a.o), reinterpret_cast<const __bf16 *>(a.dout),
-            a.n_real, a.delta);
+    const int64_t n_threads = int64_t(R) * a.T * a.Hq * (D / 8);
+    if (n_threads > 0) {
+        row_terms<D><<<int((n_threads + 255) / 256), 256, 0, s>>>(
+            R, a.T, a.Hq, reinterpret_cast<const __bf16 *>(a.o), reinterpret_cast<const __bf16 *>(a.dout), a.lse,
+            a.n_real, a.delta, a.lse2);
     }
     if (n_items_q > 0) {
         const int smem = DqLds<D>::LIST_OFF + 4 * ((a.nK + 3) & ~3);
@@ -545,6 +659,7 @@ hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b,
     a.dq = dq; a.dk = dk; a.dv = dv;
     a.lse = lse;
     a.delta = reinterpret_cast<float *>(bws + b.delta);
+    a.lse2 = reinterpret_cast<float *>(bws + b.lse2);
     a.qt_ptr = reinterpret_cast<const int32_t *>(ws + w.qt_ptr);
     a.kt_idx = reinterpret_cast<const int32_t *>(ws + w.kt_idx);
     a.kt_kind = reinterpret_cast<const uint8_t *>(ws + w.kt_kind);
@@ -564,6 +679,7 @@ hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b,
     const int64_t n_k = int64_t(sh.R) * w.nK * sh.Hkv;
     if (n_q > INT32_MAX || n_k > INT32_MAX) return hipErrorInvalidValue;
     if (sh.dtype != TREE_DT_BF16) return hipErrorInvalidValue;
+    if (sh.BQ % kQBlk != 0) return hipErrorInvalidValue;
     if (sh.D == 128) return launch_d<128>(a, sh.R, int(n_q), int(n_k), s);
     if (sh.D == 64) return launch_d<64>(a, sh.R, int(n_q), int(n_k), s);
     return hipErrorInvalidValue;

@@ -61,6 +61,7 @@ inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_
 // Backward workspace layout (caller-allocated, filled by tree_attn_bwd_plan / tree_attn_bwd).
 struct BwdLayout {
     size_t delta = 0;     // float[R*Hq*T]: rowsum(dO * O) per (row, head, token); 0 at pads
+    size_t lse2 = 0;      // float[R*Hq*T]: the forward's LSE times log2(e)
     size_t kt_ptr = 0;    // int32[R*nK + 1]: CSR over (row, k-tile) of the q-tiles that see it
     size_t q_list = 0;    // int32[R*nQ*nK]: q-tile * 4 + class, ascending q-tile per k-tile
     size_t kwork = 0;     // int32[R*nK]: (row, k-tile) items, longest list first
@@ -73,6 +74,7 @@ inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
     b.delta = take(size_t(w.R) * Hq * w.T * sizeof(float));
+    b.lse2 = take(size_t(w.R) * Hq * w.T * sizeof(float));
     b.kt_ptr = take((size_t(w.R) * w.nK + 1) * sizeof(int32_t));
     b.q_list = take(size_t(w.R) * w.nQ * w.nK * sizeof(int32_t));
     b.kwork = take(size_t(w.R) * w.nK * sizeof(int32_t));
