@@ -206,20 +206,23 @@ int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const 
  *
  * tree_attn_bwd_workspace_size: bytes of the caller-allocated backward workspace `bws`
  *   (256-byte aligned): per-token row terms D and log2-scaled LSE ([R, Hq, T] fp32 each)
- *   plus the per-k-tile lists.
- * tree_attn_bwd_plan: from the forward plan in `ws`, build into `bws` the lists of q-tiles that
- *   see each k-tile (the transposed tile lists: ascending q-tile, entry = q_tile * 4 + class)
- *   and the order of the k-tile work.  Once per batch, like tree_attn_plan; asynchronous.
+ *   plus the per-pair q-tile lists below.
+ * tree_attn_bwd_plan: from the forward plan in `ws`, build into `bws`, for every pair of
+ *   k-tiles (2p, 2p+1) of a row, the list of q-tiles that see either of them (ascending, entry =
+ *   q_tile * 16 + class(2p) * 4 + class(2p+1), classes as in tree_tile_view, a missing k-tile
+ *   2p+1 counting as SKIP) and the order of the pair work.  Once per batch, like
+ *   tree_attn_plan; asynchronous.
  * tree_attn_bwd_tiles: device pointers (into bws) of those lists, for tests:
- *   kt_ptr[R * n_ktiles + 1] CSR over (row, k-tile), q_list the entries.
+ *   kp_ptr[R * ceil(n_ktiles / 2) + 1] CSR over (row, pair), kp_list the entries.
  * tree_attn_bwd: q, k, v as given to tree_attn_fwd; o and lse as it returned them; dout in
  *   q's layout; writes dq (q's layout), dk and dv (k's layout), bf16.  Overwrites the row
- *   terms in bws (the lists are kept).  Asynchronous.  Errors: TREE_E_INVAL, TREE_E_UNSUPPORTED, TREE_E_HIP.
+ *   terms in bws (the lists are kept).  Asynchronous.  Errors: TREE_E_INVAL,
+ *   TREE_E_UNSUPPORTED, TREE_E_HIP.
  */
 int tree_attn_bwd_workspace_size(const tree_attn_desc *d, size_t *bytes);
 int tree_attn_bwd_plan(const tree_attn_desc *d, const void *ws, void *bws, void *stream);
-int tree_attn_bwd_tiles(const tree_attn_desc *d, const void *bws, const int32_t **kt_ptr,
-                        const int32_t **q_list);
+int tree_attn_bwd_tiles(const tree_attn_desc *d, const void *bws, const int32_t **kp_ptr,
+                        const int32_t **kp_list);
 int tree_attn_bwd(const tree_attn_desc *d, const void *ws, void *bws, const void *q, const void *k,
                   const void *v, const void *o, const float *lse, const void *dout, void *dq,
                   void *dk, void *dv, void *stream);

@@ -13,7 +13,7 @@ carry the C names of ``include/treeattn.h``:
   tree_attn_fwd(desc, ws, q, k, v, o, lse)  (async on the current stream)
   tree_attn_bwd_workspace_size(desc) -> bytes
   tree_attn_bwd_plan(desc, ws, bws)  (async on the current stream)
-  tree_attn_bwd_tiles(desc, bws)     -> (kt_ptr, q_list) device pointers
+  tree_attn_bwd_tiles(desc, bws)     -> (kp_ptr, kp_list) device pointers
   tree_attn_bwd(desc, ws, bws, q, k, v, o, lse, dout, dq, dk, dv)  (async on the current stream)
 
 plus thin conveniences ``make_desc``, ``attn_plan``, ``attn_fwd`` and ``attn_bwd`` that allocate torch

@@ -27,6 +27,10 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 HIP_SOURCES = ["classify.hip", "attn_fwd.hip", "attn_bwd.hip", "capi.hip"]
+# Per-source device flags.  The backward keeps every MFMA result in ordinary VGPRs: its
+# dK/dV kernel runs one wave per SIMD, and with the default accumulator-register form the
+# score MFMAs' results are copied back to VGPRs for the softmax (one extra VALU op per value).
+SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_SOURCES = ["plan.cpp"]
 
 
@@ -43,7 +47,7 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
+        cmd = [HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c",
                os.path.join(CSRC, src), "-o", obj]
         if save_temps:
             cmd.insert(1, "-save-temps=obj")

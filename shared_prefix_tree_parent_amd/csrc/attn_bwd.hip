@@ -11,10 +11,11 @@
 //   * dq_kernel: one workgroup per forward item (row, q-tile, KV head, chunk of its query
 //     heads), 8 waves of 32 query rows, walking the q-tile's k-tile list with K/V tiles
 //     staged in LDS (direct-to-LDS copies, two tiles ahead);
-//   * dkdv_kernel: one workgroup per (row, k-tile, KV head), 2 waves of 32 keys whose K and V
-//     fragments stay in registers, walking the k-tile's list of q-tiles (the transposed tile
-//     lists) and every query head of the group in blocks of 32 queries, two blocks per
-//     LDS stage (Q, dO, LSE, D), the next stage copied while the current one is used.
+//   * dkdv_kernel: one workgroup per (row, pair of k-tiles, KV head), 4 waves of 32 keys whose
+//     K and V fragments stay in registers, walking the pair's list of q-tiles (the transposed
+//     tile lists) and every query head of the group in blocks of 32 queries; each block's Q,
+//     dO, LSE and D are staged in LDS once for all four waves, three blocks ahead.  A wave
+//     whose k-tile does not see a block's q-tile skips it.
 // Every result is written exactly once (no atomics); gradients of pads are zero.
 //
 // Orientation (32x32x16 bf16 MFMA, accumulator element i of lane l at row 8(i/4) + 4(l/32) +
@@ -56,9 +57,9 @@ struct BwdArgs {
     float *delta, *lse2;
     const int32_t *qt_ptr, *kt_idx;
     const uint8_t *kt_kind;
-    const int32_t *kt_ptr, *q_list, *kwork;
+    const int32_t *kp_ptr, *kp_list, *kwork;
     const int32_t *kend, *work, *n_real, *status;
-    int32_t T, Hq, Hkv, G, HCH, nQ, nK, L, BQ;
+    int32_t T, Hq, Hkv, G, HCH, nQ, nK, nP, L, BQ;
     float c;       // scale * log2(e)
     float scale;
 };
@@ -391,20 +392,23 @@ void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- dkdv_kernel
-constexpr int kKvWaves = 2;               // 32 keys each: one 64-key tile per workgroup
-constexpr int kQBlk = 32;                 // queries per block; two blocks per LDS stage
+constexpr int kKvWaves = 4;               // 32 keys each: a pair of 64-key tiles per workgroup
+constexpr int kQBlk = 32;                 // queries per block (one LDS stage)
 
 template <int D>
 struct KvLds {
     static constexpr int TILE = kQBlk * D * 2;                  // Q or dO of one block
     static constexpr int BLK = 2 * TILE + 2 * kQBlk * 4;       // Q, dO, LSE2, D of one block
     static constexpr int Q_OFF = 0, DO_OFF = TILE, LSE_OFF = 2 * TILE, DL_OFF = 2 * TILE + kQBlk * 4;
-    static constexpr int STAGE = 2 * BLK;
-    static constexpr int NSTAGE = 2;
+    static constexpr int NS = 4;                                // stages, one block each
+    static constexpr int AHEAD = NS - 1;                        // blocks copied ahead of the one in use
+    // copies per wave per block: Q and dO split over the waves; waves 0 and 1 also copy LSE2 / D
+    static constexpr int PERW = 2 * (TILE / 1024) / kKvWaves;
+    static_assert((2 * (TILE / 1024)) % kKvWaves == 0, "waves must split a block evenly");
 };
 
 // Softmax of one block for a wave's 32 keys: P and dS as bf16 operands (accumulator register
-// order).  Element i is query q0 + 8(i/4) + 4h + i%4 of the block.
+// order).  Element i is query q0 + 8(i/4) + 4h + i%4 of the block (qh = q0 + 4h).
 template <int D>
 __device__ __forceinline__ void kv_softmax(const floatx16 &s, const floatx16 &dp, const char *blk, int h, float c,
                                            bool partial, int key, int kend_k, int qh, bf16x8_t (&pf)[2],
@@ -420,7 +424,7 @@ __device__ __forceinline__ void kv_softmax(const floatx16 &s, const floatx16 &dp
 #pragma unroll
         for (int e = 0; e < 4; ++e) pm[4 * i4 + e] = __builtin_amdgcn_exp2f(fmaf(s[4 * i4 + e], c, -lv[e]));
     }
-    if (partial) {                 // uniform: stages of FULL blocks skip the mask
+    if (partial) {                 // uniform: FULL blocks skip the mask
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
 #pragma unroll
@@ -443,41 +447,35 @@ __device__ __forceinline__ void kv_softmax(const floatx16 &s, const floatx16 &dp
     }
 }
 
-// One LDS stage (blocks A and B) for a wave: S and dP of both blocks, then the softmax and
-// the dV / dK updates of A, then of B.
+// One block for a wave: S and dP, softmax, then dV^T += dO^T P and dK^T += Q^T dS.
 template <int D>
-__device__ __forceinline__ void kv_stage(const char *st, const LaneOffsets<D> &lo, const bf16x8_t (&kf)[D / 16],
+__device__ __forceinline__ void kv_block(const char *blk, const LaneOffsets<D> &lo, const bf16x8_t (&kf)[D / 16],
                                          const bf16x8_t (&vf)[D / 16], float c, int h, int key, int kend_k,
-                                         int qa, int qb, bool pa, bool pb, floatx16 (&dk)[D / 32],
-                                         floatx16 (&dv)[D / 32]) {
+                                         int q0, bool partial, floatx16 (&dk)[D / 32], floatx16 (&dv)[D / 32]) {
     using TL = Tile<D>;
     using LD = KvLds<D>;
+    const char *Qt = blk + LD::Q_OFF;
+    const char *Ot = blk + LD::DO_OFF;
+    floatx16 s = zero16(), dp = zero16();
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const char *blk = st + b * LD::BLK;
-        const char *Qt = blk + LD::Q_OFF;
-        const char *Ot = blk + LD::DO_OFF;
-        floatx16 s = zero16(), dp = zero16();
+    for (int ds = 0; ds < TL::NDS; ++ds) {
+        s = mfma(TL::row_at(Qt + lo.row[ds]), kf[ds], s);
+        dp = mfma(TL::row_at(Ot + lo.row[ds]), vf[ds], dp);
+    }
+    bf16x8_t pf[2], sf[2];
+    kv_softmax<D>(s, dp, blk, h, c, partial, key, kend_k, q0 + 4 * h, pf, sf);
 #pragma unroll
-        for (int ds = 0; ds < TL::NDS; ++ds) {
-            s = mfma(TL::row_at(Qt + lo.row[ds]), kf[ds], s);
-            dp = mfma(TL::row_at(Ot + lo.row[ds]), vf[ds], dp);
-        }
-        bf16x8_t pf[2], sf[2];
-        kv_softmax<D>(s, dp, blk, h, c, b == 0 ? pa : pb, key, kend_k, (b == 0 ? qa : qb) + 4 * h, pf, sf);
+    for (int ks = 0; ks < 2; ++ks) {
+        const int rofs = 16 * ks * TL::ROWB;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int rofs = 16 * ks * TL::ROWB;
-#pragma unroll
-            for (int db = 0; db < TL::NDB; ++db) {
-                dv[db] = mfma(TL::tr_at(Ot + lo.tr[db][0] + rofs, Ot + lo.tr[db][1] + rofs), pf[ks], dv[db]);
-                dk[db] = mfma(TL::tr_at(Qt + lo.tr[db][0] + rofs, Qt + lo.tr[db][1] + rofs), sf[ks], dk[db]);
-            }
+        for (int db = 0; db < TL::NDB; ++db) {
+            dv[db] = mfma(TL::tr_at(Ot + lo.tr[db][0] + rofs, Ot + lo.tr[db][1] + rofs), pf[ks], dv[db]);
+            dk[db] = mfma(TL::tr_at(Qt + lo.tr[db][0] + rofs, Qt + lo.tr[db][1] + rofs), sf[ks], dk[db]);
         }
     }
 }
 
-// Position in a k-tile's sequence of 32-query blocks: list entry, query head of the group,
+// Position in a pair's sequence of 32-query blocks: list entry, query head of the group,
 // 32-query chunk of the q-tile.
 struct BlockCursor {
     int e = 0, hd = 0, ch = 0;
@@ -503,19 +501,22 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
     const int g = blockIdx.x % a.Hkv, item = blockIdx.x / a.Hkv;
-    const int ktile = a.kwork[item];
-    const int r = ktile / a.nK, kt = ktile % a.nK;
+    const int pitem = a.kwork[item];
+    const int r = pitem / a.nP, pr = pitem % a.nP;
     const int T = a.T;
     const int n_real = a.n_real[r];
-    const int key = kt * kBK + 32 * wave + l32;         // this lane's key (column of S / dP)
+    const int half = wave >> 1;                          // k-tile 2 pr + half
+    const int key = (2 * pr + half) * kBK + 32 * (wave & 1) + l32;   // this lane's key
+    const bool kin = key < T;                            // false only past an odd k-tile count
     const bool kreal = key < n_real;
-    const int kend_k = a.kend[int64_t(r) * T + key];    // == key at pads: never visible
+    const int kend_k = kin ? a.kend[int64_t(r) * T + key] : key;      // == key at pads: never visible
+    const int cls_shift = half ? 0 : 2;
 
     // K and V fragments of the wave's 32 keys (B operands of S = Q K^T and dP = dO V^T):
     // lane holds columns 16 ds + 8h .. +7 of its key; zero at pad keys.
     bf16x8_t kf[TL::NDS], vf[TL::NDS];
     {
-        const int64_t off = ((int64_t(r) * T + key) * a.Hkv + g) * D;
+        const int64_t off = ((int64_t(r) * T + (kin ? key : 0)) * a.Hkv + g) * D;
         const bf16x8_t *pk = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.k) + off);
         const bf16x8_t *pv = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.v) + off);
 #pragma unroll
@@ -539,68 +540,61 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
         dv[db] = zero16();
     }
 
-    // Blocks: (entry of the k-tile's q-tile list, query head, 32-query chunk); two per stage.
-    // An odd count is padded with an empty block (no rows copied, so Q = dO = LSE2 = D = 0,
-    // and a query position past every kend so that its P is 0).
-    const int32_t l_begin = a.kt_ptr[ktile];
-    const int NL = a.kt_ptr[ktile + 1] - l_begin;
+    // Blocks: (entry of the pair's q-tile list, query head, 32-query chunk), one LDS stage each,
+    // copied AHEAD blocks ahead of the one in use.
+    const int32_t l_begin = a.kp_ptr[pitem];
+    const int NL = a.kp_ptr[pitem + 1] - l_begin;
     const int CH = a.BQ / kQBlk;
-    const int NBLK = NL * a.G * CH;
-    const int NU = (NBLK + 1) / 2;
+    const int NB = NL * a.G * CH;
     const int q_stride = a.Hq * D * 2;
     const uint32_t lds0 = lds_base(smem);
-    constexpr int kNoQuery = 1 << 30;
-    auto block_at = [&](const BlockCursor &cu, int b, int &q0, int &head, bool &partial) __attribute__((always_inline)) {
-        if (b >= NBLK) {
-            q0 = kNoQuery;
-            head = g * a.G;
-            partial = true;
-            return;
-        }
-        const int ent = __builtin_amdgcn_readfirstlane(a.q_list[l_begin + cu.e]);
-        q0 = (ent >> 2) * a.BQ + cu.ch * kQBlk;
-        head = g * a.G + cu.hd;
-        partial = (ent & 3) == kTilePartial;
-    };
     BlockCursor ci, cc;            // next block to copy / to compute
     auto issue = [&](int n) __attribute__((always_inline)) {
-        const uint32_t st = lds0 + (n % LD::NSTAGE) * LD::STAGE;
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            int q0, head;
-            bool partial;
-            block_at(ci, 2 * n + b, q0, head, partial);
-            ci.next(a.G, CH);
-            const int n_valid = q0 == kNoQuery ? 0 : __builtin_amdgcn_readfirstlane(min(max(n_real - q0, 0), kQBlk));
-            const int q0c = q0 == kNoQuery ? 0 : q0;
-            const int64_t roff = ((int64_t(r) * T + q0c) * a.Hq + head) * D * 2;
-            const uint32_t bl = st + b * LD::BLK;
-            copy_tile<D>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, bl + LD::Q_OFF, kQBlk, wave, kKvWaves, lane);
-            copy_tile<D>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride, bl + LD::DO_OFF, kQBlk, wave, kKvWaves, lane);
-            if (wave == b && lane < kQBlk) {
-                const int64_t loff = (int64_t(r) * a.Hq + head) * T + q0c;
-                buf_to_lds4(buf_rsrc(a.lse2 + loff, uint32_t(n_valid) * 4), bl + LD::LSE_OFF, lane * 4);
-                buf_to_lds4(buf_rsrc(a.delta + loff, uint32_t(n_valid) * 4), bl + LD::DL_OFF, lane * 4);
-            }
+        const int ent = __builtin_amdgcn_readfirstlane(a.kp_list[l_begin + ci.e]);
+        const int q0 = (ent >> 4) * a.BQ + ci.ch * kQBlk;
+        const int head = g * a.G + ci.hd;
+        ci.next(a.G, CH);
+        const uint32_t bl = lds0 + (n % LD::NS) * LD::BLK;
+        const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - q0, 0), kQBlk));
+        const int64_t roff = ((int64_t(r) * T + q0) * a.Hq + head) * D * 2;
+        copy_tile<D>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, bl + LD::Q_OFF, kQBlk, wave, kKvWaves, lane);
+        copy_tile<D>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride, bl + LD::DO_OFF, kQBlk, wave, kKvWaves, lane);
+        if (wave < 2 && lane < kQBlk) {
+            const int64_t loff = (int64_t(r) * a.Hq + head) * T + q0;
+            const float *src = wave == 0 ? a.lse2 : a.delta;
+            buf_to_lds4(buf_rsrc(src + loff, uint32_t(n_valid) * 4), bl + (wave == 0 ? LD::LSE_OFF : LD::DL_OFF), lane * 4);
         }
     };
 
-    if (NU > 0) issue(0);
-    for (int n = 0; n < NU; ++n) {
-        wait_loads();
+#pragma unroll
+    for (int n = 0; n < LD::AHEAD; ++n)
+        if (n < NB) issue(n);
+    for (int n = 0; n < NB; ++n) {
+        // Block n has landed for this wave once only the newer blocks' copies (at most
+        // AHEAD - 1 of them) may be in flight; the barrier extends that to every wave and
+        // also means every wave is done with block n - 1, whose stage block n + AHEAD takes.
+        const int newer = min(LD::AHEAD - 1, NB - 1 - n);
+        if (wave < 2) {
+            if (newer >= 2) wait_loads_but<2 * (LD::PERW + 1)>();
+            else if (newer == 1) wait_loads_but<LD::PERW + 1>();
+            else wait_loads();
+        } else {
+            if (newer >= 2) wait_loads_but<2 * LD::PERW>();
+            else if (newer == 1) wait_loads_but<LD::PERW>();
+            else wait_loads();
+        }
         block_barrier();
-        if (n + 1 < NU) issue(n + 1);
-        int qa, qb, ha, hb;
-        bool pa, pb;
-        block_at(cc, 2 * n, qa, ha, pa);
+        if (n + LD::AHEAD < NB) issue(n + LD::AHEAD);
+        const int ent = __builtin_amdgcn_readfirstlane(a.kp_list[l_begin + cc.e]);
+        const int q0 = (ent >> 4) * a.BQ + cc.ch * kQBlk;
         cc.next(a.G, CH);
-        block_at(cc, 2 * n + 1, qb, hb, pb);
-        cc.next(a.G, CH);
-        const char *st = smem + (n % LD::NSTAGE) * LD::STAGE;
-        kv_stage<D>(st, lo, kf, vf, a.c, h, key, kend_k, qa, qb, pa, pb, dk, dv);
+        const int cls = (ent >> cls_shift) & 3;
+        if (cls != kTileSkip)
+            kv_block<D>(smem + (n % LD::NS) * LD::BLK, lo, kf, vf, a.c, h, key, kend_k, q0, cls == kTilePartial, dk, dv);
     }
 
     // dK = scale dS^T Q, dV = P^T dO: lane holds its key, 4 consecutive d per register group.
+    if (!kin) return;
     const int64_t off = ((int64_t(r) * T + key) * a.Hkv + g) * D;
     __bf16 *pk = reinterpret_cast<__bf16 *>(a.dk) + off;
     __bf16 *pv = reinterpret_cast<__bf16 *>(a.dv) + off;
@@ -640,7 +634,7 @@ hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, hipSt
         dq_kernel<D><<<n_items_q, kDqWaves * 64, smem, s>>>(a);
     }
     if (n_items_k > 0) {
-        const int smem = KvLds<D>::NSTAGE * KvLds<D>::STAGE;
+        const int smem = KvLds<D>::NS * KvLds<D>::BLK;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(dkdv_kernel<D>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return e;
@@ -663,20 +657,20 @@ hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b,
     a.qt_ptr = reinterpret_cast<const int32_t *>(ws + w.qt_ptr);
     a.kt_idx = reinterpret_cast<const int32_t *>(ws + w.kt_idx);
     a.kt_kind = reinterpret_cast<const uint8_t *>(ws + w.kt_kind);
-    a.kt_ptr = reinterpret_cast<const int32_t *>(bws + b.kt_ptr);
-    a.q_list = reinterpret_cast<const int32_t *>(bws + b.q_list);
+    a.kp_ptr = reinterpret_cast<const int32_t *>(bws + b.kp_ptr);
+    a.kp_list = reinterpret_cast<const int32_t *>(bws + b.kp_list);
     a.kwork = reinterpret_cast<const int32_t *>(bws + b.kwork);
     a.kend = reinterpret_cast<const int32_t *>(ws + w.kend);
     a.work = reinterpret_cast<const int32_t *>(ws + w.work);
     a.n_real = reinterpret_cast<const int32_t *>(ws + w.n_real);
     a.status = reinterpret_cast<const int32_t *>(ws + w.status);
     a.T = sh.T; a.Hq = sh.Hq; a.Hkv = sh.Hkv; a.G = sh.G; a.HCH = sh.HCH;
-    a.nQ = w.nQ; a.nK = w.nK; a.BQ = sh.BQ;
+    a.nQ = w.nQ; a.nK = w.nK; a.nP = b.nP; a.BQ = sh.BQ;
     a.L = sh.Hkv * (sh.G / sh.HCH);
     a.scale = sh.scale;
     a.c = sh.scale * kLog2e;
     const int64_t n_q = int64_t(sh.R) * w.nQ * a.L;
-    const int64_t n_k = int64_t(sh.R) * w.nK * sh.Hkv;
+    const int64_t n_k = int64_t(sh.R) * b.nP * sh.Hkv;
     if (n_q > INT32_MAX || n_k > INT32_MAX) return hipErrorInvalidValue;
     if (sh.dtype != TREE_DT_BF16) return hipErrorInvalidValue;
     if (sh.BQ % kQBlk != 0) return hipErrorInvalidValue;

@@ -164,15 +164,15 @@ extern "C" int tree_attn_bwd_plan(const tree_attn_desc *d, const void *ws, void 
     return e == hipSuccess ? TREE_OK : TREE_E_HIP;
 }
 
-extern "C" int tree_attn_bwd_tiles(const tree_attn_desc *d, const void *bws, const int32_t **kt_ptr,
-                                   const int32_t **q_list) {
+extern "C" int tree_attn_bwd_tiles(const tree_attn_desc *d, const void *bws, const int32_t **kp_ptr,
+                                   const int32_t **kp_list) {
     WsLayout w;
     BwdLayout b;
     const int rc = bwd_check(d, &w, &b);
     if (rc != TREE_OK) return rc;
-    if (bws == nullptr || kt_ptr == nullptr || q_list == nullptr) return TREE_E_INVAL;
-    *kt_ptr = reinterpret_cast<const int32_t *>(static_cast<const char *>(bws) + b.kt_ptr);
-    *q_list = reinterpret_cast<const int32_t *>(static_cast<const char *>(bws) + b.q_list);
+    if (bws == nullptr || kp_ptr == nullptr || kp_list == nullptr) return TREE_E_INVAL;
+    *kp_ptr = reinterpret_cast<const int32_t *>(static_cast<const char *>(bws) + b.kp_ptr);
+    *kp_list = reinterpret_cast<const int32_t *>(static_cast<const char *>(bws) + b.kp_list);
     return TREE_OK;
 }
 

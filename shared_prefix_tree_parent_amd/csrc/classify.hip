@@ -239,67 +239,77 @@ __global__ void fill_lists(int32_t nK, int32_t n_tiles, const uint8_t *__restric
     }
 }
 
-// ------------------------------------------------------------------ backward (k-tile) lists
+// ------------------------------------------------------------------ backward (k-tile pair) lists
 //
-// The backward's dK/dV pass walks, for every (row, k-tile), the q-tiles that see it: the
-// transpose of the per-q-tile lists, read from the same class map.
+// The backward's dK/dV pass walks, for every (row, pair of k-tiles 2p and 2p+1), the q-tiles
+// that see either of them, with both classes: the transpose of the per-q-tile lists, read from
+// the same class map.  A missing k-tile 2p+1 (odd tile count) counts as SKIP.
 
-// One wave per (row, k-tile): number of non-skip q-tiles, to kt_ptr[tile + 1].
-__global__ void count_cols(int32_t nQ, int32_t nK, int32_t n_ktiles, const uint8_t *__restrict__ cmap,
-                           int32_t *__restrict__ kt_ptr) {
-    const int32_t tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (tile >= n_ktiles) return;
+__device__ __forceinline__ void pair_classes(const uint8_t *cm, int32_t nK, int32_t qt, int32_t kt0, uint8_t &ca,
+                                             uint8_t &cb) {
+    ca = cm[int64_t(qt) * nK + kt0];
+    cb = kt0 + 1 < nK ? cm[int64_t(qt) * nK + kt0 + 1] : uint8_t(kTileSkip);
+}
+
+// One wave per (row, pair): number of q-tiles that see the pair, to kp_ptr[item + 1].
+__global__ void count_pairs(int32_t nQ, int32_t nK, int32_t nP, int32_t n_items, const uint8_t *__restrict__ cmap,
+                            int32_t *__restrict__ kp_ptr) {
+    const int32_t item = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (item >= n_items) return;
     const int lane = threadIdx.x & 63;
-    const int32_t r = tile / nK, kt = tile % nK;
-    const uint8_t *cm = cmap + int64_t(r) * nQ * nK + kt;
+    const int32_t r = item / nP, p = item % nP;
+    const uint8_t *cm = cmap + int64_t(r) * nQ * nK;
     int32_t cnt = 0;
     for (int32_t q0 = 0; q0 < nQ; q0 += 64) {
         const int32_t qt = q0 + lane;
-        const bool on = qt < nQ && cm[int64_t(qt) * nK] != kTileSkip;
-        cnt += __popcll(__ballot(on));
+        uint8_t ca = kTileSkip, cb = kTileSkip;
+        if (qt < nQ) pair_classes(cm, nK, qt, 2 * p, ca, cb);
+        cnt += __popcll(__ballot(ca != kTileSkip || cb != kTileSkip));
     }
-    if (lane == 0) kt_ptr[tile + 1] = cnt;
+    if (lane == 0) kp_ptr[item + 1] = cnt;
 }
 
-// One workgroup: scan of the k-tile counts and the longest-first k-tile work list.
-__global__ void finish_cols(int32_t nQ, int32_t n_ktiles, int32_t *__restrict__ kt_ptr,
-                            int32_t *__restrict__ khist, int32_t *__restrict__ kwork) {
+// One workgroup: scan of the pair counts and the longest-first work list.
+__global__ void finish_pairs(int32_t nQ, int32_t n_items, int32_t *__restrict__ kp_ptr,
+                             int32_t *__restrict__ khist, int32_t *__restrict__ kwork) {
     __shared__ int32_t part[1024 / 64];
     __shared__ int32_t carry;
-    if (threadIdx.x == 0) kt_ptr[0] = 0;
+    if (threadIdx.x == 0) kp_ptr[0] = 0;
     for (int32_t i = threadIdx.x; i < nQ + 2; i += blockDim.x) khist[i] = 0;
     __syncthreads();
-    block_scan(n_ktiles, kt_ptr, part, &carry);
+    block_scan(n_items, kp_ptr, part, &carry);
     __threadfence_block();
     __syncthreads();
-    for (int32_t t = threadIdx.x; t < n_ktiles; t += blockDim.x)
-        atomicAdd(&khist[1 + nQ - (kt_ptr[t + 1] - kt_ptr[t])], 1);
+    for (int32_t t = threadIdx.x; t < n_items; t += blockDim.x)
+        atomicAdd(&khist[1 + nQ - (kp_ptr[t + 1] - kp_ptr[t])], 1);
     __threadfence_block();
     __syncthreads();
     block_scan(nQ + 1, khist, part, &carry);
     __threadfence_block();
     __syncthreads();
-    for (int32_t t = threadIdx.x; t < n_ktiles; t += blockDim.x) {
-        const int32_t c = kt_ptr[t + 1] - kt_ptr[t];
+    for (int32_t t = threadIdx.x; t < n_items; t += blockDim.x) {
+        const int32_t c = kp_ptr[t + 1] - kp_ptr[t];
         kwork[atomicAdd(&khist[nQ - c], 1)] = t;
     }
 }
 
-// One wave per (row, k-tile): the non-skip q-tiles in ascending order, as q-tile * 4 + class.
-__global__ void fill_cols(int32_t nQ, int32_t nK, int32_t n_ktiles, const uint8_t *__restrict__ cmap,
-                          const int32_t *__restrict__ kt_ptr, int32_t *__restrict__ q_list) {
-    const int32_t tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (tile >= n_ktiles) return;
+// One wave per (row, pair): the q-tiles in ascending order, as q-tile*16 + class_a*4 + class_b.
+__global__ void fill_pairs(int32_t nQ, int32_t nK, int32_t nP, int32_t n_items, const uint8_t *__restrict__ cmap,
+                           const int32_t *__restrict__ kp_ptr, int32_t *__restrict__ kp_list) {
+    const int32_t item = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (item >= n_items) return;
     const int lane = threadIdx.x & 63;
-    const int32_t r = tile / nK, kt = tile % nK;
-    const uint8_t *cm = cmap + int64_t(r) * nQ * nK + kt;
-    int32_t pos = kt_ptr[tile];
+    const int32_t r = item / nP, p = item % nP;
+    const uint8_t *cm = cmap + int64_t(r) * nQ * nK;
+    int32_t pos = kp_ptr[item];
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int32_t q0 = 0; q0 < nQ; q0 += 64) {
         const int32_t qt = q0 + lane;
-        const uint8_t cls = qt < nQ ? cm[int64_t(qt) * nK] : kTileSkip;
-        const uint64_t m = __ballot(cls != kTileSkip);
-        if (cls != kTileSkip) q_list[pos + __popcll(m & below)] = qt * 4 + cls;
+        uint8_t ca = kTileSkip, cb = kTileSkip;
+        if (qt < nQ) pair_classes(cm, nK, qt, 2 * p, ca, cb);
+        const bool on = ca != kTileSkip || cb != kTileSkip;
+        const uint64_t m = __ballot(on);
+        if (on) kp_list[pos + __popcll(m & below)] = qt * 16 + ca * 4 + cb;
         pos += __popcll(m);
     }
 }
@@ -308,16 +318,16 @@ __global__ void fill_cols(int32_t nQ, int32_t nK, int32_t n_ktiles, const uint8_
 
 hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, const char *ws, char *bws, hipStream_t s) {
     const uint8_t *cmap = reinterpret_cast<const uint8_t *>(ws + w.cmap);
-    int32_t *kt_ptr = reinterpret_cast<int32_t *>(bws + b.kt_ptr);
-    int32_t *q_list = reinterpret_cast<int32_t *>(bws + b.q_list);
+    int32_t *kp_ptr = reinterpret_cast<int32_t *>(bws + b.kp_ptr);
+    int32_t *kp_list = reinterpret_cast<int32_t *>(bws + b.kp_list);
     int32_t *kwork = reinterpret_cast<int32_t *>(bws + b.kwork);
     int32_t *khist = reinterpret_cast<int32_t *>(bws + b.khist);
-    const int32_t n_ktiles = w.R * w.nK;
-    if (n_ktiles > 0)
-        count_cols<<<(n_ktiles + 3) / 4, 256, 0, s>>>(w.nQ, w.nK, n_ktiles, cmap, kt_ptr);
-    finish_cols<<<1, 1024, 0, s>>>(w.nQ, n_ktiles, kt_ptr, khist, kwork);
-    if (n_ktiles > 0)
-        fill_cols<<<(n_ktiles + 3) / 4, 256, 0, s>>>(w.nQ, w.nK, n_ktiles, cmap, kt_ptr, q_list);
+    const int32_t n_items = w.R * b.nP;
+    if (n_items > 0)
+        count_pairs<<<(n_items + 3) / 4, 256, 0, s>>>(w.nQ, w.nK, b.nP, n_items, cmap, kp_ptr);
+    finish_pairs<<<1, 1024, 0, s>>>(w.nQ, n_items, kp_ptr, khist, kwork);
+    if (n_items > 0)
+        fill_pairs<<<(n_items + 3) / 4, 256, 0, s>>>(w.nQ, w.nK, b.nP, n_items, cmap, kp_ptr, kp_list);
     return hipGetLastError();
 }
 

@@ -59,25 +59,28 @@ inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_
 }
 
 // Backward workspace layout (caller-allocated, filled by tree_attn_bwd_plan / tree_attn_bwd).
+// The dK/dV pass works on pairs of k-tiles (k-tiles 2p and 2p+1, 128 keys).
 struct BwdLayout {
     size_t delta = 0;     // float[R*Hq*T]: rowsum(dO * O) per (row, head, token); 0 at pads
     size_t lse2 = 0;      // float[R*Hq*T]: the forward's LSE times log2(e)
-    size_t kt_ptr = 0;    // int32[R*nK + 1]: CSR over (row, k-tile) of the q-tiles that see it
-    size_t q_list = 0;    // int32[R*nQ*nK]: q-tile * 4 + class, ascending q-tile per k-tile
-    size_t kwork = 0;     // int32[R*nK]: (row, k-tile) items, longest list first
+    size_t kp_ptr = 0;    // int32[R*nP + 1]: CSR over (row, k-tile pair) of the q-tiles that see it
+    size_t kp_list = 0;   // int32[R*nQ*nP]: q-tile*16 + class(2p)*4 + class(2p+1), ascending q-tile
+    size_t kwork = 0;     // int32[R*nP]: (row, pair) items, longest list first
     size_t khist = 0;     // int32[nQ + 2]
     size_t total = 0;
+    int32_t nP = 0;       // k-tile pairs per row: ceil(nK / 2)
 };
 
 inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq) {
     BwdLayout b;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    b.nP = (w.nK + 1) / 2;
     b.delta = take(size_t(w.R) * Hq * w.T * sizeof(float));
     b.lse2 = take(size_t(w.R) * Hq * w.T * sizeof(float));
-    b.kt_ptr = take((size_t(w.R) * w.nK + 1) * sizeof(int32_t));
-    b.q_list = take(size_t(w.R) * w.nQ * w.nK * sizeof(int32_t));
-    b.kwork = take(size_t(w.R) * w.nK * sizeof(int32_t));
+    b.kp_ptr = take((size_t(w.R) * b.nP + 1) * sizeof(int32_t));
+    b.kp_list = take(size_t(w.R) * w.nQ * b.nP * sizeof(int32_t));
+    b.kwork = take(size_t(w.R) * b.nP * sizeof(int32_t));
     b.khist = take((size_t(w.nQ) + 2) * sizeof(int32_t));
     b.total = off;
     return b;

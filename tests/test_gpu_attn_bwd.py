@@ -6,7 +6,8 @@ the launch configuration the benchmark times, dQ at sampled queries and dK / dV 
 keys the oracle computes one by one, plus two identities that hold at any size and cover
 every key of the row: sum_j dV_j = sum_i dO_i over a row's real queries (each softmax row
 sums to one) and sum_j dK_j = 0 (each row of dS sums to zero), per KV head.  The backward's
-transposed tile lists are compared bit for bit with lists built from the oracle's classes.
+per-pair q-tile lists (the transposed tile lists) are compared bit for bit with lists built
+from the oracle's classes.
 Tolerances: tests/gpu_util.py (check_grad); pads exactly zero.
 """
 import numpy as np
@@ -107,6 +108,14 @@ def test_bwd_one_segment_and_singletons():
     inp.seg_parent, inp.seg_pos0 = np.full(n, -1, np.int32), np.zeros(n, np.int32)
     inp.real_len = np.array([n])
     _full_check(inp, "singleton roots")
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,D", [(576, 8, 2, 128), (320, 4, 1, 64)])
+def test_bwd_odd_ktile_count(T, Hq, Hkv, D):
+    """Rows of an odd number of 64-key tiles: the last k-tile pair has one tile."""
+    rng = np.random.default_rng(T + D)
+    inp = _random_inputs(rng, R=2, T=T, Hq=Hq, Hkv=Hkv, D=D)
+    _full_check(inp, f"odd k-tiles T{T} {Hq}/{Hkv} D{D}")
 
 
 def test_bwd_empty_middle_row():
@@ -245,22 +254,28 @@ def test_bwd_full_size_configs_sampled(cfg):
 
 # ------------------------------------------------------------------ lists, pads, determinism
 
-def _want_cols(inp, BQ, BK):
+def _want_pairs(inp, BQ, BK):
+    """Per (row, pair of k-tiles 2p, 2p+1): ascending q-tiles that see either, as
+    q-tile*16 + class(2p)*4 + class(2p+1) (a missing k-tile 2p+1 is SKIP), from the oracle's
+    class map."""
     cmap = M.tile_plan(inp, BQ, BK)["class_map"]                  # [R, nQ, nK]
     R, nQ, nK = cmap.shape
     ptr, lst = [0], []
     for r in range(R):
-        for kt in range(nK):
-            qts = np.flatnonzero(cmap[r, :, kt] != M.SKIP)
-            lst += [int(q) * 4 + int(cmap[r, q, kt]) for q in qts]
+        for p in range(0, nK, 2):
+            for qt in range(nQ):
+                ca = int(cmap[r, qt, p])
+                cb = int(cmap[r, qt, p + 1]) if p + 1 < nK else M.SKIP
+                if ca != M.SKIP or cb != M.SKIP:
+                    lst.append(qt * 16 + ca * 4 + cb)
             ptr.append(len(lst))
     return np.asarray(ptr, np.int32), np.asarray(lst, np.int32)
 
 
-def _fetch_cols(plan, n_ktiles):
+def _fetch_pairs(plan, n_items):
     import torch
     bws = plan.bwd_plan()
-    kp, ql = ta.tree_attn_bwd_tiles(plan.desc, bws)
+    kp, kl = ta.tree_attn_bwd_tiles(plan.desc, bws)
     torch.cuda.synchronize()
     base = bws.data_ptr()
 
@@ -269,22 +284,24 @@ def _fetch_cols(plan, n_ktiles):
         assert 0 <= off and off + 4 * count <= bws.numel()
         return bws[off:off + 4 * count].cpu().numpy().view(np.int32).copy()
 
-    ptr = grab(kp, n_ktiles + 1)
-    return ptr, grab(ql, int(ptr[-1]))
+    ptr = grab(kp, n_items + 1)
+    return ptr, grab(kl, int(ptr[-1]))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 5, "random"])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5, "random", "odd"])
 def test_bwd_tile_lists_match_oracle(cfg):
     if cfg == "random":
         inp = _random_inputs(np.random.default_rng(21), 3, 1024, 8, 4, 128)
+    elif cfg == "odd":
+        inp = _random_inputs(np.random.default_rng(22), 2, 576, 8, 2, 128)
     else:
         inp = make_config(cfg, with_qkv=False)
     if inp.dtype != "bf16":
         inp.dtype = "bf16"                                # the lists do not depend on the dtype
     plan = ta.attn_plan(inp)
     BQ, BK = ta.tree_attn_blocks(plan.desc)
-    want_ptr, want_list = _want_cols(inp, BQ, BK)
-    got_ptr, got_list = _fetch_cols(plan, inp.n_rows * (inp.row_len // BK))
+    want_ptr, want_list = _want_pairs(inp, BQ, BK)
+    got_ptr, got_list = _fetch_pairs(plan, inp.n_rows * ((inp.row_len // BK + 1) // 2))
     assert np.array_equal(got_ptr, want_ptr)
     assert np.array_equal(got_list, want_list)
 
