@@ -13,7 +13,8 @@ stream it runs on) and the CPU oracle timed on a bounded sample of the same work
 Beside it, the backward (tree_attn_bwd: dQ, dK, dV for a seeded upstream gradient, bf16
 workloads) is timed on the same inputs and reported as `bwd`, with its FLOPs counted the
 FlashAttention way: 2.5 x the forward's useful FLOPs (S recomputed once, dP, dV, dK and dQ,
-each 2 * head_dim per visible pair and query head).
+each 2 * head_dim per visible pair and query head).  `packing` holds the host packing
+comparisons on the global-tree batch and the planner's cost as that batch grows.
 """
 from __future__ import annotations
 
@@ -131,6 +132,40 @@ def host_plan_ms(cfg: int, reps: int = 5) -> float | None:
     return float(np.median(times))
 
 
+def packing_report(reps: int = 3) -> dict:
+    """Host packing comparisons on the global-tree batch (config 4: 384 sequences, 48 RL
+    groups, 3 task families, 4096-token rows) with the library's planner: rows under the
+    global tree vs one tree per group ([PTP] scope passage), best-fit-decreasing vs the
+    in-order filler ([PTP] historical section), and no sharing at all; then planner cost as
+    the same recipe grows to 12 / 48 / 192 / 768 groups ([PTP] planning-cost table)."""
+    import shared_prefix_tree_parent_amd as ta
+    from workloads import config4_sequences
+    batch, _ = config4_sequences(4)
+    rows, real = {}, {}
+    for scope, sc in (("global", ta.TREE_SCOPE_GLOBAL), ("per_group", ta.TREE_SCOPE_PER_GROUP)):
+        for place, pc in (("bfd", ta.TREE_PLACE_BFD), ("in_order", ta.TREE_PLACE_IN_ORDER)):
+            plan = ta.pack_batch(batch, 4096, 64, placement=pc, tree_scope=sc)
+            rows[f"{scope}_{place}"] = plan["n_rows"]
+            real[f"{scope}_{place}"] = plan["real_tokens"]
+    none = ta.pack_batch(batch, 4096, 64, use_groups=False, tree_scope=ta.TREE_SCOPE_PER_GROUP)
+    rows["no_sharing"], real["no_sharing"] = none["n_rows"], none["real_tokens"]
+    scaling = []
+    for n_groups in (12, 48, 192, 768):
+        b, _ = config4_sequences(4, n_groups=n_groups)
+        best = None
+        for _ in range(reps):
+            plan = ta.pack_batch(b, 4096, 64)
+            t = (plan["tree_walk_ns"] / 1e6, plan["bin_pack_ns"] / 1e6)
+            best = t if best is None or sum(t) < sum(best) else best
+        scaling.append({"groups": n_groups, "sequences": b.n, "tokens": int(b.offsets[-1]),
+                        "tree_walk_ms": round(best[0], 3), "bin_pack_ms": round(best[1], 3),
+                        "rows": plan["n_rows"]})
+    return {"workload": "config 4: 384 sequences, 48 groups, 4096-token rows", "rows": rows,
+            "real_tokens": real, "unpacked_tokens": int(batch.offsets[-1]),
+            "scaling": scaling, "scaling_recipe": "config 4 recipe with 12/48/192/768 groups of 8, "
+            "global tree + best-fit-decreasing, best of 3, one host thread"}
+
+
 def cpu_baseline(inp, pairs_total: int, budget_s: float = 15.0) -> dict:
     """The float64 oracle, as it stands, on a bounded sample of query positions of the same
     workload (all heads); scaled to TFLOP/s by the sample's useful FLOPs."""
@@ -175,6 +210,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-packing", action="store_true", help="skip the host packing comparisons")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -307,6 +343,7 @@ def main() -> int:
         "roofline": roofline,
         "clock_adjusted": None,
         "bwd": bwd,
+        "packing": None,
         "cpu_baseline": None,
     }
     clk = recorded_clock_ghz(args.config, args.uniform_lengths)
@@ -321,6 +358,8 @@ def main() -> int:
         out["host_plan_ms"] = round(host_plan_ms(args.config), 3)
     except Exception as e:  # host planning is reported, not required for the device step
         out["host_plan_ms"] = f"error: {e}"
+    if not args.no_packing:
+        out["packing"] = packing_report()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, pairs, args.cpu_budget)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 5)

@@ -48,6 +48,7 @@ enum {
 
 enum { TREE_DT_BF16 = 1, TREE_DT_F32 = 2 };
 enum { TREE_PLACE_BFD = 0, TREE_PLACE_IN_ORDER = 1 };
+enum { TREE_SCOPE_GLOBAL = 0, TREE_SCOPE_PER_GROUP = 1 };
 
 /* ------------------------------------------------------------------------------------ *
  * 1. Host planning
@@ -61,6 +62,11 @@ typedef struct {
     int32_t placement;     /* TREE_PLACE_BFD ([PTP] placement listing) or TREE_PLACE_IN_ORDER
                               ([PTP] historical section: fill the current row, move on for good
                               when the next leaf does not fit) */
+    int32_t tree_scope;    /* TREE_SCOPE_GLOBAL ([PTP] scope passage: one tree over every
+                              sequence, no group boundary) or TREE_SCOPE_PER_GROUP (the
+                              comparison that passage draws: one tree per group of group_ids,
+                              groups in order of first appearance; nothing is shared across
+                              groups).  Packing is the same either way. */
 } tree_pack_params;
 
 typedef struct tree_plan tree_plan;   /* opaque, host memory, owned by the library */

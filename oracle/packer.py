@@ -8,7 +8,8 @@ Follows [PTP] ("Prefix tree packing", furtherai.github.io):
   * the two refinements after it: a configurable minimum shared-segment length
     (64 by default) and no sharing of trainable tokens;
   * the off-by-one note: each branch keeps its own copy of the non-trainable join token;
-  * the scope passage: one global tree over every queued sequence, no group boundary;
+  * the scope passage: one global tree over every queued sequence, no group boundary (and,
+    for the comparison that passage draws, one tree per group);
   * the bin-packing passage and its placement listing: a leaf's cost in a bin is the
     total length of its path segments that bin does not hold yet; best fit with a
     strict "<" over the bins in creation order; groups placed by their most expensive
@@ -30,6 +31,8 @@ notes of the repository):
   R13 singleton parts (a member whose next token is not shareable) follow the shareable
      parts, in input order; shareable parts are ordered by token value.
   R14 position id = the token's index in its own unpacked sequence.
+  R21 per-group trees: the same build over each group's sequences separately, groups in
+     order of first appearance; segment ids run tree by tree.
 """
 from __future__ import annotations
 
@@ -73,11 +76,13 @@ def shareable(x, tau, t) -> bool:
     return True
 
 
-def build_tree(seqs, trainable, min_shared: int) -> Tree:
+def build_tree(seqs, trainable, min_shared: int, scopes=None) -> Tree:
     """Radix segment build of [PTP]'s tree-building passage with the minimum-length and
     trainable-token refinements (readings R1, R2, R13).
 
-    ``seqs`` / ``trainable``: lists of 1-D int arrays, one per sequence.
+    ``seqs`` / ``trainable``: lists of 1-D int arrays, one per sequence.  ``scopes``: lists
+    of sequence indices that each get a tree of their own, built in list order (reading
+    R21); default one tree over every sequence ([PTP] scope passage).
     """
     if min_shared < 1:
         raise ValueError("min_shared must be >= 1")
@@ -121,7 +126,8 @@ def build_tree(seqs, trainable, min_shared: int) -> Tree:
     old = sys.getrecursionlimit()
     sys.setrecursionlimit(max(old, 10 * n + 1000))
     try:
-        build(list(range(n)), 0, -1)
+        for members in ([list(range(n))] if scopes is None else scopes):
+            build(list(members), 0, -1)
     finally:
         sys.setrecursionlimit(old)
 
@@ -203,8 +209,16 @@ def in_order_fill(paths, capacity: int) -> list:
     return bins
 
 
+def group_members(groups) -> list:
+    """Members of each group (input order), groups in order of first appearance."""
+    members: dict = {}
+    for s, g in enumerate(groups):
+        members.setdefault(g, []).append(s)
+    return list(members.values())
+
+
 def pack_plan(seqs, trainable=None, groups=None, row_len: int = 4096, min_shared: int = 64,
-              pad_multiple: int = 0, placement: str = "bfd") -> dict:
+              pad_multiple: int = 0, placement: str = "bfd", tree_scope: str = "global") -> dict:
     """The whole integer plan: tree, rows, per-row segment tables and per-token maps.
 
     Row layout (reading R5): row r is the r-th bin in creation order; its segments are the
@@ -222,7 +236,13 @@ def pack_plan(seqs, trainable=None, groups=None, row_len: int = 4096, min_shared
     for s in range(n):
         if len(seqs[s]) == 0:
             raise ValueError(f"sequence {s} is empty")
-    tree = build_tree(seqs, [np.asarray(t) for t in trainable], min_shared)
+    if tree_scope == "global":
+        scopes = None
+    elif tree_scope == "per_group":
+        scopes = group_members([int(g) for g in groups])
+    else:
+        raise ValueError(tree_scope)
+    tree = build_tree(seqs, [np.asarray(t) for t in trainable], min_shared, scopes)
     if placement == "bfd":
         bins = best_fit_decreasing(tree.paths, [int(g) for g in groups], row_len)
     elif placement == "in_order":
@@ -284,9 +304,9 @@ def pack_plan(seqs, trainable=None, groups=None, row_len: int = 4096, min_shared
 
 
 def pack_batch(batch, row_len: int = 4096, min_shared: int = 64, pad_multiple: int = 0,
-               use_groups: bool = True, placement: str = "bfd") -> dict:
+               use_groups: bool = True, placement: str = "bfd", tree_scope: str = "global") -> dict:
     """``pack_plan`` on a ``workloads.SeqBatch``."""
     seqs = [batch.seq(s) for s in range(batch.n)]
     tr = [batch.train(s) for s in range(batch.n)]
     groups = [int(g) for g in batch.groups] if use_groups else None
-    return pack_plan(seqs, tr, groups, row_len, min_shared, pad_multiple, placement)
+    return pack_plan(seqs, tr, groups, row_len, min_shared, pad_multiple, placement, tree_scope)

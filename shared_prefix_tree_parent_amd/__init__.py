@@ -33,6 +33,7 @@ TREE_OK, TREE_E_INVAL, TREE_E_TOOLONG, TREE_E_LAYOUT, TREE_E_NOMEM, TREE_E_HIP, 
     0, -1, -2, -3, -4, -5, -6
 TREE_DT_BF16, TREE_DT_F32 = 1, 2
 TREE_PLACE_BFD, TREE_PLACE_IN_ORDER = 0, 1
+TREE_SCOPE_GLOBAL, TREE_SCOPE_PER_GROUP = 0, 1
 
 EXPORTS = ("tree_pack_plan", "tree_plan_get", "tree_plan_free", "tree_attn_blocks",
            "tree_attn_workspace_size", "tree_attn_plan", "tree_attn_plan_status", "tree_attn_tiles",
@@ -50,7 +51,8 @@ class TreeError(RuntimeError):
 
 class PackParams(ctypes.Structure):
     _fields_ = [("row_len", ctypes.c_int32), ("min_shared", ctypes.c_int32),
-                ("pad_multiple", ctypes.c_int32), ("placement", ctypes.c_int32)]
+                ("pad_multiple", ctypes.c_int32), ("placement", ctypes.c_int32),
+                ("tree_scope", ctypes.c_int32)]
 
 
 class PlanView(ctypes.Structure):
@@ -143,14 +145,14 @@ _PLAN_ARRAYS = {
 
 
 def tree_pack_plan(tokens, seq_offsets, trainable=None, group_ids=None, row_len=4096, min_shared=64,
-                   pad_multiple=0, placement=TREE_PLACE_BFD) -> dict:
+                   pad_multiple=0, placement=TREE_PLACE_BFD, tree_scope=TREE_SCOPE_GLOBAL) -> dict:
     """Run the host planner; returns the plan's scalars and copies of its arrays."""
     tok = np.ascontiguousarray(tokens, dtype=np.int32)
     off = np.ascontiguousarray(seq_offsets, dtype=np.int64)
     tr = None if trainable is None else np.ascontiguousarray(trainable, dtype=np.uint8)
     gr = None if group_ids is None else np.ascontiguousarray(group_ids, dtype=np.int32)
     n = len(off) - 1
-    p = PackParams(row_len, min_shared, pad_multiple, placement)
+    p = PackParams(row_len, min_shared, pad_multiple, placement, tree_scope)
     h = ctypes.c_void_p()
     _check(lib().tree_pack_plan(_ptr(tok), _ptr(off), n, _ptr(tr), _ptr(gr), ctypes.byref(p),
                                 ctypes.byref(h)), "tree_pack_plan")
@@ -172,10 +174,11 @@ def tree_pack_plan(tokens, seq_offsets, trainable=None, group_ids=None, row_len=
 
 
 def pack_batch(batch, row_len=4096, min_shared=64, pad_multiple=0, use_groups=True,
-               placement=TREE_PLACE_BFD) -> dict:
+               placement=TREE_PLACE_BFD, tree_scope=TREE_SCOPE_GLOBAL) -> dict:
     """``tree_pack_plan`` on a ``workloads.SeqBatch``-like object (tokens/offsets/trainable/groups)."""
     return tree_pack_plan(batch.tokens, batch.offsets, batch.trainable,
-                          batch.groups if use_groups else None, row_len, min_shared, pad_multiple, placement)
+                          batch.groups if use_groups else None, row_len, min_shared, pad_multiple, placement,
+                          tree_scope)
 
 
 # ------------------------------------------------------------------------------ device attention

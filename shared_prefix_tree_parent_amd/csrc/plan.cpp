@@ -10,7 +10,8 @@
 //   * bin-packing passage and placement listing: a leaf's cost in a row is the length of
 //     its path segments the row does not hold yet; best fit (strict <, rows in creation
 //     order); groups placed by their most expensive leaf, descending;
-//   * historical section: the older in-order filler (optional placement).
+//   * historical section: the older in-order filler (optional placement);
+//   * the per-group trees the scope passage compares against (optional tree scope).
 // Readings of open points (same as the design notes): a short common run is pushed down
 // into the parts it splits into and rebuilt from the same start; singleton parts (next
 // token not shareable) follow the token-keyed parts in input order; a sequence longer than
@@ -74,14 +75,17 @@ struct Work {
     int32_t parent;
 };
 
-void build_tree(const Input &in, int32_t min_shared, Tree &tree) {
+// `scopes`: the member lists of the independent trees (one list for the global tree), built
+// one after the other, so segment ids are pre-order within each tree and trees follow in
+// list order.
+void build_tree(const Input &in, int32_t min_shared, const std::vector<std::vector<int32_t>> &scopes,
+                Tree &tree) {
     tree.segs.clear();
     tree.leaf_of.assign(in.n, -1);
     std::vector<Work> stack;
-    {
+    for (size_t i = scopes.size(); i-- > 0;) {
         Work w;
-        w.members.resize(in.n);
-        for (int32_t s = 0; s < in.n; ++s) w.members[s] = s;
+        w.members = scopes[i];
         w.start = 0;
         w.parent = -1;
         stack.push_back(std::move(w));
@@ -189,7 +193,8 @@ extern "C" int tree_pack_plan(const int32_t *tokens, const int64_t *seq_offsets,
     if (out == nullptr) return TREE_E_INVAL;
     *out = nullptr;
     if (p == nullptr || n_seqs < 0 || p->row_len <= 0 || p->min_shared < 1 || p->pad_multiple < 0 ||
-        (p->placement != TREE_PLACE_BFD && p->placement != TREE_PLACE_IN_ORDER))
+        (p->placement != TREE_PLACE_BFD && p->placement != TREE_PLACE_IN_ORDER) ||
+        (p->tree_scope != TREE_SCOPE_GLOBAL && p->tree_scope != TREE_SCOPE_PER_GROUP))
         return TREE_E_INVAL;
     if (n_seqs > 0 && (seq_offsets == nullptr || tokens == nullptr)) return TREE_E_INVAL;
     if (n_seqs > 0 && seq_offsets[0] != 0) return TREE_E_INVAL;
@@ -206,9 +211,38 @@ extern "C" int tree_pack_plan(const int32_t *tokens, const int64_t *seq_offsets,
         Input in{tokens, seq_offsets, trainable, n_seqs};
         plan->n_seqs = n_seqs;
 
+        // Groups: the caller's ids (else one per sequence), in order of first appearance,
+        // members in input order.  They order the placement, and with the per-group scope
+        // each is its own tree.
+        std::vector<int32_t> gid(n_seqs);
+        for (int32_t s = 0; s < n_seqs; ++s) gid[s] = group_ids ? group_ids[s] : s;
+        std::vector<std::vector<int32_t>> members;
+        {
+            std::vector<std::pair<int32_t, int32_t>> idx;   // (group key, slot), sorted by key
+            for (int32_t s = 0; s < n_seqs; ++s) {
+                auto it = std::lower_bound(idx.begin(), idx.end(), std::make_pair(gid[s], INT32_MIN));
+                if (it == idx.end() || it->first != gid[s]) {
+                    const int32_t slot = static_cast<int32_t>(members.size());
+                    idx.insert(it, {gid[s], slot});
+                    members.emplace_back();
+                    members[slot].push_back(s);
+                } else {
+                    members[it->second].push_back(s);
+                }
+            }
+        }
+
         const auto t0 = clk::now();
         Tree tree;
-        build_tree(in, p->min_shared, tree);
+        if (p->tree_scope == TREE_SCOPE_PER_GROUP) {
+            build_tree(in, p->min_shared, members, tree);
+        } else {
+            std::vector<std::vector<int32_t>> all(1);
+            all[0].resize(n_seqs);
+            for (int32_t s = 0; s < n_seqs; ++s) all[0][s] = s;
+            if (n_seqs == 0) all.clear();
+            build_tree(in, p->min_shared, all, tree);
+        }
         const int32_t n_segs_total = static_cast<int32_t>(tree.segs.size());
         std::vector<Path> paths(n_seqs);
         std::vector<int64_t> cost(n_seqs, 0);
@@ -226,25 +260,6 @@ extern "C" int tree_pack_plan(const int32_t *tokens, const int64_t *seq_offsets,
         std::vector<int32_t> order;
         order.reserve(n_seqs);
         if (p->placement == TREE_PLACE_BFD) {
-            std::vector<int32_t> gid(n_seqs);
-            for (int32_t s = 0; s < n_seqs; ++s) gid[s] = group_ids ? group_ids[s] : s;
-            std::vector<int32_t> first_seen;         // group keys in first-appearance order
-            std::vector<std::vector<int32_t>> members;
-            {
-                std::vector<std::pair<int32_t, int32_t>> idx;   // (group key, slot)
-                for (int32_t s = 0; s < n_seqs; ++s) {
-                    auto it = std::lower_bound(idx.begin(), idx.end(), std::make_pair(gid[s], INT32_MIN));
-                    if (it == idx.end() || it->first != gid[s]) {
-                        const int32_t slot = static_cast<int32_t>(members.size());
-                        idx.insert(it, {gid[s], slot});
-                        members.emplace_back();
-                        first_seen.push_back(gid[s]);
-                        members[slot].push_back(s);
-                    } else {
-                        members[it->second].push_back(s);
-                    }
-                }
-            }
             std::vector<int64_t> gmax(members.size(), 0);
             std::vector<int32_t> slots(members.size());
             for (size_t g = 0; g < members.size(); ++g) {

@@ -311,3 +311,73 @@ def test_pad_multiple_row_len():
     plan = P.pack_plan([np.arange(100), np.arange(50) + 1000], None, None, row_len=4096,
                        min_shared=64, pad_multiple=128)
     assert plan["n_rows"] == 1 and plan["row_len"] == 256
+
+
+# ---------------------------------------------------------------- per-group trees (reading R21)
+
+def _segments_as_sets(tree):
+    return sorted((tuple(sorted(sg.members)), sg.start, sg.end) for sg in tree.segments)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(0, 10 ** 9), st.integers(1, 20), st.sampled_from([1, 4, 64]))
+def test_per_group_one_group_is_global(seed, n, min_shared):
+    """All sequences in one group: the per-group forest is the global tree, id for id."""
+    rng = np.random.default_rng(seed)
+    b = random_sequences(rng, n, alphabet=2, max_len=80, p_trainable=0.3)
+    seqs = [b.seq(s) for s in range(b.n)]
+    tr = [b.train(s) for s in range(b.n)]
+    cap = max(len(s) for s in seqs) + 20
+    a = P.pack_plan(seqs, tr, [7] * n, cap, min_shared, tree_scope="global")
+    g = P.pack_plan(seqs, tr, [7] * n, cap, min_shared, tree_scope="per_group")
+    for k in ("seg_row_ptr", "seg_start", "seg_len", "seg_parent", "seg_global_id", "pos_ids", "gather_seq",
+              "gather_pos", "seq_row"):
+        assert np.array_equal(a[k], g[k]), k
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(0, 10 ** 9), st.integers(1, 20))
+def test_per_group_singletons_share_nothing(seed, n):
+    """Every sequence its own group: each path is one segment of the whole sequence, and the
+    rows hold exactly the unpacked tokens."""
+    rng = np.random.default_rng(seed)
+    b = random_sequences(rng, n, alphabet=2, max_len=80, p_trainable=0.3)
+    seqs = [b.seq(s) for s in range(b.n)]
+    tr = [b.train(s) for s in range(b.n)]
+    cap = max(len(s) for s in seqs) + 20
+    p = P.pack_plan(seqs, tr, list(range(n)), cap, 1, tree_scope="per_group")
+    assert [len(path) for path in p["tree"].paths] == [1] * n
+    assert [sg.length for sg in p["tree"].segments] == [len(s) for s in seqs]
+    assert p["real_tokens"] == p["unpacked_tokens"]
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(0, 10 ** 9), st.integers(2, 16), st.integers(2, 4))
+def test_per_group_disjoint_groups_same_segments(seed, n, n_groups):
+    """Groups whose sequences start with different tokens share nothing in the global tree
+    either, so both scopes give the same segments (ids may differ)."""
+    rng = np.random.default_rng(seed)
+    b = random_sequences(rng, n, alphabet=2, max_len=80, p_trainable=0.3)
+    seqs, groups = [], []
+    for s in range(b.n):
+        g = s % n_groups
+        seqs.append(np.concatenate([[100 + g], b.seq(s)]))     # group-private first token
+        groups.append(g)
+    tr = [np.concatenate([[0], b.train(s)]) for s in range(b.n)]
+    a = P.build_tree(seqs, tr, 1)
+    g = P.build_tree(seqs, tr, 1, P.group_members(groups))
+    assert _segments_as_sets(a) == _segments_as_sets(g)
+
+
+def test_per_group_forest_order():
+    """Per-group segment ids: each group's tree in pre-order, groups in order of first
+    appearance (reading R21)."""
+    x = np.arange(70)
+    seqs = [np.concatenate([x, [1, 2]]), np.concatenate([x, [3]]), np.concatenate([x, [1, 5]]),
+            np.concatenate([x, [4]])]
+    tr = [np.zeros(len(s), np.uint8) for s in seqs]
+    t = P.build_tree(seqs, tr, 64, P.group_members([5, 9, 5, 9]))
+    # group 5 = sequences 0, 2: shared 70-token run + two leaves; then group 9 = 1, 3.
+    assert [(sg.members, sg.start, sg.end, sg.parent) for sg in t.segments] == [
+        ([0, 2], 0, 71, -1), ([0], 71, 72, 0), ([2], 71, 72, 0),
+        ([1, 3], 0, 70, -1), ([1], 70, 71, 3), ([3], 70, 71, 3)]

@@ -53,19 +53,22 @@ def _compare(got, want):
     assert np.array_equal(got["row_used"], want["used"])
 
 
-@settings(max_examples=250, deadline=None)
+@settings(max_examples=300, deadline=None)
 @given(st.integers(0, 10 ** 9), st.integers(1, 30), st.sampled_from([1, 2, 4, 64]), st.integers(2, 4),
-       st.booleans(), st.sampled_from([0, 16]), st.sampled_from(["bfd", "in_order"]))
-def test_planner_bit_exact_fuzz(L, seed, n, min_shared, alpha, groups, pad, placement):
+       st.booleans(), st.sampled_from([0, 16]), st.sampled_from(["bfd", "in_order"]),
+       st.sampled_from(["global", "per_group"]))
+def test_planner_bit_exact_fuzz(L, seed, n, min_shared, alpha, groups, pad, placement, scope):
     rng = np.random.default_rng(seed)
     b = random_sequences(rng, n, alphabet=alpha, max_len=70, p_trainable=0.5, n_groups=3 if groups else 0)
     seqs = [b.seq(s) for s in range(b.n)]
     tr = [b.train(s) for s in range(b.n)]
     cap = max(len(s) for s in seqs) + int(rng.integers(0, 50))
     g = list(b.groups) if groups else None
-    want = P.pack_plan(seqs, tr, g, row_len=cap, min_shared=min_shared, pad_multiple=pad, placement=placement)
+    want = P.pack_plan(seqs, tr, g, row_len=cap, min_shared=min_shared, pad_multiple=pad, placement=placement,
+                       tree_scope=scope)
     got = ta.tree_pack_plan(b.tokens, b.offsets, b.trainable, b.groups if groups else None, cap,
-                            min_shared, pad, ta.TREE_PLACE_BFD if placement == "bfd" else ta.TREE_PLACE_IN_ORDER)
+                            min_shared, pad, ta.TREE_PLACE_BFD if placement == "bfd" else ta.TREE_PLACE_IN_ORDER,
+                            ta.TREE_SCOPE_GLOBAL if scope == "global" else ta.TREE_SCOPE_PER_GROUP)
     _compare(got, want)
 
 
@@ -91,6 +94,23 @@ def test_planner_config4_bit_exact(L):
     assert got["n_rows"] == 55 and got["unpacked_tokens"] > got["real_tokens"]
 
 
+def test_planner_config4_scopes_and_placements(L):
+    """Config 4 (48 groups, 3 task families, a shared 350-token system prompt, 4096-token rows)
+    under every tree scope and placement, bit-exact against the oracle.  [PTP]'s scope passage
+    reports per-group trees needing more rows than the global tree (66 vs 61 on its batch);
+    the same direction holds here."""
+    batch, _ = config4_sequences(4)
+    rows = {}
+    for scope, sc in (("global", ta.TREE_SCOPE_GLOBAL), ("per_group", ta.TREE_SCOPE_PER_GROUP)):
+        for place, pc in (("bfd", ta.TREE_PLACE_BFD), ("in_order", ta.TREE_PLACE_IN_ORDER)):
+            want = P.pack_batch(batch, 4096, 64, placement=place, tree_scope=scope)
+            got = ta.pack_batch(batch, 4096, 64, placement=pc, tree_scope=sc)
+            _compare(got, want)
+            rows[scope, place] = got["n_rows"]
+    assert rows["per_group", "bfd"] > rows["global", "bfd"]
+    assert rows["global", "in_order"] >= rows["global", "bfd"]
+
+
 def test_planner_errors(L):
     tok, off, _ = _flat([np.arange(10)])
     with pytest.raises(ta.TreeError) as e:
@@ -108,6 +128,9 @@ def test_planner_errors(L):
         with pytest.raises(ta.TreeError) as e:
             ta.tree_pack_plan(tok, off, **args)
         assert e.value.code == ta.TREE_E_INVAL
+    bad = ta.PackParams(9, 1, 0, 0, 7)
+    h0 = ctypes.c_void_p()
+    assert L.tree_pack_plan(None, None, 0, None, None, ctypes.byref(bad), ctypes.byref(h0)) == ta.TREE_E_INVAL
     p = ta.PackParams(9, 1, 0, 0)
     h = ctypes.c_void_p()
     assert L.tree_pack_plan(None, None, 1, None, None, ctypes.byref(p), ctypes.byref(h)) == ta.TREE_E_INVAL

@@ -221,13 +221,13 @@ def _config5(rng):
     return dict(T=T, h_q=64, h_kv=8, D=128, dtype="bf16", tree=(out_l, out_p, out_0), k_scale=True)
 
 
-def config4_sequences(seed: int = 4) -> tuple[SeqBatch, np.random.Generator]:
+def config4_sequences(seed: int = 4, n_groups: int = 48) -> tuple[SeqBatch, np.random.Generator]:
     """384 token sequences of the global-tree batch, group-major, and the rng to continue.
 
     Draw order: the 350-token system prompt; for each of 3 families its length U{200..600}
-    then tokens; then for each of 48 groups (family = g mod 3) the group-prompt length
-    U{100..800} and tokens, then 8 completions, each length U{50..600} then tokens.
-    Tokens are uniform over [0, 32000).  Completion tokens are trainable.
+    then tokens; then for each of ``n_groups`` groups (48 for the workload; family = g mod 3)
+    the group-prompt length U{100..800} and tokens, then 8 completions, each length U{50..600}
+    then tokens.  Tokens are uniform over [0, 32000).  Completion tokens are trainable.
     """
     rng = np.random.default_rng(seed)
     system = rng.integers(0, VOCAB, size=350)
@@ -236,7 +236,7 @@ def config4_sequences(seed: int = 4) -> tuple[SeqBatch, np.random.Generator]:
         n = int(rng.integers(200, 601))
         fams.append(rng.integers(0, VOCAB, size=n))
     seqs, trains, groups = [], [], []
-    for g in range(48):
+    for g in range(n_groups):
         fam = fams[g % 3]
         n = int(rng.integers(100, 801))
         prompt = rng.integers(0, VOCAB, size=n)
