@@ -14,7 +14,8 @@ Beside it, the backward (tree_attn_bwd: dQ, dK, dV for a seeded upstream gradien
 workloads) is timed on the same inputs and reported as `bwd`, with its FLOPs counted the
 FlashAttention way: 2.5 x the forward's useful FLOPs (S recomputed once, dP, dV, dK and dQ,
 each 2 * head_dim per visible pair and query head).  `packing` holds the host packing
-comparisons on the global-tree batch and the planner's cost as that batch grows.
+comparisons on the global-tree batch and the planner's cost as that batch grows; `rope` the
+in-place rotary embedding at tree positions (tree_rope) against HBM bandwidth.
 """
 from __future__ import annotations
 
@@ -211,6 +212,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-packing", action="store_true", help="skip the host packing comparisons")
+    ap.add_argument("--no-rope", action="store_true", help="skip the tree_rope timing")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -314,6 +316,31 @@ def main() -> int:
                "fwd_plus_bwd_ms": round(fwd_ms + bwd_ms, 4),
                "calls": "tree_attn_bwd (row terms + dQ kernel + dK/dV kernel); plan once per batch"}
 
+    rope = None
+    if not args.no_rope:
+        # tree positions: seg_pos0 + offset inside the segment (the plan's pos_ids), 0 at pads
+        pos = np.zeros((inp.n_rows, inp.row_len), np.int32)
+        for r in range(inp.n_rows):
+            for sg in range(int(inp.seg_row_ptr[r]), int(inp.seg_row_ptr[r + 1])):
+                a0, n0 = int(inp.seg_start[sg]), int(inp.seg_len[sg])
+                pos[r, a0:a0 + n0] = int(inp.seg_pos0[sg]) + np.arange(n0)
+        pos_d = torch.from_numpy(pos.reshape(-1)).to(dev)
+        qr, kr = q.clone(), k.clone()
+
+        def rope_step():
+            ta.tree_rope(plan.desc, pos_d, 10000.0, 0, qr, kr)
+
+        for _ in range(args.warmup):
+            rope_step()
+        rope_ms = timed(rope_step, args.steps)
+        esz = 2 if inp.dtype == "bf16" else 4
+        rope_bytes = 2 * inp.n_rows * inp.row_len * (inp.h_q + inp.h_kv) * inp.head_dim * esz + \
+            4 * inp.n_rows * inp.row_len
+        gbs = rope_bytes / (rope_ms * 1e-3) / 1e9
+        rope = {"us": round(rope_ms * 1e3, 2), "bytes_per_call": rope_bytes, "achieved_GBs": round(gbs, 1),
+                "peak_GBs": HBM_GBS, "frac": round(gbs / HBM_GBS, 4), "bound": "hbm",
+                "call": "tree_rope in place on q and k (theta 10000, positions = plan pos_ids)"}
+
     peak = PEAK_BF16_TFLOPS if inp.dtype == "bf16" else PEAK_F32_TFLOPS
     value = useful / (ms_step * 1e-3) / 1e12
     fwd_tflops = useful / (fwd_ms * 1e-3) / 1e12
@@ -343,6 +370,7 @@ def main() -> int:
         "roofline": roofline,
         "clock_adjusted": None,
         "bwd": bwd,
+        "rope": rope,
         "packing": None,
         "cpu_baseline": None,
     }

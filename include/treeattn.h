@@ -233,6 +233,27 @@ int tree_attn_bwd(const tree_attn_desc *d, const void *ws, void *bws, const void
                   const void *v, const void *o, const float *lse, const void *dout, void *dq,
                   void *dk, void *dv, void *stream);
 
+/*
+ * tree_rope — rotary position embedding at tree positions, in place on q and/or k.
+ * [PTP]: a packed row must reproduce every unpacked sequence exactly, so a token is rotated
+ * at its position in its own sequence (the plan's pos_ids: the segment's pos0 plus the offset
+ * in the segment), not at its row offset; with these positions the tree-masked attention of
+ * each root-to-leaf path equals rotary causal attention over that path unpacked.
+ *
+ *   d        shapes and dtype (n_rows, row_len, h_q, h_kv, head_dim, dtype); the segment
+ *            arrays are not used.
+ *   pos_ids  DEVICE int32 [n_rows * row_len] (tree_plan_view.pos_ids uploaded; pads 0).
+ *   theta    rotary base (> 1, e.g. 10000).  Pair i < D/2 (elements i and i + D/2, the
+ *            rotate-half pairing) turns by pos * theta^(-2i/D); angles are computed in fp64.
+ *   inverse  0: rotate by +angle; 1: by -angle (the backward of the rotation, for dq / dk).
+ *   q, k     DEVICE [n_rows, row_len, h_q | h_kv, head_dim] in dtype, rotated in place;
+ *            either may be NULL.  Asynchronous on `stream`.
+ * Errors: TREE_E_INVAL (shape, theta, inverse, null pos_ids or both q and k null),
+ * TREE_E_HIP.
+ */
+int tree_rope(const tree_attn_desc *d, const int32_t *pos_ids, float theta, int32_t inverse, void *q,
+              void *k, void *stream);
+
 const char *tree_status_str(int code);
 
 #ifdef __cplusplus

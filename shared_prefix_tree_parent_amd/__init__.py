@@ -15,6 +15,7 @@ carry the C names of ``include/treeattn.h``:
   tree_attn_bwd_plan(desc, ws, bws)  (async on the current stream)
   tree_attn_bwd_tiles(desc, bws)     -> (kp_ptr, kp_list) device pointers
   tree_attn_bwd(desc, ws, bws, q, k, v, o, lse, dout, dq, dk, dv)  (async on the current stream)
+  tree_rope(desc, pos_ids, theta, inverse, q, k)  (in place, async on the current stream)
 
 plus thin conveniences ``make_desc``, ``attn_plan``, ``attn_fwd`` and ``attn_bwd`` that allocate torch
 tensors.  If the library is missing this module raises on first use: there is no fallback.
@@ -38,7 +39,7 @@ TREE_SCOPE_GLOBAL, TREE_SCOPE_PER_GROUP = 0, 1
 EXPORTS = ("tree_pack_plan", "tree_plan_get", "tree_plan_free", "tree_attn_blocks",
            "tree_attn_workspace_size", "tree_attn_plan", "tree_attn_plan_status", "tree_attn_tiles",
            "tree_attn_fwd", "tree_attn_bwd_workspace_size", "tree_attn_bwd_plan", "tree_attn_bwd_tiles",
-           "tree_attn_bwd", "tree_status_str")
+           "tree_attn_bwd", "tree_rope", "tree_status_str")
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -108,6 +109,7 @@ def lib() -> ctypes.CDLL:
         L.tree_attn_bwd_plan.argtypes = [D, vp, vp, vp]
         L.tree_attn_bwd_tiles.argtypes = [D, vp, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.tree_attn_bwd.argtypes = [D] + [vp] * 12
+        L.tree_rope.argtypes = [D, vp, ctypes.c_float, ctypes.c_int32, vp, vp, vp]
         L.tree_status_str.argtypes = [ctypes.c_int]
         L.tree_status_str.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -258,6 +260,11 @@ def tree_attn_bwd(desc: AttnDesc, ws, bws, q, k, v, o, lse, dout, dq, dk, dv, st
            "tree_attn_bwd")
 
 
+def tree_rope(desc: AttnDesc, pos_ids, theta, inverse, q, k, stream=None) -> None:
+    _check(lib().tree_rope(ctypes.byref(desc), _ptr(pos_ids), float(theta), int(inverse), _ptr(q), _ptr(k),
+                           _stream(stream)), "tree_rope")
+
+
 # ------------------------------------------------------------------------------ conveniences
 
 class AttnPlan:
@@ -324,3 +331,13 @@ def attn_bwd(q, k, v, o, lse, dout, plan: AttnPlan, dq=None, dk=None, dv=None):
             raise ValueError("tensors must be contiguous")
     tree_attn_bwd(plan.desc, plan.ws, bws, q, k, v, o, lse, dout, dq, dk, dv)
     return dq, dk, dv
+
+
+def rope_(q, k, pos_ids, plan: AttnPlan, theta=10000.0, inverse=False):
+    """Rotary embedding at the plan's tree positions, in place on q and k (either may be None);
+    ``pos_ids`` is a device int32 tensor [n_rows * row_len].  Returns (q, k)."""
+    for t in (q, k, pos_ids):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    tree_rope(plan.desc, pos_ids, theta, 1 if inverse else 0, q, k)
+    return q, k

@@ -199,6 +199,15 @@ extern "C" int tree_attn_bwd(const tree_attn_desc *d, const void *ws, void *bws,
     return e == hipSuccess ? TREE_OK : TREE_E_HIP;
 }
 
+extern "C" int tree_rope(const tree_attn_desc *d, const int32_t *pos_ids, float theta, int32_t inverse, void *q,
+                         void *k, void *stream) {
+    if (!shape_ok(d) || !(theta > 1.0f) || (inverse != 0 && inverse != 1)) return TREE_E_INVAL;
+    if (d->n_rows > 0 && (pos_ids == nullptr || (q == nullptr && k == nullptr))) return TREE_E_INVAL;
+    const hipError_t e = launch_rope(d->n_rows, d->row_len, d->h_q, d->h_kv, d->head_dim, d->dtype, pos_ids, theta,
+                                     inverse, q, k, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TREE_OK : TREE_E_HIP;
+}
+
 extern "C" const char *tree_status_str(int code) {
     switch (code) {
         case TREE_OK: return "ok";

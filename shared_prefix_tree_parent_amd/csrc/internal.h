@@ -89,6 +89,8 @@ inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq) {
 // Launchers (defined in classify.hip / attn_fwd.hip / attn_bwd.hip).  Return hipSuccess or the
 // first error.
 hipError_t launch_plan(const tree_attn_desc &d, const WsLayout &w, char *ws, hipStream_t s);
+hipError_t launch_rope(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
+                       const int32_t *pos_ids, float theta, int32_t inverse, void *q, void *k, hipStream_t s);
 hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, const char *ws, char *bws, hipStream_t s);
 
 struct FwdShape {
