@@ -4,7 +4,8 @@ Plain, slow, obviously-correct reference implementations of what the GPU path
 computes: the radix segment build and best-fit-decreasing row packing
 (``oracle.packer``), the token-forest attention mask and tile classes
 (``oracle.mask``), masked softmax attention in float64, forward and gradients
-(``oracle.attention``), and rotary embedding at tree positions (``oracle.rope``).
+(``oracle.attention``), rotary embedding at tree positions (``oracle.rope``) and the
+gated delta rule threaded along the token tree (``oracle.gdn``).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path (the C-ABI library and
@@ -21,4 +22,4 @@ Parity status: every function here is pinned by a ``-m "not gpu"`` test against
 something other than itself (worked examples printed on the pages, closed forms,
 library routines, brute force, independent algorithms).  None is "parity unpinned".
 """
-from . import packer, mask, attention, rope  # noqa: F401
+from . import packer, mask, attention, rope, gdn  # noqa: F401

@@ -13,6 +13,8 @@ from .gen import (  # noqa: F401
     f32_from_bf16_bits,
     make_config,
     config4_sequences,
+    GdnInputs,
+    draw_gdn,
     draw_grad,
     draw_qkv,
     fill_pads,

@@ -360,3 +360,37 @@ def random_sequences(rng: np.random.Generator, n: int, alphabet: int = 3, max_le
         trains.append(t)
     groups = (rng.integers(0, n_groups, size=n) if n_groups > 0 else np.arange(n)).astype(np.int32)
     return _pack_seqs(seqs, trains, groups)
+
+
+# --------------------------------------------------------------------------- GDN inputs
+
+@dataclasses.dataclass
+class GdnInputs:
+    """Tree-packed rows for a gated delta-rule layer: the segment table of a ``RowInputs``
+    plus the layer's inputs.  x_q, x_k, x_v ``[R, T, H, D]`` bf16 bit patterns (before the
+    short convolution); conv_w ``[3, H*D, W]`` float32 (q, k, v; tap W-1 is the current
+    token); g ``[R, T, H]`` float32 log-decays (<= 0); beta ``[R, T, H]`` float32 in (0, 1)."""
+    rows: RowInputs
+    heads: int
+    head_dim: int
+    width: int
+    x_q: np.ndarray
+    x_k: np.ndarray
+    x_v: np.ndarray
+    conv_w: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+
+
+def draw_gdn(rows: RowInputs, heads: int = 16, head_dim: int = 128, width: int = 4, seed: int = 0) -> GdnInputs:
+    """GDN inputs on the tree of ``rows``, from ``default_rng(seed)`` in this order: x_q, x_k,
+    x_v ~ N(0, 1) (bf16-rounded), conv_w ~ N(0, 1/width), g = -softplus(N(0, 1)) / 8 (a decay
+    per token in about [0.6, 1)), beta = sigmoid(N(0, 1))."""
+    rng = np.random.default_rng(seed)
+    R, T = rows.n_rows, rows.row_len
+    xs = [bf16_bits_from_f32(rng.standard_normal((R, T, heads, head_dim), dtype=np.float32)) for _ in range(3)]
+    conv_w = (rng.standard_normal((3, heads * head_dim, width)) / np.sqrt(width)).astype(np.float32)
+    z = rng.standard_normal((R, T, heads))
+    g = (-np.log1p(np.exp(z)) / 8.0).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((R, T, heads))))).astype(np.float32)
+    return GdnInputs(rows, heads, head_dim, width, xs[0], xs[1], xs[2], conv_w, g, beta)
