@@ -15,7 +15,8 @@ workloads) is timed on the same inputs and reported as `bwd`, with its FLOPs cou
 FlashAttention way: 2.5 x the forward's useful FLOPs (S recomputed once, dP, dV, dK and dQ,
 each 2 * head_dim per visible pair and query head).  `packing` holds the host packing
 comparisons on the global-tree batch and the planner's cost as that batch grows; `rope` the
-in-place rotary embedding at tree positions (tree_rope) against HBM bandwidth.
+in-place rotary embedding at tree positions (tree_rope) against HBM bandwidth; `gdn` the
+gated delta rule threaded along the same token tree (tree_gdn_fwd, 16 heads x 128).
 """
 from __future__ import annotations
 
@@ -213,6 +214,7 @@ def main() -> int:
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-packing", action="store_true", help="skip the host packing comparisons")
     ap.add_argument("--no-rope", action="store_true", help="skip the tree_rope timing")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the tree_gdn_fwd timing")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -341,6 +343,36 @@ def main() -> int:
                 "peak_GBs": HBM_GBS, "frac": round(gbs / HBM_GBS, 4), "bound": "hbm",
                 "call": "tree_rope in place on q and k (theta 10000, positions = plan pos_ids)"}
 
+    gdn = None
+    if not args.no_gdn and inp.dtype == "bf16":
+        from workloads import draw_gdn
+        H_g = 16
+        gin = draw_gdn(inp, heads=H_g, seed=args.config)
+        gplan = ta.GdnPlan(inp.seg_row_ptr, inp.seg_start, inp.seg_len, inp.seg_parent, inp.n_rows, inp.row_len,
+                           H_g, device=dev)
+        tb = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        tf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+        gx = [tb(x) for x in (gin.x_q, gin.x_k, gin.x_v)]
+        gw, gg, gbeta = tf(gin.conv_w), tf(gin.g), tf(gin.beta)
+        go = torch.zeros_like(gx[0])
+
+        def gdn_step():
+            ta.tree_gdn_fwd(gplan.desc, gplan.info, gplan.gws, *gx, gw, gg, gbeta, go)
+
+        for _ in range(args.warmup):
+            gdn_step()
+        gdn_ms = timed(gdn_step, args.steps)
+        n_real = int(inp.real_len.sum())
+        rec_flops = 8.0 * 128 * 128 * H_g * n_real                  # per token and head: k^T h, update, h^T q
+        chunk_flops = gplan.info.n_chunks * H_g * (2 * 2 * 64 * 64 * 128 + 2 * 64 * 64 * 256 +
+                                                    3 * 2 * 64 * 128 * 128 + 2 * 64 * 64 * 128)
+        gdn = {"ms": round(gdn_ms, 4), "heads": H_g, "head_dim": 128, "tokens": n_real,
+               "chunks": gplan.info.n_chunks, "levels": gplan.info.n_levels,
+               "recurrent_gflop": round(rec_flops / 1e9, 3), "chunked_gflop": round(chunk_flops / 1e9, 3),
+               "tokens_per_s": round(n_real / (gdn_ms * 1e-3), 1),
+               "tflops_chunked": round(chunk_flops / (gdn_ms * 1e-3) / 1e12, 2),
+               "call": "tree_gdn_fwd (conv + norm, chunk factors, one state scan per tree depth)"}
+
     peak = PEAK_BF16_TFLOPS if inp.dtype == "bf16" else PEAK_F32_TFLOPS
     value = useful / (ms_step * 1e-3) / 1e12
     fwd_tflops = useful / (fwd_ms * 1e-3) / 1e12
@@ -371,6 +403,7 @@ def main() -> int:
         "clock_adjusted": None,
         "bwd": bwd,
         "rope": rope,
+        "gdn": gdn,
         "packing": None,
         "cpu_baseline": None,
     }

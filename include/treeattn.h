@@ -234,6 +234,42 @@ int tree_attn_bwd(const tree_attn_desc *d, const void *ws, void *bws, const void
                   void *dk, void *dv, void *stream);
 
 /*
+ * Gated delta rule (GDN) threaded along the token tree ([PTP] GDN passage: a recurrent layer
+ * needs no mask but a running state, forked once per branch point and reset at every root;
+ * the conv context is carried across the join).  Per head (head_dim 128, width-4 conv):
+ *   y_c(t) = SiLU(sum_j conv_w[c][ch][3 - j] * x_c(pi^j(t)))   c = q, k, v; pi = token parent,
+ *            zero input past a root's first token
+ *   q^ = y_q / sqrt(|y_q|^2 + 1e-6) / sqrt(128),  k^ = y_k / sqrt(|y_k|^2 + 1e-6),  v^ = y_v
+ *   h_t = exp(g_t) (h_pi(t) - beta_t k^_t (k^_t^T h_pi(t))) + beta_t k^_t v^_t^T  (h = 0 at roots)
+ *   o_t = h_t^T q^_t
+ * Shapes from the descriptor: h_q = h_kv = heads, head_dim 128, dtype bf16 (else
+ * TREE_E_INVAL).  The host planner's segment table (host copies) drives the depth levels.
+ *
+ * tree_gdn_workspace_size: bytes of the caller-allocated GDN workspace (256-byte aligned):
+ *   token parents, chunk / segment / level records, conv outputs (3 x [R, T, H, 128] bf16),
+ *   per-(chunk, head) WY factors (~56 KiB each) and one 128 x 128 fp32 state per (segment,
+ *   head).
+ * tree_gdn_plan: validates the host segment table (segments back to back from token 0, a
+ *   parent before its children; else TREE_E_LAYOUT), writes the records into gws (synchronous
+ *   on `stream`) and fills *info, which tree_gdn_fwd needs.  Once per batch.
+ * tree_gdn_fwd: x_q, x_k, x_v DEVICE [R, T, H, 128] bf16 (before the conv); conv_w DEVICE
+ *   float32 [3][H * 128][4] (tap 3 = current token); g, beta DEVICE float32 [R, T, H] (log
+ *   decay <= 0, beta in [0, 1]); writes o DEVICE [R, T, H, 128] bf16 at real tokens (pads
+ *   untouched).  Asynchronous; overwrites everything in gws after the records.
+ */
+typedef struct {
+    int32_t n_chunks, n_segs, n_levels, max_level_segs;
+} tree_gdn_info;
+int tree_gdn_workspace_size(const tree_attn_desc *d, const int32_t *h_seg_row_ptr, const int32_t *h_seg_len,
+                            size_t *bytes);
+int tree_gdn_plan(const tree_attn_desc *d, const int32_t *h_seg_row_ptr, const int32_t *h_seg_start,
+                  const int32_t *h_seg_len, const int32_t *h_seg_parent, void *gws, tree_gdn_info *info,
+                  void *stream);
+int tree_gdn_fwd(const tree_attn_desc *d, const tree_gdn_info *info, void *gws, const void *x_q,
+                 const void *x_k, const void *x_v, const float *conv_w, const float *g, const float *beta,
+                 void *o, void *stream);
+
+/*
  * tree_rope — rotary position embedding at tree positions, in place on q and/or k.
  * [PTP]: a packed row must reproduce every unpacked sequence exactly, so a token is rotated
  * at its position in its own sequence (the plan's pos_ids: the segment's pos0 plus the offset

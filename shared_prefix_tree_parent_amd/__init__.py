@@ -16,6 +16,9 @@ carry the C names of ``include/treeattn.h``:
   tree_attn_bwd_tiles(desc, bws)     -> (kp_ptr, kp_list) device pointers
   tree_attn_bwd(desc, ws, bws, q, k, v, o, lse, dout, dq, dk, dv)  (async on the current stream)
   tree_rope(desc, pos_ids, theta, inverse, q, k)  (in place, async on the current stream)
+  tree_gdn_workspace_size(desc, seg_row_ptr, seg_len) -> bytes   (host segment arrays)
+  tree_gdn_plan(desc, seg_row_ptr, seg_start, seg_len, seg_parent, gws) -> GdnInfo
+  tree_gdn_fwd(desc, info, gws, x_q, x_k, x_v, conv_w, g, beta, o)  (async on the current stream)
 
 plus thin conveniences ``make_desc``, ``attn_plan``, ``attn_fwd`` and ``attn_bwd`` that allocate torch
 tensors.  If the library is missing this module raises on first use: there is no fallback.
@@ -39,7 +42,8 @@ TREE_SCOPE_GLOBAL, TREE_SCOPE_PER_GROUP = 0, 1
 EXPORTS = ("tree_pack_plan", "tree_plan_get", "tree_plan_free", "tree_attn_blocks",
            "tree_attn_workspace_size", "tree_attn_plan", "tree_attn_plan_status", "tree_attn_tiles",
            "tree_attn_fwd", "tree_attn_bwd_workspace_size", "tree_attn_bwd_plan", "tree_attn_bwd_tiles",
-           "tree_attn_bwd", "tree_rope", "tree_status_str")
+           "tree_attn_bwd", "tree_rope", "tree_gdn_workspace_size", "tree_gdn_plan", "tree_gdn_fwd",
+           "tree_status_str")
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -82,6 +86,11 @@ class TileView(ctypes.Structure):
                 ("work", ctypes.c_void_p), ("status", ctypes.c_void_p)]
 
 
+class GdnInfo(ctypes.Structure):
+    _fields_ = [("n_chunks", ctypes.c_int32), ("n_segs", ctypes.c_int32), ("n_levels", ctypes.c_int32),
+                ("max_level_segs", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -110,6 +119,9 @@ def lib() -> ctypes.CDLL:
         L.tree_attn_bwd_tiles.argtypes = [D, vp, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.tree_attn_bwd.argtypes = [D] + [vp] * 12
         L.tree_rope.argtypes = [D, vp, ctypes.c_float, ctypes.c_int32, vp, vp, vp]
+        L.tree_gdn_workspace_size.argtypes = [D, vp, vp, ctypes.POINTER(ctypes.c_size_t)]
+        L.tree_gdn_plan.argtypes = [D, vp, vp, vp, vp, vp, ctypes.POINTER(GdnInfo), vp]
+        L.tree_gdn_fwd.argtypes = [D, ctypes.POINTER(GdnInfo), vp] + [vp] * 7 + [vp]
         L.tree_status_str.argtypes = [ctypes.c_int]
         L.tree_status_str.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -260,6 +272,31 @@ def tree_attn_bwd(desc: AttnDesc, ws, bws, q, k, v, o, lse, dout, dq, dk, dv, st
            "tree_attn_bwd")
 
 
+def _host_i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def tree_gdn_workspace_size(desc: AttnDesc, seg_row_ptr, seg_len) -> int:
+    n = ctypes.c_size_t()
+    rp, ln = _host_i32(seg_row_ptr), _host_i32(seg_len)
+    _check(lib().tree_gdn_workspace_size(ctypes.byref(desc), _ptr(rp), _ptr(ln), ctypes.byref(n)),
+           "tree_gdn_workspace_size")
+    return n.value
+
+
+def tree_gdn_plan(desc: AttnDesc, seg_row_ptr, seg_start, seg_len, seg_parent, gws, stream=None) -> GdnInfo:
+    info = GdnInfo()
+    arrs = [_host_i32(a) for a in (seg_row_ptr, seg_start, seg_len, seg_parent)]
+    _check(lib().tree_gdn_plan(ctypes.byref(desc), *[_ptr(a) for a in arrs], _ptr(gws), ctypes.byref(info),
+                               _stream(stream)), "tree_gdn_plan")
+    return info
+
+
+def tree_gdn_fwd(desc: AttnDesc, info: GdnInfo, gws, x_q, x_k, x_v, conv_w, g, beta, o, stream=None) -> None:
+    _check(lib().tree_gdn_fwd(ctypes.byref(desc), ctypes.byref(info), _ptr(gws), _ptr(x_q), _ptr(x_k), _ptr(x_v),
+                              _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(o), _stream(stream)), "tree_gdn_fwd")
+
+
 def tree_rope(desc: AttnDesc, pos_ids, theta, inverse, q, k, stream=None) -> None:
     _check(lib().tree_rope(ctypes.byref(desc), _ptr(pos_ids), float(theta), int(inverse), _ptr(q), _ptr(k),
                            _stream(stream)), "tree_rope")
@@ -341,3 +378,30 @@ def rope_(q, k, pos_ids, plan: AttnPlan, theta=10000.0, inverse=False):
             raise ValueError("tensors must be contiguous")
     tree_rope(plan.desc, pos_ids, theta, 1 if inverse else 0, q, k)
     return q, k
+
+
+
+class GdnPlan:
+    """Segment table + GDN workspace for one batch: heads of head_dim 128, bf16."""
+
+    def __init__(self, seg_row_ptr, seg_start, seg_len, seg_parent, n_rows, row_len, heads, device="cuda"):
+        import torch
+        as_dev = lambda a: torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+        self.host = [np.ascontiguousarray(a, dtype=np.int32) for a in (seg_row_ptr, seg_start, seg_len, seg_parent)]
+        self.seg = [as_dev(a) for a in self.host]
+        self.desc = make_desc(n_rows, row_len, heads, heads, 128, "bf16", *self.seg)
+        nbytes = tree_gdn_workspace_size(self.desc, self.host[0], self.host[2])
+        self.gws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        self.info = tree_gdn_plan(self.desc, *self.host, self.gws)
+
+
+def gdn_fwd(x_q, x_k, x_v, conv_w, g, beta, plan: GdnPlan, o=None):
+    """Gated delta rule over the plan's token tree; returns o [R, T, H, 128] bf16 (pads zero)."""
+    import torch
+    if o is None:
+        o = torch.zeros_like(x_q)
+    for t in (x_q, x_k, x_v, conv_w, g, beta, o):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    tree_gdn_fwd(plan.desc, plan.info, plan.gws, x_q, x_k, x_v, conv_w, g, beta, o)
+    return o

@@ -1,6 +1,7 @@
 // C-ABI entry points of the device half of libtreeattn (see include/treeattn.h): argument
 // checks, workspace layout, launches.  No device memory is allocated here.
 #include <cmath>
+#include <vector>
 
 #include "internal.h"
 
@@ -196,6 +197,130 @@ extern "C" int tree_attn_bwd(const tree_attn_desc *d, const void *ws, void *bws,
     sh.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->head_dim));
     const hipError_t e = launch_bwd(sh, w, b, static_cast<const char *>(ws), static_cast<char *>(bws), q, k, v,
                                     o, lse, dout, dq, dk, dv, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TREE_OK : TREE_E_HIP;
+}
+
+// ----------------------------------------------------------------------------- gated delta rule
+
+namespace {
+bool gdn_shape_ok(const tree_attn_desc *d) {
+    return shape_ok(d) && d->h_q == d->h_kv && d->head_dim == 128 && d->dtype == TREE_DT_BF16;
+}
+
+int gdn_counts(const tree_attn_desc *d, const int32_t *rp, const int32_t *len, int32_t *n_segs, int32_t *n_chunks) {
+    if (!gdn_shape_ok(d)) return TREE_E_INVAL;
+    if (d->n_rows > 0 && (rp == nullptr || len == nullptr)) return TREE_E_INVAL;
+    if (d->n_rows > 0 && rp[0] != 0) return TREE_E_LAYOUT;
+    int64_t chunks = 0;
+    for (int32_t r = 0; r < d->n_rows; ++r) {
+        if (rp[r + 1] < rp[r]) return TREE_E_LAYOUT;
+        for (int32_t s = rp[r]; s < rp[r + 1]; ++s) {
+            if (len[s] <= 0 || len[s] > d->row_len) return TREE_E_LAYOUT;
+            chunks += (len[s] + 63) / 64;
+        }
+    }
+    if (chunks > INT32_MAX / 64) return TREE_E_INVAL;
+    *n_segs = d->n_rows > 0 ? rp[d->n_rows] : 0;
+    *n_chunks = static_cast<int32_t>(chunks);
+    return TREE_OK;
+}
+}  // namespace
+
+extern "C" int tree_gdn_workspace_size(const tree_attn_desc *d, const int32_t *h_seg_row_ptr,
+                                       const int32_t *h_seg_len, size_t *bytes) {
+    int32_t n_segs = 0, n_chunks = 0;
+    if (bytes == nullptr) return TREE_E_INVAL;
+    const int rc = gdn_counts(d, h_seg_row_ptr, h_seg_len, &n_segs, &n_chunks);
+    if (rc != TREE_OK) return rc;
+    *bytes = make_gdn_layout(d->n_rows, d->row_len, d->h_q, n_chunks, n_segs).total;
+    return TREE_OK;
+}
+
+extern "C" int tree_gdn_plan(const tree_attn_desc *d, const int32_t *h_seg_row_ptr, const int32_t *h_seg_start,
+                             const int32_t *h_seg_len, const int32_t *h_seg_parent, void *gws,
+                             tree_gdn_info *info, void *stream) {
+    int32_t n_segs = 0, n_chunks = 0;
+    const int rc = gdn_counts(d, h_seg_row_ptr, h_seg_len, &n_segs, &n_chunks);
+    if (rc != TREE_OK) return rc;
+    if (info == nullptr || gws == nullptr || (d->n_rows > 0 && (h_seg_start == nullptr || h_seg_parent == nullptr)))
+        return TREE_E_INVAL;
+    const int32_t R = d->n_rows, T = d->row_len;
+    // Validate the table (segments back to back from token 0, parents before children) and
+    // build token parents, chunks, segment records and depth levels.
+    std::vector<int32_t> pi(size_t(R) * T, -2), chunk_meta, seg_meta(size_t(n_segs) * 4), depth(n_segs, 0);
+    chunk_meta.reserve(size_t(n_chunks) * 4);
+    for (int32_t r = 0; r < R; ++r) {
+        const int32_t a = h_seg_row_ptr[r], b = h_seg_row_ptr[r + 1];
+        int64_t off = 0;
+        for (int32_t g = a; g < b; ++g) {
+            const int32_t st = h_seg_start[g], n = h_seg_len[g], p = h_seg_parent[g];
+            if (st != off || off + n > T || p < -1 || p >= g - a) return TREE_E_LAYOUT;
+            off += n;
+            const int64_t base = int64_t(r) * T;
+            pi[base + st] = p < 0 ? -1 : int32_t(base + h_seg_start[a + p] + h_seg_len[a + p] - 1);
+            for (int32_t i = 1; i < n; ++i) pi[base + st + i] = int32_t(base + st + i - 1);
+            depth[g] = p < 0 ? 0 : depth[a + p] + 1;
+            seg_meta[size_t(g) * 4 + 0] = r;
+            seg_meta[size_t(g) * 4 + 1] = static_cast<int32_t>(chunk_meta.size() / 4);
+            seg_meta[size_t(g) * 4 + 2] = (n + 63) / 64;
+            seg_meta[size_t(g) * 4 + 3] = p < 0 ? -1 : a + p;
+            for (int32_t c0 = 0; c0 < n; c0 += 64) {
+                chunk_meta.push_back(r);
+                chunk_meta.push_back(st + c0);
+                chunk_meta.push_back(std::min(64, n - c0));
+                chunk_meta.push_back(g);
+            }
+        }
+    }
+    int32_t n_levels = 0;
+    for (int32_t g = 0; g < n_segs; ++g) n_levels = std::max(n_levels, depth[g] + 1);
+    std::vector<int32_t> level_ptr(size_t(n_levels) + 1, 0), level_segs(n_segs);
+    for (int32_t g = 0; g < n_segs; ++g) ++level_ptr[depth[g] + 1];
+    int32_t max_level = 0;
+    for (int32_t l = 0; l < n_levels; ++l) {
+        max_level = std::max(max_level, level_ptr[l + 1]);
+        level_ptr[l + 1] += level_ptr[l];
+    }
+    {
+        std::vector<int32_t> fill(level_ptr.begin(), level_ptr.end() - 1);
+        for (int32_t g = 0; g < n_segs; ++g) level_segs[fill[depth[g]]++] = g;
+    }
+    const GdnLayout L = make_gdn_layout(R, T, d->h_q, n_chunks, n_segs);
+    char *w = static_cast<char *>(gws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    struct Part { size_t off; const void *src; size_t bytes; };
+    const Part parts[] = {{L.pi, pi.data(), pi.size() * 4},
+                          {L.chunk_meta, chunk_meta.data(), chunk_meta.size() * 4},
+                          {L.seg_meta, seg_meta.data(), seg_meta.size() * 4},
+                          {L.level_ptr, level_ptr.data(), level_ptr.size() * 4},
+                          {L.level_segs, level_segs.data(), level_segs.size() * 4}};
+    for (const Part &pt : parts)
+        if (pt.bytes > 0 && hipMemcpyAsync(w + pt.off, pt.src, pt.bytes, hipMemcpyHostToDevice, s) != hipSuccess)
+            return TREE_E_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return TREE_E_HIP;   // the host arrays are temporaries
+    info->n_chunks = n_chunks;
+    info->n_segs = n_segs;
+    info->n_levels = n_levels;
+    info->max_level_segs = max_level;
+    return TREE_OK;
+}
+
+extern "C" int tree_gdn_fwd(const tree_attn_desc *d, const tree_gdn_info *info, void *gws, const void *x_q,
+                            const void *x_k, const void *x_v, const float *conv_w, const float *g, const float *beta,
+                            void *o, void *stream) {
+    if (!gdn_shape_ok(d) || info == nullptr || gws == nullptr) return TREE_E_INVAL;
+    if (info->n_chunks < 0 || info->n_segs < 0 || info->n_levels < 0 || info->n_levels > info->n_segs ||
+        info->max_level_segs < 0 || info->max_level_segs > info->n_segs)
+        return TREE_E_INVAL;
+    if (d->n_rows > 0 && (x_q == nullptr || x_k == nullptr || x_v == nullptr || conv_w == nullptr || g == nullptr ||
+                          beta == nullptr || o == nullptr))
+        return TREE_E_INVAL;
+    GdnLayout L = make_gdn_layout(d->n_rows, d->row_len, d->h_q, info->n_chunks, info->n_segs);
+    L.n_levels = info->n_levels;
+    L.max_level_segs = info->max_level_segs;
+    GdnShape sh{d->n_rows, d->row_len, d->h_q, 1e-6f};
+    const hipError_t e = launch_gdn(sh, L, static_cast<char *>(gws), x_q, x_k, x_v, conv_w, g, beta, o,
+                                    static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TREE_OK : TREE_E_HIP;
 }
 

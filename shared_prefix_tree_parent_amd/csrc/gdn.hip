@@ -1,0 +1,415 @@
+// Gated delta rule over tree-packed rows for gfx950 (CDNA4), head_dim 128, bf16 in and out.
+//
+// "Prefix tree packing" (furtherai.github.io), GDN passage: the layer is recurrent, so a
+// running state is threaded token by token, forked once per branch point and reset at every
+// root; the planner walks the tree depth by depth and runs one causal-conv pass and one
+// chunked delta-rule pass per depth, a child starting from its parent's final state.  The
+// layer itself (not printed on the page) is the published gated delta rule with a width-4
+// depthwise causal convolution, per head:
+//   y_c(t) = SiLU(sum_j w_c[:, 3-j] x_c(pi^j(t)))      (pi: token parent; zero past a root)
+//   q^ = y_q / sqrt(|y_q|^2 + eps) / sqrt(D),  k^ = y_k / sqrt(|y_k|^2 + eps),  v^ = y_v
+//   h_t = a_t (h_pi(t) - b_t k^_t (k^_t^T h_pi(t))) + b_t k^_t v^_t^T,  o_t = h_t^T q^_t.
+//
+// Launches (all on the caller's stream):
+//   * gdn_conv: one workgroup per token; the conv follows the token-parent chain, so a child's
+//     first tokens convolve with its parent's last ones (the context carried across the join).
+//   * gdn_prep: one workgroup per (chunk, head), chunk-parallel.  Chunks are 64 tokens of one
+//     segment, counted from the segment's start (the last one ragged), so every segment ends
+//     on a chunk boundary and its exact final state is available to its children: no tail is
+//     replayed.  With G the cumulative log-decay inside the chunk, gamma = exp(G):
+//       A_ts = b_t gamma_t/gamma_s k_t.k_s (s < t),  P_ts = gamma_t/gamma_s q_t.k_s (s <= t),
+//       U = (I + A)^-1 diag(b) V,  Y = (I + A)^-1 diag(b gamma) K      (forward substitution)
+//     Gram and QK^T on MFMA; the solves in fp32 (one thread per column of [V | K]).
+//   * gdn_scan, once per tree depth: one workgroup per (segment of that depth, head), 4 waves,
+//     each holding 32 columns of the 128 x 128 state H in fp32 MFMA accumulators, from the
+//     parent's final state (zero at roots); per chunk
+//       W = U - Y H,   O = diag(gamma) Q H + P W,   H <- gamma_C H + K^T diag(gamma_C/gamma) W
+//     with bf16 operands (H rounded for the products only) and fp32 accumulation; the
+//     segment's final H is stored for its children.
+#include "internal.h"
+#include "tile_ops.h"
+
+namespace treeattn {
+namespace {
+
+using namespace tile;
+
+constexpr int kGD = 128;                  // head_dim
+constexpr int kGW = 4;                    // conv width
+constexpr int kGC = 64;                   // chunk length
+constexpr float kGLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------------------ gdn_conv
+//
+// One workgroup (256 threads) per token; a thread takes 8 consecutive channels of a tensor,
+// 16 threads one head (the L2 norm is a 16-lane sum).
+__global__ __launch_bounds__(256) void gdn_conv(int32_t n_tok, int32_t H, const int32_t *__restrict__ pi,
+                                                const __bf16 *__restrict__ xq, const __bf16 *__restrict__ xk,
+                                                const __bf16 *__restrict__ xv, const float *__restrict__ w,
+                                                float eps, __bf16 *__restrict__ qh, __bf16 *__restrict__ kh,
+                                                __bf16 *__restrict__ vh) {
+    const int64_t tok = blockIdx.x;
+    if (tok >= n_tok) return;
+    const int p = pi[tok];
+    if (p < -1) return;                                   // pad: never read downstream
+    // ch[j] = pi^j(tok) (global token indices; -1 past a root's first token)
+    int64_t ch[kGW];
+    ch[0] = tok;
+    int64_t nxt = p;
+    for (int j = 1; j < kGW; ++j) {
+        ch[j] = nxt;
+        nxt = nxt >= 0 ? pi[nxt] : -1;
+    }
+    const int C = H * kGD;                                 // channels per tensor
+    const float qscale = 0.08838834764831845f;             // 1 / sqrt(128)
+    for (int c8 = threadIdx.x * 8; c8 < C; c8 += blockDim.x * 8) {
+#pragma unroll
+        for (int tsr = 0; tsr < 3; ++tsr) {
+            const __bf16 *x = tsr == 0 ? xq : (tsr == 1 ? xk : xv);
+            const float *wt = w + (int64_t(tsr) * C + c8) * kGW;
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = 0.f;
+#pragma unroll
+            for (int j = 0; j < kGW; ++j) {
+                if (ch[j] < 0) break;
+                const bf16x8_t xv8 = *reinterpret_cast<const bf16x8_t *>(x + ch[j] * C + c8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = fmaf(wt[e * kGW + (kGW - 1 - j)], float(xv8[e]), y[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = y[e] / (1.f + __expf(-y[e]));
+            float scale = 1.f;
+            if (tsr < 2) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+#pragma unroll
+                for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 16);
+                scale = rsqrtf(ss + eps) * (tsr == 0 ? qscale : 1.f);
+            }
+            bf16x8_t o8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[e] = static_cast<__bf16>(y[e] * scale);
+            __bf16 *out = tsr == 0 ? qh : (tsr == 1 ? kh : vh);
+            *reinterpret_cast<bf16x8_t *>(out + tok * C + c8) = o8;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ gdn_prep
+//
+// LDS: Q, K, V chunk tiles (64 x 128 bf16, swizzled), A (64 x 64 fp32), the solve's columns
+// X (64 x 256 fp32: [beta V | beta gamma K] -> [U | Y]), G and beta (64 fp32 each).
+struct PrepLds {
+    static constexpr int TILE = kGC * kGD * 2;
+    static constexpr int Q_OFF = 0, K_OFF = TILE, V_OFF = 2 * TILE, A_OFF = 3 * TILE;
+    static constexpr int X_OFF = A_OFF + kGC * kGC * 4;
+    static constexpr int G_OFF = X_OFF + kGC * 256 * 4, GB_OFF = G_OFF + kGC * 4;
+    static constexpr int SIZE = GB_OFF + kGC * 4;
+};
+
+struct GdnArgs {
+    int32_t R, T, H, n_chunks;
+    const int4 *chunk_meta;      // (row, t0, n, seg)
+    const int4 *seg_meta;        // (row, first chunk, n chunks, parent segment or -1)
+    const int32_t *level_ptr, *level_segs;
+    const __bf16 *qh, *kh, *vh;
+    const float *g, *beta;
+    float *U;                    // [n_chunks, H, 64, 128]
+    __bf16 *Yn;                  // [n_chunks, H, 64, 128]  (-Y)
+    __bf16 *P;                   // [n_chunks, H, 64, 64]
+    float *G;                    // [n_chunks, H, 64]
+    float *states;               // [n_segs, H, 128, 128]
+    __bf16 *o;                   // [R, T, H, 128]
+};
+
+__global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
+    using T128 = Tile<kGD>;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = blockIdx.x % a.H, c = blockIdx.x / a.H;
+    if (c >= a.n_chunks) return;
+    const int4 cm = a.chunk_meta[c];
+    const int r = cm.x, t0 = cm.y, n = cm.z;
+    const int64_t tok0 = int64_t(r) * a.T + t0;
+    const int stride = a.H * kGD * 2;
+    const uint32_t lds0 = lds_base(smem);
+    const int64_t hoff = (tok0 * a.H + h) * kGD * 2;
+    copy_tile<kGD>(reinterpret_cast<const char *>(a.qh) + hoff, n, stride, lds0 + PrepLds::Q_OFF, kGC, wave, 4, lane);
+    copy_tile<kGD>(reinterpret_cast<const char *>(a.kh) + hoff, n, stride, lds0 + PrepLds::K_OFF, kGC, wave, 4, lane);
+    copy_tile<kGD>(reinterpret_cast<const char *>(a.vh) + hoff, n, stride, lds0 + PrepLds::V_OFF, kGC, wave, 4, lane);
+    float *Gs = reinterpret_cast<float *>(smem + PrepLds::G_OFF);
+    float *Bs = reinterpret_cast<float *>(smem + PrepLds::GB_OFF);
+    if (wave == 0) {
+        // inclusive cumulative log-decay over the chunk; pad rows: g = 0, beta = 0
+        const bool on = lane < n;
+        float gv = on ? a.g[(tok0 + lane) * a.H + h] : 0.f;
+        const float bv = on ? a.beta[(tok0 + lane) * a.H + h] : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(gv, off, 64);
+            if (lane >= off) gv += y;
+        }
+        Gs[lane] = gv;
+        Bs[lane] = bv;
+        a.G[(int64_t(c) * a.H + h) * kGC + lane] = gv;
+    }
+    wait_loads();
+    __syncthreads();
+
+    // Gram K K^T and Q K^T: wave w takes the 32 x 32 block (t block w/2, s block w%2).
+    const char *Qt = smem + PrepLds::Q_OFF, *Kt = smem + PrepLds::K_OFF;
+    const int bt = wave >> 1, bs = wave & 1;
+    floatx16 kk = zero16(), qk = zero16();
+#pragma unroll
+    for (int ds = 0; ds < kGD / 16; ++ds) {
+        const bf16x8_t kb = T128::row_frag(Kt, 32 * bs, lane, ds);
+        kk = mfma(T128::row_frag(Kt, 32 * bt, lane, ds), kb, kk);
+        qk = mfma(T128::row_frag(Qt, 32 * bt, lane, ds), kb, qk);
+    }
+    float *As = reinterpret_cast<float *>(smem + PrepLds::A_OFF);
+    __bf16 *Pout = a.P + (int64_t(c) * a.H + h) * kGC * kGC;
+    const int s = 32 * bs + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int t = 32 * bt + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
+        const float dec = __builtin_amdgcn_exp2f((Gs[t] - Gs[s]) * kGLog2e);   // gamma_t / gamma_s for s <= t
+        As[t * kGC + s] = s < t ? Bs[t] * dec * kk[i] : 0.f;
+        Pout[t * kGC + s] = static_cast<__bf16>(s <= t ? dec * qk[i] : 0.f);
+    }
+    __syncthreads();
+
+    // Forward substitution, one thread per column of [beta V | beta gamma K]:
+    //   x_t = rhs_t - sum_{s < t} A_ts x_s,  the column kept in LDS (X[t][column]).
+    {
+        const int col = tid & 127;
+        const bool isk = tid >= 128;
+        const char *src = isk ? Kt : smem + PrepLds::V_OFF;
+        float *X = reinterpret_cast<float *>(smem + PrepLds::X_OFF) + tid;
+        for (int t = 0; t < kGC; ++t) {
+            const float gam = isk ? __builtin_amdgcn_exp2f(Gs[t] * kGLog2e) : 1.f;
+            float acc = Bs[t] * gam * T128::at(src, t, col);
+            const float *Arow = As + t * kGC;
+            int s4 = 0;
+            for (; s4 + 4 <= t; s4 += 4) {
+                const float4 a4 = *reinterpret_cast<const float4 *>(Arow + s4);
+                acc = fmaf(-a4.x, X[(s4 + 0) * 256], acc);
+                acc = fmaf(-a4.y, X[(s4 + 1) * 256], acc);
+                acc = fmaf(-a4.z, X[(s4 + 2) * 256], acc);
+                acc = fmaf(-a4.w, X[(s4 + 3) * 256], acc);
+            }
+            for (; s4 < t; ++s4) acc = fmaf(-Arow[s4], X[s4 * 256], acc);
+            X[t * 256] = acc;
+        }
+        if (!isk) {
+            float *Uo = a.U + (int64_t(c) * a.H + h) * kGC * kGD + col;
+            for (int t = 0; t < kGC; ++t) Uo[t * kGD] = X[t * 256];
+        } else {
+            __bf16 *Yo = a.Yn + (int64_t(c) * a.H + h) * kGC * kGD + col;
+            for (int t = 0; t < kGC; ++t) Yo[t * kGD] = static_cast<__bf16>(-X[t * 256]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------ gdn_scan
+struct ScanLds {
+    static constexpr int TILE = kGC * kGD * 2;                  // 64 x 128 bf16
+    static constexpr int Q_OFF = 0, K_OFF = TILE, Y_OFF = 2 * TILE, P_OFF = 3 * TILE;
+    static constexpr int G_OFF = P_OFF + kGC * kGC * 2;
+    static constexpr int SIZE = G_OFF + kGC * 4;
+};
+
+__global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
+    using T128 = Tile<kGD>;
+    using T64 = Tile<kGC>;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hh = lane >> 5, l32 = lane & 31;
+    const int h = blockIdx.x % a.H, k = blockIdx.x / a.H;
+    const int lb = a.level_ptr[level], le = a.level_ptr[level + 1];
+    if (lb + k >= le) return;
+    const int seg = a.level_segs[lb + k];
+    const int4 sm = a.seg_meta[seg];
+    const int r = sm.x, c_first = sm.y, n_ch = sm.z, parent = sm.w;
+    const int col = 32 * wave + l32;                   // this lane's state / value column
+
+    // State columns 32 wave .. +31, rows in 4 blocks of 32 (accumulator layout).
+    floatx16 Hs[4];
+    if (parent < 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Hs[j] = zero16();
+    } else {
+        const float *src = a.states + (int64_t(parent) * a.H + h) * kGD * kGD;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Hs[j][i] = src[(32 * j + 8 * (i / 4) + 4 * hh + (i % 4)) * kGD + col];
+    }
+
+    const int stride = a.H * kGD * 2;
+    const uint32_t lds0 = lds_base(smem);
+    const float *Gs = reinterpret_cast<const float *>(smem + ScanLds::G_OFF);
+    for (int ci = 0; ci < n_ch; ++ci) {
+        const int c = c_first + ci;
+        const int4 cm = a.chunk_meta[c];
+        const int t0 = cm.y, n = cm.z;
+        const int64_t tok0 = int64_t(r) * a.T + t0;
+        const int64_t hoff = (tok0 * a.H + h) * kGD * 2;
+        const int64_t chh = int64_t(c) * a.H + h;
+        __syncthreads();                               // the previous chunk's reads are done
+        copy_tile<kGD>(reinterpret_cast<const char *>(a.qh) + hoff, n, stride, lds0 + ScanLds::Q_OFF, kGC, wave, 4, lane);
+        copy_tile<kGD>(reinterpret_cast<const char *>(a.kh) + hoff, n, stride, lds0 + ScanLds::K_OFF, kGC, wave, 4, lane);
+        copy_tile<kGD>(reinterpret_cast<const char *>(a.Yn) + chh * kGC * kGD * 2, kGC, kGD * 2,
+                       lds0 + ScanLds::Y_OFF, kGC, wave, 4, lane);
+        copy_tile<kGC>(reinterpret_cast<const char *>(a.P) + chh * kGC * kGC * 2, kGC, kGC * 2,
+                       lds0 + ScanLds::P_OFF, kGC, wave, 4, lane);
+        if (wave == 0) {
+            float *Gw = reinterpret_cast<float *>(smem + ScanLds::G_OFF);
+            Gw[lane] = a.G[chh * kGC + lane];
+        }
+        // W = U - Y H starts from U (fp32, accumulator layout).
+        floatx16 W[2];
+        const float *Ug = a.U + chh * kGC * kGD + col;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) W[tb][i] = Ug[(32 * tb + 8 * (i / 4) + 4 * hh + (i % 4)) * kGD];
+        wait_loads();
+        __syncthreads();
+
+        const char *Qt = smem + ScanLds::Q_OFF, *Kt = smem + ScanLds::K_OFF;
+        const char *Yt = smem + ScanLds::Y_OFF, *Pt = smem + ScanLds::P_OFF;
+        floatx16 O[2];
+        {
+            // W = U - Y H and Q H, H as bf16 B operands
+            bf16x8_t hb[4][2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) hb[j][ks] = acc_frag(Hs[j], ks);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                O[tb] = zero16();
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        W[tb] = mfma(T128::perm_frag(Yt, 32 * tb, lane, 2 * j + ks), hb[j][ks], W[tb]);
+                        O[tb] = mfma(T128::perm_frag(Qt, 32 * tb, lane, 2 * j + ks), hb[j][ks], O[tb]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // O = diag(gamma) Q H + P W;  accumulator rows t = 32 tb + 8(i/4) + 4hh + i%4
+        {
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    O[tb][i] *= __builtin_amdgcn_exp2f(Gs[32 * tb + 8 * (i / 4) + 4 * hh + (i % 4)] * kGLog2e);
+            bf16x8_t wb[2][2];
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) wb[sb][ks] = acc_frag(W[sb], ks);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        O[tb] = mfma(T64::perm_frag(Pt, 32 * tb, lane, 2 * sb + ks), wb[sb][ks], O[tb]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+            __bf16 *og = a.o + (tok0 * a.H + h) * kGD + col;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = 32 * tb + 8 * (i / 4) + 4 * hh + (i % 4);
+                    if (t < n) og[int64_t(t) * a.H * kGD] = static_cast<__bf16>(O[tb][i]);
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // H <- gamma_C H + K^T diag(gamma_C / gamma) W
+        {
+            const float gC = Gs[kGC - 1];
+            bf16x8_t wg[2][2];
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    W[tb][i] *= __builtin_amdgcn_exp2f((gC - Gs[32 * tb + 8 * (i / 4) + 4 * hh + (i % 4)]) * kGLog2e);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) wg[tb][ks] = acc_frag(W[tb], ks);
+            }
+            const float dC = __builtin_amdgcn_exp2f(gC * kGLog2e);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) Hs[j][i] *= dC;
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        Hs[j] = mfma(T128::tr_frag(Kt, 32 * tb, lane, ks, j), wg[tb][ks], Hs[j]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
+        }
+    }
+    float *dst = a.states + (int64_t(seg) * a.H + h) * kGD * kGD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dst[(32 * j + 8 * (i / 4) + 4 * hh + (i % 4)) * kGD + col] = Hs[j][i];
+}
+
+}  // namespace
+
+hipError_t launch_gdn(const GdnShape &sh, const GdnLayout &L, char *gws, const void *xq, const void *xk,
+                      const void *xv, const float *conv_w, const float *g, const float *beta, void *o,
+                      hipStream_t s) {
+    GdnArgs a;
+    a.R = sh.R; a.T = sh.T; a.H = sh.H; a.n_chunks = L.n_chunks;
+    a.chunk_meta = reinterpret_cast<const int4 *>(gws + L.chunk_meta);
+    a.seg_meta = reinterpret_cast<const int4 *>(gws + L.seg_meta);
+    a.level_ptr = reinterpret_cast<const int32_t *>(gws + L.level_ptr);
+    a.level_segs = reinterpret_cast<const int32_t *>(gws + L.level_segs);
+    a.qh = reinterpret_cast<const __bf16 *>(gws + L.qh);
+    a.kh = reinterpret_cast<const __bf16 *>(gws + L.kh);
+    a.vh = reinterpret_cast<const __bf16 *>(gws + L.vh);
+    a.g = g; a.beta = beta;
+    a.U = reinterpret_cast<float *>(gws + L.U);
+    a.Yn = reinterpret_cast<__bf16 *>(gws + L.Yn);
+    a.P = reinterpret_cast<__bf16 *>(gws + L.P);
+    a.G = reinterpret_cast<float *>(gws + L.G);
+    a.states = reinterpret_cast<float *>(gws + L.states);
+    a.o = static_cast<__bf16 *>(o);
+    const int64_t n_tok = int64_t(sh.R) * sh.T;
+    if (n_tok > INT32_MAX || int64_t(L.n_chunks) * sh.H > INT32_MAX) return hipErrorInvalidValue;
+    if (n_tok > 0)
+        gdn_conv<<<int(n_tok), 256, 0, s>>>(int32_t(n_tok), sh.H, reinterpret_cast<const int32_t *>(gws + L.pi),
+                                            static_cast<const __bf16 *>(xq), static_cast<const __bf16 *>(xk),
+                                            static_cast<const __bf16 *>(xv), conv_w, sh.eps,
+                                            reinterpret_cast<__bf16 *>(gws + L.qh), reinterpret_cast<__bf16 *>(gws + L.kh),
+                                            reinterpret_cast<__bf16 *>(gws + L.vh));
+    if (L.n_chunks > 0) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_prep),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
+        if (e != hipSuccess) return e;
+        gdn_prep<<<L.n_chunks * sh.H, 256, PrepLds::SIZE, s>>>(a);
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                ScanLds::SIZE);
+        if (e != hipSuccess) return e;
+        for (int32_t lev = 0; lev < L.n_levels; ++lev)
+            gdn_scan<<<L.max_level_segs * sh.H, 256, ScanLds::SIZE, s>>>(a, lev);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace treeattn

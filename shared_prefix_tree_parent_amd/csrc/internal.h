@@ -86,9 +86,56 @@ inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq) {
     return b;
 }
 
+// Gated delta rule workspace (caller-allocated; metadata written by tree_gdn_plan).
+struct GdnShape {
+    int32_t R, T, H;
+    float eps;
+};
+struct GdnLayout {
+    size_t pi = 0;           // int32[R*T]: global token parent, -1 at a root's first token, -2 pads
+    size_t chunk_meta = 0;   // int4[n_chunks]: (row, first token, tokens, segment)
+    size_t seg_meta = 0;     // int4[n_segs]: (row, first chunk, chunks, parent segment or -1)
+    size_t level_ptr = 0;    // int32[n_levels + 1] (room for n_segs + 1): segments per depth, CSR
+    size_t level_segs = 0;   // int32[n_segs]: segments by depth
+    size_t qh = 0, kh = 0, vh = 0;   // bf16[R*T*H*128] each: conv + norm outputs
+    size_t U = 0;            // f32[n_chunks*H*64*128]
+    size_t Yn = 0;           // bf16[n_chunks*H*64*128]
+    size_t P = 0;            // bf16[n_chunks*H*64*64]
+    size_t G = 0;            // f32[n_chunks*H*64]
+    size_t states = 0;       // f32[n_segs*H*128*128]: final state of every segment
+    size_t total = 0;
+    int32_t n_chunks = 0, n_segs = 0, n_levels = 0, max_level_segs = 0;
+};
+inline GdnLayout make_gdn_layout(int32_t R, int32_t T, int32_t H, int32_t n_chunks, int32_t n_segs) {
+    GdnLayout g;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    const size_t tok = size_t(R) * T;
+    g.pi = take(tok * 4);
+    g.chunk_meta = take(size_t(n_chunks) * 16);
+    g.seg_meta = take(size_t(n_segs) * 16);
+    g.level_ptr = take((size_t(n_segs) + 1) * 4);
+    g.level_segs = take(size_t(n_segs) * 4);
+    g.qh = take(tok * H * 128 * 2);
+    g.kh = take(tok * H * 128 * 2);
+    g.vh = take(tok * H * 128 * 2);
+    g.U = take(size_t(n_chunks) * H * 64 * 128 * 4);
+    g.Yn = take(size_t(n_chunks) * H * 64 * 128 * 2);
+    g.P = take(size_t(n_chunks) * H * 64 * 64 * 2);
+    g.G = take(size_t(n_chunks) * H * 64 * 4);
+    g.states = take(size_t(n_segs) * H * 128 * 128 * 4);
+    g.total = off;
+    g.n_chunks = n_chunks;
+    g.n_segs = n_segs;
+    return g;
+}
+
 // Launchers (defined in classify.hip / attn_fwd.hip / attn_bwd.hip).  Return hipSuccess or the
 // first error.
 hipError_t launch_plan(const tree_attn_desc &d, const WsLayout &w, char *ws, hipStream_t s);
+hipError_t launch_gdn(const GdnShape &sh, const GdnLayout &L, char *gws, const void *xq, const void *xk,
+                      const void *xv, const float *conv_w, const float *g, const float *beta, void *o,
+                      hipStream_t s);
 hipError_t launch_rope(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
                        const int32_t *pos_ids, float theta, int32_t inverse, void *q, void *k, hipStream_t s);
 hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, const char *ws, char *bws, hipStream_t s);
