@@ -26,6 +26,9 @@
 //       W = U - Y H,   O = diag(gamma) Q H + P W,   H <- gamma_C H + K^T diag(gamma_C/gamma) W
 //     with bf16 operands (H rounded for the products only) and fp32 accumulation; the
 //     segment's final H is stored for its children.
+#include <type_traits>
+#include <utility>
+
 #include "internal.h"
 #include "tile_ops.h"
 
@@ -41,73 +44,95 @@ constexpr float kGLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------------------------ gdn_conv
 //
-// One workgroup (256 threads) per token; a thread takes 8 consecutive channels of a tensor,
-// 16 threads one head (the L2 norm is a 16-lane sum).
+// One workgroup (256 threads) per block of kConvTok tokens; a thread takes 8 consecutive
+// channels of every tensor and keeps their conv weights in registers for the whole block; 16
+// threads cover a head (the L2 norm is a 16-lane sum).
+constexpr int kConvTok = 16;
+
 __global__ __launch_bounds__(256) void gdn_conv(int32_t n_tok, int32_t H, const int32_t *__restrict__ pi,
                                                 const __bf16 *__restrict__ xq, const __bf16 *__restrict__ xk,
                                                 const __bf16 *__restrict__ xv, const float *__restrict__ w,
                                                 float eps, __bf16 *__restrict__ qh, __bf16 *__restrict__ kh,
                                                 __bf16 *__restrict__ vh) {
-    const int64_t tok = blockIdx.x;
-    if (tok >= n_tok) return;
-    const int p = pi[tok];
-    if (p < -1) return;                                   // pad: never read downstream
-    // ch[j] = pi^j(tok) (global token indices; -1 past a root's first token)
-    int64_t ch[kGW];
-    ch[0] = tok;
-    int64_t nxt = p;
-    for (int j = 1; j < kGW; ++j) {
-        ch[j] = nxt;
-        nxt = nxt >= 0 ? pi[nxt] : -1;
-    }
     const int C = H * kGD;                                 // channels per tensor
     const float qscale = 0.08838834764831845f;             // 1 / sqrt(128)
+    const int64_t tok_begin = int64_t(blockIdx.x) * kConvTok;
     for (int c8 = threadIdx.x * 8; c8 < C; c8 += blockDim.x * 8) {
+        // weights of this thread's 8 channels, 3 tensors x 4 taps: [tensor][channel][tap]
+        float wr[3][8][kGW];
 #pragma unroll
-        for (int tsr = 0; tsr < 3; ++tsr) {
-            const __bf16 *x = tsr == 0 ? xq : (tsr == 1 ? xk : xv);
-            const float *wt = w + (int64_t(tsr) * C + c8) * kGW;
-            float y[8];
+        for (int tsr = 0; tsr < 3; ++tsr)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = 0.f;
+            for (int e = 0; e < 8; ++e) {
+                const float4 w4 = *reinterpret_cast<const float4 *>(w + ((int64_t(tsr) * C + c8 + e) * kGW));
+                wr[tsr][e][0] = w4.x; wr[tsr][e][1] = w4.y; wr[tsr][e][2] = w4.z; wr[tsr][e][3] = w4.w;
+            }
+        for (int k = 0; k < kConvTok; ++k) {
+            const int64_t tok = tok_begin + k;
+            if (tok >= n_tok) break;
+            const int p = __builtin_amdgcn_readfirstlane(pi[tok]);
+            if (p < -1) continue;                          // pad: never read downstream
+            // ch[j] = pi^j(tok) (global token indices; -1 past a root's first token)
+            int64_t ch[kGW];
+            ch[0] = tok;
+            int64_t nxt = p;
 #pragma unroll
-            for (int j = 0; j < kGW; ++j) {
-                if (ch[j] < 0) break;
-                const bf16x8_t xv8 = *reinterpret_cast<const bf16x8_t *>(x + ch[j] * C + c8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = fmaf(wt[e * kGW + (kGW - 1 - j)], float(xv8[e]), y[e]);
+            for (int j = 1; j < kGW; ++j) {
+                ch[j] = nxt;
+                nxt = nxt >= 0 ? __builtin_amdgcn_readfirstlane(pi[nxt]) : -1;
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = y[e] / (1.f + __expf(-y[e]));
-            float scale = 1.f;
-            if (tsr < 2) {
-                float ss = 0.f;
+            for (int tsr = 0; tsr < 3; ++tsr) {
+                const __bf16 *x = tsr == 0 ? xq : (tsr == 1 ? xk : xv);
+                float y[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+                for (int e = 0; e < 8; ++e) y[e] = 0.f;
 #pragma unroll
-                for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 16);
-                scale = rsqrtf(ss + eps) * (tsr == 0 ? qscale : 1.f);
+                for (int j = 0; j < kGW; ++j) {
+                    if (ch[j] < 0) break;
+                    const bf16x8_t xv8 = *reinterpret_cast<const bf16x8_t *>(x + ch[j] * C + c8);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] = fmaf(wr[tsr][e][kGW - 1 - j], float(xv8[e]), y[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = y[e] * __builtin_amdgcn_rcpf(1.f + __expf(-y[e]));
+                float scale = 1.f;
+                if (tsr < 2) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
+#pragma unroll
+                    for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 16);
+                    scale = rsqrtf(ss + eps) * (tsr == 0 ? qscale : 1.f);
+                }
+                bf16x8_t o8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o8[e] = static_cast<__bf16>(y[e] * scale);
+                __bf16 *out = tsr == 0 ? qh : (tsr == 1 ? kh : vh);
+                *reinterpret_cast<bf16x8_t *>(out + tok * C + c8) = o8;
             }
-            bf16x8_t o8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o8[e] = static_cast<__bf16>(y[e] * scale);
-            __bf16 *out = tsr == 0 ? qh : (tsr == 1 ? kh : vh);
-            *reinterpret_cast<bf16x8_t *>(out + tok * C + c8) = o8;
         }
     }
 }
 
 // ------------------------------------------------------------------------------ gdn_prep
 //
-// LDS: Q, K, V chunk tiles (64 x 128 bf16, swizzled), A (64 x 64 fp32), the solve's columns
-// X (64 x 256 fp32: [beta V | beta gamma K] -> [U | Y]), G and beta (64 fp32 each).
+// LDS: Q, K, V chunk tiles (64 x 128 bf16, swizzled), A (64 x 64 fp32), G and beta (64 fp32).
 struct PrepLds {
     static constexpr int TILE = kGC * kGD * 2;
     static constexpr int Q_OFF = 0, K_OFF = TILE, V_OFF = 2 * TILE, A_OFF = 3 * TILE;
-    static constexpr int X_OFF = A_OFF + kGC * kGC * 4;
-    static constexpr int G_OFF = X_OFF + kGC * 256 * 4, GB_OFF = G_OFF + kGC * 4;
+    static constexpr int G_OFF = A_OFF + kGC * kGC * 4, GB_OFF = G_OFF + kGC * 4;
     static constexpr int SIZE = GB_OFF + kGC * 4;
 };
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 struct GdnArgs {
     int32_t R, T, H, n_chunks;
@@ -176,39 +201,41 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
     for (int i = 0; i < 16; ++i) {
         const int t = 32 * bt + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
         const float dec = __builtin_amdgcn_exp2f((Gs[t] - Gs[s]) * kGLog2e);   // gamma_t / gamma_s for s <= t
-        As[t * kGC + s] = s < t ? Bs[t] * dec * kk[i] : 0.f;
+        As[s * kGC + t] = s < t ? Bs[t] * dec * kk[i] : 0.f;         // transposed: A^T[s][t]
         Pout[t * kGC + s] = static_cast<__bf16>(s <= t ? dec * qk[i] : 0.f);
     }
     __syncthreads();
 
-    // Forward substitution, one thread per column of [beta V | beta gamma K]:
-    //   x_t = rhs_t - sum_{s < t} A_ts x_s,  the column kept in LDS (X[t][column]).
+    // Forward substitution, one thread per column of [beta V | beta gamma K], the column in
+    // registers: x starts as the right-hand side; once x_s is final every later row takes
+    // its term  x_t -= A_ts x_s  (A^T rows read four at a time).
     {
         const int col = tid & 127;
         const bool isk = tid >= 128;
         const char *src = isk ? Kt : smem + PrepLds::V_OFF;
-        float *X = reinterpret_cast<float *>(smem + PrepLds::X_OFF) + tid;
+        float x[kGC];
+#pragma unroll
         for (int t = 0; t < kGC; ++t) {
             const float gam = isk ? __builtin_amdgcn_exp2f(Gs[t] * kGLog2e) : 1.f;
-            float acc = Bs[t] * gam * T128::at(src, t, col);
-            const float *Arow = As + t * kGC;
-            int s4 = 0;
-            for (; s4 + 4 <= t; s4 += 4) {
-                const float4 a4 = *reinterpret_cast<const float4 *>(Arow + s4);
-                acc = fmaf(-a4.x, X[(s4 + 0) * 256], acc);
-                acc = fmaf(-a4.y, X[(s4 + 1) * 256], acc);
-                acc = fmaf(-a4.z, X[(s4 + 2) * 256], acc);
-                acc = fmaf(-a4.w, X[(s4 + 3) * 256], acc);
-            }
-            for (; s4 < t; ++s4) acc = fmaf(-Arow[s4], X[s4 * 256], acc);
-            X[t * 256] = acc;
+            x[t] = Bs[t] * gam * T128::at(src, t, col);
         }
+        static_for<kGC - 1>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int s0 = decltype(sc)::value;
+            const float *Acol = As + s0 * kGC;             // A^T row s0: A_ts for every t
+            static_for<kGC - 1 - s0>([&](auto tc) __attribute__((always_inline)) {
+                constexpr int t = s0 + 1 + decltype(tc)::value;
+                x[t] = fmaf(-Acol[t], x[s0], x[t]);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
         if (!isk) {
             float *Uo = a.U + (int64_t(c) * a.H + h) * kGC * kGD + col;
-            for (int t = 0; t < kGC; ++t) Uo[t * kGD] = X[t * 256];
+#pragma unroll
+            for (int t = 0; t < kGC; ++t) Uo[t * kGD] = x[t];
         } else {
             __bf16 *Yo = a.Yn + (int64_t(c) * a.H + h) * kGC * kGD + col;
-            for (int t = 0; t < kGC; ++t) Yo[t * kGD] = static_cast<__bf16>(-X[t * 256]);
+#pragma unroll
+            for (int t = 0; t < kGC; ++t) Yo[t * kGD] = static_cast<__bf16>(-x[t]);
         }
     }
 }
@@ -393,7 +420,7 @@ hipError_t launch_gdn(const GdnShape &sh, const GdnLayout &L, char *gws, const v
     const int64_t n_tok = int64_t(sh.R) * sh.T;
     if (n_tok > INT32_MAX || int64_t(L.n_chunks) * sh.H > INT32_MAX) return hipErrorInvalidValue;
     if (n_tok > 0)
-        gdn_conv<<<int(n_tok), 256, 0, s>>>(int32_t(n_tok), sh.H, reinterpret_cast<const int32_t *>(gws + L.pi),
+        gdn_conv<<<int((n_tok + kConvTok - 1) / kConvTok), 256, 0, s>>>(int32_t(n_tok), sh.H, reinterpret_cast<const int32_t *>(gws + L.pi),
                                             static_cast<const __bf16 *>(xq), static_cast<const __bf16 *>(xk),
                                             static_cast<const __bf16 *>(xv), conv_w, sh.eps,
                                             reinterpret_cast<__bf16 *>(gws + L.qh), reinterpret_cast<__bf16 *>(gws + L.kh),
