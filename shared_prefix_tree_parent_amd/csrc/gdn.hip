@@ -241,11 +241,17 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
 }
 
 // ------------------------------------------------------------------------------ gdn_scan
+//
+// LDS: two stages of chunk tiles (Q, K, -Y: 64 x 128 bf16; P: 64 x 64 bf16; G: 64 fp32), the
+// next chunk's stage copied while the current one is used, and one buffer for U (64 x 128
+// fp32), refilled with the next chunk's U once every wave has read the current one.
 struct ScanLds {
     static constexpr int TILE = kGC * kGD * 2;                  // 64 x 128 bf16
     static constexpr int Q_OFF = 0, K_OFF = TILE, Y_OFF = 2 * TILE, P_OFF = 3 * TILE;
     static constexpr int G_OFF = P_OFF + kGC * kGC * 2;
-    static constexpr int SIZE = G_OFF + kGC * 4;
+    static constexpr int STAGE = G_OFF + kGC * 4;
+    static constexpr int U_OFF = 2 * STAGE;
+    static constexpr int SIZE = U_OFF + kGC * kGD * 4;
 };
 
 __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
@@ -278,37 +284,54 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
 
     const int stride = a.H * kGD * 2;
     const uint32_t lds0 = lds_base(smem);
-    const float *Gs = reinterpret_cast<const float *>(smem + ScanLds::G_OFF);
-    for (int ci = 0; ci < n_ch; ++ci) {
+    auto issue_stage = [&](int ci) __attribute__((always_inline)) {
         const int c = c_first + ci;
         const int4 cm = a.chunk_meta[c];
-        const int t0 = cm.y, n = cm.z;
-        const int64_t tok0 = int64_t(r) * a.T + t0;
-        const int64_t hoff = (tok0 * a.H + h) * kGD * 2;
+        const int64_t hoff = ((int64_t(r) * a.T + cm.y) * a.H + h) * kGD * 2;
         const int64_t chh = int64_t(c) * a.H + h;
-        __syncthreads();                               // the previous chunk's reads are done
-        copy_tile<kGD>(reinterpret_cast<const char *>(a.qh) + hoff, n, stride, lds0 + ScanLds::Q_OFF, kGC, wave, 4, lane);
-        copy_tile<kGD>(reinterpret_cast<const char *>(a.kh) + hoff, n, stride, lds0 + ScanLds::K_OFF, kGC, wave, 4, lane);
+        const uint32_t base = lds0 + (ci & 1) * ScanLds::STAGE;
+        copy_tile<kGD>(reinterpret_cast<const char *>(a.qh) + hoff, cm.z, stride, base + ScanLds::Q_OFF, kGC, wave, 4, lane);
+        copy_tile<kGD>(reinterpret_cast<const char *>(a.kh) + hoff, cm.z, stride, base + ScanLds::K_OFF, kGC, wave, 4, lane);
         copy_tile<kGD>(reinterpret_cast<const char *>(a.Yn) + chh * kGC * kGD * 2, kGC, kGD * 2,
-                       lds0 + ScanLds::Y_OFF, kGC, wave, 4, lane);
+                       base + ScanLds::Y_OFF, kGC, wave, 4, lane);
         copy_tile<kGC>(reinterpret_cast<const char *>(a.P) + chh * kGC * kGC * 2, kGC, kGC * 2,
-                       lds0 + ScanLds::P_OFF, kGC, wave, 4, lane);
-        if (wave == 0) {
-            float *Gw = reinterpret_cast<float *>(smem + ScanLds::G_OFF);
-            Gw[lane] = a.G[chh * kGC + lane];
-        }
-        // W = U - Y H starts from U (fp32, accumulator layout).
-        floatx16 W[2];
-        const float *Ug = a.U + chh * kGC * kGD + col;
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) W[tb][i] = Ug[(32 * tb + 8 * (i / 4) + 4 * hh + (i % 4)) * kGD];
+                       base + ScanLds::P_OFF, kGC, wave, 4, lane);
+        if (wave == 0) buf_to_lds4(buf_rsrc(a.G + chh * kGC, kGC * 4), base + ScanLds::G_OFF, lane * 4);
+    };
+    auto issue_u = [&](int ci) __attribute__((always_inline)) {
+        const int64_t chh = int64_t(c_first + ci) * a.H + h;
+        const int32x4_t rs = buf_rsrc(a.U + chh * kGC * kGD, kGC * kGD * 4);
+        for (int blk = wave; blk < kGC * kGD * 4 / 1024; blk += 4)
+            buf_to_lds16(rs, lds0 + ScanLds::U_OFF + blk * 1024, blk * 1024 + lane * 16);
+    };
+
+    issue_stage(0);
+    issue_u(0);
+    for (int ci = 0; ci < n_ch; ++ci) {
+        // Chunk ci's stage and U have landed for every wave; every wave is done with chunk
+        // ci-1, whose stage buffer chunk ci+1 takes.
         wait_loads();
         __syncthreads();
+        if (ci + 1 < n_ch) issue_stage(ci + 1);
+        const int4 cm = a.chunk_meta[c_first + ci];
+        const int t0 = cm.y, n = cm.z;
+        const int64_t tok0 = int64_t(r) * a.T + t0;
+        const char *st = smem + (ci & 1) * ScanLds::STAGE;
+        const char *Qt = st + ScanLds::Q_OFF, *Kt = st + ScanLds::K_OFF;
+        const char *Yt = st + ScanLds::Y_OFF, *Pt = st + ScanLds::P_OFF;
+        const float *Gs = reinterpret_cast<const float *>(st + ScanLds::G_OFF);
+        // W = U - Y H starts from U (accumulator layout); then U's buffer takes chunk ci+1.
+        floatx16 W[2];
+        {
+            const float *Us = reinterpret_cast<const float *>(smem + ScanLds::U_OFF) + col;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) W[tb][i] = Us[(32 * tb + 8 * (i / 4) + 4 * hh + (i % 4)) * kGD];
+        }
+        __syncthreads();
+        if (ci + 1 < n_ch) issue_u(ci + 1);
 
-        const char *Qt = smem + ScanLds::Q_OFF, *Kt = smem + ScanLds::K_OFF;
-        const char *Yt = smem + ScanLds::Y_OFF, *Pt = smem + ScanLds::P_OFF;
         floatx16 O[2];
         {
             // W = U - Y H and Q H, H as bf16 B operands

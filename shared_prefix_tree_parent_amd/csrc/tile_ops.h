@@ -10,7 +10,7 @@
 // [n = l%32]; accumulator element i of lane l is C[8(i/4) + 4(l/32) + i%4][l%32].  acc_frag
 // turns accumulator registers 8 ks .. 8 ks + 7 into a B operand whose k slots hold the rows
 // 16 ks + 4(l/32) + {0..3} and 16 ks + 8 + 4(l/32) + {0..3}; an A operand paired with it must
-// supply the same k order (perm_at / Tile::tr_at).
+// supply the same k order (Tile::perm_frag / Tile::tr_frag).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -103,6 +103,10 @@ __device__ __forceinline__ int32x4_t buf_rsrc(const void *base, uint32_t num_rec
 }
 __device__ __forceinline__ void buf_to_lds16(int32x4_t r, uint32_t lds, int voff) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %0, 0 offen lds"
+                 :: "s"(r), "s"(lds), "v"(voff) : "memory", "m0");
+}
+__device__ __forceinline__ void buf_to_lds4(int32x4_t r, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %0, 0 offen lds"
                  :: "s"(r), "s"(lds), "v"(voff) : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_base(const char *p) {
