@@ -19,7 +19,10 @@
 //     replayed.  With G the cumulative log-decay inside the chunk, gamma = exp(G):
 //       A_ts = b_t gamma_t/gamma_s k_t.k_s (s < t),  P_ts = gamma_t/gamma_s q_t.k_s (s <= t),
 //       U = (I + A)^-1 diag(b) V,  Y = (I + A)^-1 diag(b gamma) K      (forward substitution)
-//     Gram and QK^T on MFMA; the solves in fp32 (one thread per column of [V | K]).
+//     Gram and QK^T on MFMA; the solves in fp32 (one thread per column of [V | K]).  Prep
+//     also writes the decay factors gamma_t and gamma_C / gamma_t, and U in the order the
+//     scan's accumulators hold it, so the scan computes no exponential and reads U as whole
+//     16-byte lanes.
 //   * gdn_scan, once per tree depth: one workgroup per (segment of that depth, head), 4 waves,
 //     each holding 32 columns of the 128 x 128 state H in fp32 MFMA accumulators, from the
 //     parent's final state (zero at roots); per chunk
@@ -141,10 +144,10 @@ struct GdnArgs {
     const int32_t *level_ptr, *level_segs;
     const __bf16 *qh, *kh, *vh;
     const float *g, *beta;
-    float *U;                    // [n_chunks, H, 64, 128]
+    float *U;                    // [n_chunks, H, 64 x 128] in scan accumulator order (below)
     __bf16 *Yn;                  // [n_chunks, H, 64, 128]  (-Y)
     __bf16 *P;                   // [n_chunks, H, 64, 64]
-    float *G;                    // [n_chunks, H, 64]
+    float *F;                    // [n_chunks, H, 128]: gamma_t (t < 64), gamma_C / gamma_t
     float *states;               // [n_segs, H, 128, 128]
     __bf16 *o;                   // [R, T, H, 128]
 };
@@ -179,7 +182,11 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
         }
         Gs[lane] = gv;
         Bs[lane] = bv;
-        a.G[(int64_t(c) * a.H + h) * kGC + lane] = gv;
+        // decay factors for the scan: gamma_t and gamma_C / gamma_t (both <= 1)
+        const float gC = __shfl(gv, kGC - 1, 64);
+        float *Fo = a.F + (int64_t(c) * a.H + h) * 2 * kGC;
+        Fo[lane] = __builtin_amdgcn_exp2f(gv * kGLog2e);
+        Fo[kGC + lane] = __builtin_amdgcn_exp2f((gC - gv) * kGLog2e);
     }
     wait_loads();
     __syncthreads();
@@ -229,9 +236,14 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         });
         if (!isk) {
-            float *Uo = a.U + (int64_t(c) * a.H + h) * kGC * kGD + col;
+            // accumulator order of the scan: element (t, col) sits with scan wave col/32, lane
+            // 32 ((t/4) % 2) + col % 32, register 4 ((t % 32) / 8) + t % 4 of row block t/32;
+            // four consecutive t are one 16-byte store.
+            float4 *Uo = reinterpret_cast<float4 *>(a.U + (int64_t(c) * a.H + h) * kGC * kGD) +
+                         (col >> 5) * (kGC * 32 / 4) + (col & 31);
 #pragma unroll
-            for (int t = 0; t < kGC; ++t) Uo[t * kGD] = x[t];
+            for (int k4 = 0; k4 < kGC / 4; ++k4)
+                Uo[(k4 >> 1) * 64 + (k4 & 1) * 32] = make_float4(x[4 * k4], x[4 * k4 + 1], x[4 * k4 + 2], x[4 * k4 + 3]);
         } else {
             __bf16 *Yo = a.Yn + (int64_t(c) * a.H + h) * kGC * kGD + col;
 #pragma unroll
@@ -242,16 +254,17 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
 
 // ------------------------------------------------------------------------------ gdn_scan
 //
-// LDS: two stages of chunk tiles (Q, K, -Y: 64 x 128 bf16; P: 64 x 64 bf16; G: 64 fp32), the
-// next chunk's stage copied while the current one is used, and one buffer for U (64 x 128
-// fp32), refilled with the next chunk's U once every wave has read the current one.
+// LDS: two stages of chunk tiles (Q, K, -Y: 64 x 128 bf16; P: 64 x 64 bf16; the decay
+// factors: 128 fp32), the next chunk's stage copied while the current one is used.  U goes
+// straight from HBM into registers (prep wrote it in accumulator order), one chunk ahead.
+// Nothing in the chunk loop waits on a scalar load: chunk ci of a segment starts at the
+// segment's first token + 64 ci.
 struct ScanLds {
     static constexpr int TILE = kGC * kGD * 2;                  // 64 x 128 bf16
     static constexpr int Q_OFF = 0, K_OFF = TILE, Y_OFF = 2 * TILE, P_OFF = 3 * TILE;
-    static constexpr int G_OFF = P_OFF + kGC * kGC * 2;
-    static constexpr int STAGE = G_OFF + kGC * 4;
-    static constexpr int U_OFF = 2 * STAGE;
-    static constexpr int SIZE = U_OFF + kGC * kGD * 4;
+    static constexpr int F_OFF = P_OFF + kGC * kGC * 2;
+    static constexpr int STAGE = F_OFF + 2 * kGC * 4;
+    static constexpr int SIZE = 2 * STAGE;
 };
 
 __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
@@ -267,6 +280,8 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
     const int seg = a.level_segs[lb + k];
     const int4 sm = a.seg_meta[seg];
     const int r = sm.x, c_first = sm.y, n_ch = sm.z, parent = sm.w;
+    const int seg_t0 = n_ch > 0 ? a.chunk_meta[c_first].y : 0;
+    const int last_n = n_ch > 0 ? a.chunk_meta[c_first + n_ch - 1].z : 0;
     const int col = 32 * wave + l32;                   // this lane's state / value column
 
     // State columns 32 wave .. +31, rows in 4 blocks of 32 (accumulator layout).
@@ -284,97 +299,159 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
 
     const int stride = a.H * kGD * 2;
     const uint32_t lds0 = lds_base(smem);
-    auto issue_stage = [&](int ci) __attribute__((always_inline)) {
-        const int c = c_first + ci;
-        const int4 cm = a.chunk_meta[c];
-        const int64_t hoff = ((int64_t(r) * a.T + cm.y) * a.H + h) * kGD * 2;
-        const int64_t chh = int64_t(c) * a.H + h;
-        const uint32_t base = lds0 + (ci & 1) * ScanLds::STAGE;
-        copy_tile<kGD>(reinterpret_cast<const char *>(a.qh) + hoff, cm.z, stride, base + ScanLds::Q_OFF, kGC, wave, 4, lane);
-        copy_tile<kGD>(reinterpret_cast<const char *>(a.kh) + hoff, cm.z, stride, base + ScanLds::K_OFF, kGC, wave, 4, lane);
-        copy_tile<kGD>(reinterpret_cast<const char *>(a.Yn) + chh * kGC * kGD * 2, kGC, kGD * 2,
-                       base + ScanLds::Y_OFF, kGC, wave, 4, lane);
-        copy_tile<kGC>(reinterpret_cast<const char *>(a.P) + chh * kGC * kGC * 2, kGC, kGC * 2,
-                       base + ScanLds::P_OFF, kGC, wave, 4, lane);
-        if (wave == 0) buf_to_lds4(buf_rsrc(a.G + chh * kGC, kGC * 4), base + ScanLds::G_OFF, lane * 4);
+    // Chunk ci's stage is copied in 1 KB jobs that the chunk before spreads over its MFMA steps.
+    // Per wave: jobs 0-3 Q, 4-7 K, 8-11 -Y, 12-13 P, 14 the decay factors (waves 0 and 1).
+    struct StageSrc {
+        int32x4_t q, k, y, p, f;
+        uint32_t base;
     };
-    auto issue_u = [&](int ci) __attribute__((always_inline)) {
+    auto stage_src = [&](int ci) __attribute__((always_inline)) {
+        StageSrc ss;
+        const int n = ci + 1 < n_ch ? kGC : last_n;
+        const int64_t hoff = ((int64_t(r) * a.T + seg_t0 + kGC * ci) * a.H + h) * kGD * 2;
         const int64_t chh = int64_t(c_first + ci) * a.H + h;
-        const int32x4_t rs = buf_rsrc(a.U + chh * kGC * kGD, kGC * kGD * 4);
-        for (int blk = wave; blk < kGC * kGD * 4 / 1024; blk += 4)
-            buf_to_lds16(rs, lds0 + ScanLds::U_OFF + blk * 1024, blk * 1024 + lane * 16);
+        ss.q = tile_rsrc(reinterpret_cast<const char *>(a.qh) + hoff, n, stride);
+        ss.k = tile_rsrc(reinterpret_cast<const char *>(a.kh) + hoff, n, stride);
+        ss.y = tile_rsrc(reinterpret_cast<const char *>(a.Yn) + chh * kGC * kGD * 2, kGC, kGD * 2);
+        ss.p = tile_rsrc(reinterpret_cast<const char *>(a.P) + chh * kGC * kGC * 2, kGC, kGC * 2);
+        ss.f = buf_rsrc(a.F + chh * 2 * kGC + (wave & 1) * kGC, kGC * 4);
+        ss.base = lds0 + (ci & 1) * ScanLds::STAGE;
+        return ss;
+    };
+    auto stage_job = [&](const StageSrc &ss, int jb) __attribute__((always_inline)) {
+        if (jb < 4) copy_block<kGD>(ss.q, stride, ss.base + ScanLds::Q_OFF, wave + 4 * jb, lane);
+        else if (jb < 8) copy_block<kGD>(ss.k, stride, ss.base + ScanLds::K_OFF, wave + 4 * (jb - 4), lane);
+        else if (jb < 12) copy_block<kGD>(ss.y, kGD * 2, ss.base + ScanLds::Y_OFF, wave + 4 * (jb - 8), lane);
+        else if (jb < 14) copy_block<kGC>(ss.p, kGC * 2, ss.base + ScanLds::P_OFF, wave + 4 * (jb - 12), lane);
+        else if (jb == 14 && wave < 2) buf_to_lds4(ss.f, ss.base + ScanLds::F_OFF + wave * kGC * 4, lane * 4);
+    };
+    constexpr int kStageJobs = 15;
+    // U of chunk ci, this wave's 32 columns: un[tb][q] holds (t = 32 tb + 8 q + 4 hh + e, col).
+    float4 un[2][4];
+    auto u_src = [&](int ci) __attribute__((always_inline)) {
+        return reinterpret_cast<const float4 *>(a.U + (int64_t(c_first + ci) * a.H + h) * kGC * kGD) +
+               wave * (kGC * 32 / 4) + lane;
     };
 
-    issue_stage(0);
-    issue_u(0);
+    if (n_ch > 0) {
+        const StageSrc s0 = stage_src(0);
+#pragma unroll
+        for (int jb = 0; jb < kStageJobs; ++jb) stage_job(s0, jb);
+        const float4 *us = u_src(0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) un[u / 4][u % 4] = us[u * 64];
+    }
     for (int ci = 0; ci < n_ch; ++ci) {
         // Chunk ci's stage and U have landed for every wave; every wave is done with chunk
         // ci-1, whose stage buffer chunk ci+1 takes.
         wait_loads();
         __syncthreads();
-        if (ci + 1 < n_ch) issue_stage(ci + 1);
-        const int4 cm = a.chunk_meta[c_first + ci];
-        const int t0 = cm.y, n = cm.z;
-        const int64_t tok0 = int64_t(r) * a.T + t0;
+        const bool more = ci + 1 < n_ch;
+        const StageSrc nx = stage_src(ci + 1);
+        const float4 *nu = u_src(ci + 1);
+        const int n = more ? kGC : last_n;
+        const int64_t tok0 = int64_t(r) * a.T + seg_t0 + kGC * ci;
         const char *st = smem + (ci & 1) * ScanLds::STAGE;
         const char *Qt = st + ScanLds::Q_OFF, *Kt = st + ScanLds::K_OFF;
         const char *Yt = st + ScanLds::Y_OFF, *Pt = st + ScanLds::P_OFF;
-        const float *Gs = reinterpret_cast<const float *>(st + ScanLds::G_OFF);
-        // W = U - Y H starts from U (accumulator layout); then U's buffer takes chunk ci+1.
-        floatx16 W[2];
-        {
-            const float *Us = reinterpret_cast<const float *>(smem + ScanLds::U_OFF) + col;
+        const float *Fs = reinterpret_cast<const float *>(st + ScanLds::F_OFF);
+        floatx16 W[2], O[2];
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < 2; ++tb) {
+            O[tb] = zero16();
 #pragma unroll
-                for (int i = 0; i < 16; ++i) W[tb][i] = Us[(32 * tb + 8 * (i / 4) + 4 * hh + (i % 4)) * kGD];
+            for (int q = 0; q < 4; ++q) {
+                W[tb][4 * q + 0] = un[tb][q].x;
+                W[tb][4 * q + 1] = un[tb][q].y;
+                W[tb][4 * q + 2] = un[tb][q].z;
+                W[tb][4 * q + 3] = un[tb][q].w;
+            }
         }
-        __syncthreads();
-        if (ci + 1 < n_ch) issue_u(ci + 1);
 
-        floatx16 O[2];
+        // W = U - Y H and Q H, H as bf16 B operands; step s covers k rows 16 s .. 16 s + 15 for
+        // both row blocks, its A fragments read one step ahead; the next chunk's stage copies
+        // ride along two jobs a step.
         {
-            // W = U - Y H and Q H, H as bf16 B operands
-            bf16x8_t hb[4][2];
+            bf16x8_t hb[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) hb[j][ks] = acc_frag(Hs[j], ks);
+                for (int ks = 0; ks < 2; ++ks) hb[2 * j + ks] = acc_frag(Hs[j], ks);
+            bf16x8_t fy[2], fq[2];
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-                O[tb] = zero16();
+                fy[tb] = T128::perm_frag(Yt, 32 * tb, lane, 0);
+                fq[tb] = T128::perm_frag(Qt, 32 * tb, lane, 0);
+            }
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+            for (int s = 0; s < 8; ++s) {
+                bf16x8_t ny[2], nq[2];
+                if (s + 1 < 8) {
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        W[tb] = mfma(T128::perm_frag(Yt, 32 * tb, lane, 2 * j + ks), hb[j][ks], W[tb]);
-                        O[tb] = mfma(T128::perm_frag(Qt, 32 * tb, lane, 2 * j + ks), hb[j][ks], O[tb]);
-                        __builtin_amdgcn_sched_barrier(0);
+                    for (int tb = 0; tb < 2; ++tb) {
+                        ny[tb] = T128::perm_frag(Yt, 32 * tb, lane, s + 1);
+                        nq[tb] = T128::perm_frag(Qt, 32 * tb, lane, s + 1);
                     }
+                }
+                if (more) {
+                    if (2 * s < kStageJobs) stage_job(nx, 2 * s);
+                    if (2 * s + 1 < kStageJobs) stage_job(nx, 2 * s + 1);
+                }
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    W[tb] = mfma(fy[tb], hb[s], W[tb]);
+                    O[tb] = mfma(fq[tb], hb[s], O[tb]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (s + 1 < 8) {
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb) {
+                        fy[tb] = ny[tb];
+                        fq[tb] = nq[tb];
+                    }
+                }
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // O = diag(gamma) Q H + P W;  accumulator rows t = 32 tb + 8(i/4) + 4hh + i%4
+        // O = diag(gamma) Q H + P W;  accumulator rows t = 32 tb + 8 q + 4 hh + e.  The next
+        // chunk's U rides along two loads a step.
         {
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    O[tb][i] *= __builtin_amdgcn_exp2f(Gs[32 * tb + 8 * (i / 4) + 4 * hh + (i % 4)] * kGLog2e);
-            bf16x8_t wb[2][2];
+                for (int q = 0; q < 4; ++q) {
+                    const float4 gm = *reinterpret_cast<const float4 *>(Fs + 32 * tb + 8 * q + 4 * hh);
+                    O[tb][4 * q + 0] *= gm.x;
+                    O[tb][4 * q + 1] *= gm.y;
+                    O[tb][4 * q + 2] *= gm.z;
+                    O[tb][4 * q + 3] *= gm.w;
+                }
+            bf16x8_t wb[4];
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) wb[sb][ks] = acc_frag(W[sb], ks);
+                for (int ks = 0; ks < 2; ++ks) wb[2 * sb + ks] = acc_frag(W[sb], ks);
+            bf16x8_t fp[2];
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
+            for (int tb = 0; tb < 2; ++tb) fp[tb] = T64::perm_frag(Pt, 32 * tb, lane, 0);
 #pragma unroll
-                for (int sb = 0; sb < 2; ++sb)
+            for (int s = 0; s < 4; ++s) {
+                bf16x8_t np[2];
+                if (s + 1 < 4) {
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        O[tb] = mfma(T64::perm_frag(Pt, 32 * tb, lane, 2 * sb + ks), wb[sb][ks], O[tb]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
+                    for (int tb = 0; tb < 2; ++tb) np[tb] = T64::perm_frag(Pt, 32 * tb, lane, s + 1);
+                }
+                if (more) {
+                    un[(2 * s) / 4][(2 * s) % 4] = nu[(2 * s) * 64];
+                    un[(2 * s + 1) / 4][(2 * s + 1) % 4] = nu[(2 * s + 1) * 64];
+                }
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) O[tb] = mfma(fp[tb], wb[s], O[tb]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (s + 1 < 4) {
+#pragma unroll
+                    for (int tb = 0; tb < 2; ++tb) fp[tb] = np[tb];
+                }
+            }
             __bf16 *og = a.o + (tok0 * a.H + h) * kGD + col;
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
@@ -385,30 +462,45 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
                 }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // H <- gamma_C H + K^T diag(gamma_C / gamma) W
+        // H <- gamma_C H + K^T diag(gamma_C / gamma) W; step s = (row block tb, k half ks), the
+        // four state blocks j interleaved, K^T fragments read one step ahead.
         {
-            const float gC = Gs[kGC - 1];
-            bf16x8_t wg[2][2];
+            bf16x8_t wg[4];
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    W[tb][i] *= __builtin_amdgcn_exp2f((gC - Gs[32 * tb + 8 * (i / 4) + 4 * hh + (i % 4)]) * kGLog2e);
+                for (int q = 0; q < 4; ++q) {
+                    const float4 dg = *reinterpret_cast<const float4 *>(Fs + kGC + 32 * tb + 8 * q + 4 * hh);
+                    W[tb][4 * q + 0] *= dg.x;
+                    W[tb][4 * q + 1] *= dg.y;
+                    W[tb][4 * q + 2] *= dg.z;
+                    W[tb][4 * q + 3] *= dg.w;
+                }
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) wg[tb][ks] = acc_frag(W[tb], ks);
+                for (int ks = 0; ks < 2; ++ks) wg[2 * tb + ks] = acc_frag(W[tb], ks);
             }
-            const float dC = __builtin_amdgcn_exp2f(gC * kGLog2e);
+            const float dC = Fs[kGC - 1];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) Hs[j][i] *= dC;
+            bf16x8_t fk[4];
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
+            for (int j = 0; j < 4; ++j) fk[j] = T128::tr_frag(Kt, 0, lane, 0, j);
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        Hs[j] = mfma(T128::tr_frag(Kt, 32 * tb, lane, ks, j), wg[tb][ks], Hs[j]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
+            for (int s = 0; s < 4; ++s) {
+                bf16x8_t nk[4];
+                if (s + 1 < 4) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) nk[j] = T128::tr_frag(Kt, 32 * ((s + 1) / 2), lane, (s + 1) % 2, j);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Hs[j] = mfma(fk[j], wg[s], Hs[j]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (s + 1 < 4) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) fk[j] = nk[j];
+                }
             }
         }
     }
@@ -437,7 +529,7 @@ hipError_t launch_gdn(const GdnShape &sh, const GdnLayout &L, char *gws, const v
     a.U = reinterpret_cast<float *>(gws + L.U);
     a.Yn = reinterpret_cast<__bf16 *>(gws + L.Yn);
     a.P = reinterpret_cast<__bf16 *>(gws + L.P);
-    a.G = reinterpret_cast<float *>(gws + L.G);
+    a.F = reinterpret_cast<float *>(gws + L.F);
     a.states = reinterpret_cast<float *>(gws + L.states);
     a.o = static_cast<__bf16 *>(o);
     const int64_t n_tok = int64_t(sh.R) * sh.T;

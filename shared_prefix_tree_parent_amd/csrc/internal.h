@@ -98,10 +98,10 @@ struct GdnLayout {
     size_t level_ptr = 0;    // int32[n_levels + 1] (room for n_segs + 1): segments per depth, CSR
     size_t level_segs = 0;   // int32[n_segs]: segments by depth
     size_t qh = 0, kh = 0, vh = 0;   // bf16[R*T*H*128] each: conv + norm outputs
-    size_t U = 0;            // f32[n_chunks*H*64*128]
+    size_t U = 0;            // f32[n_chunks*H*64*128], in the scan's accumulator order
     size_t Yn = 0;           // bf16[n_chunks*H*64*128]
     size_t P = 0;            // bf16[n_chunks*H*64*64]
-    size_t G = 0;            // f32[n_chunks*H*64]
+    size_t F = 0;            // f32[n_chunks*H*128]: gamma_t, then gamma_C / gamma_t
     size_t states = 0;       // f32[n_segs*H*128*128]: final state of every segment
     size_t total = 0;
     int32_t n_chunks = 0, n_segs = 0, n_levels = 0, max_level_segs = 0;
@@ -122,7 +122,7 @@ inline GdnLayout make_gdn_layout(int32_t R, int32_t T, int32_t H, int32_t n_chun
     g.U = take(size_t(n_chunks) * H * 64 * 128 * 4);
     g.Yn = take(size_t(n_chunks) * H * 64 * 128 * 2);
     g.P = take(size_t(n_chunks) * H * 64 * 64 * 2);
-    g.G = take(size_t(n_chunks) * H * 64 * 4);
+    g.F = take(size_t(n_chunks) * H * 128 * 4);
     g.states = take(size_t(n_segs) * H * 128 * 128 * 4);
     g.total = off;
     g.n_chunks = n_chunks;

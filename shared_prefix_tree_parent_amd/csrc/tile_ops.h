@@ -115,19 +115,29 @@ __device__ __forceinline__ uint32_t lds_base(const char *p) {
 }
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// Resource for a tile of rows with HBM row stride `stride` bytes whose rows past n_valid read
+// as zero.
+__device__ __forceinline__ int32x4_t tile_rsrc(const char *src, int n_valid, int stride) {
+    return buf_rsrc(src, uint32_t(n_valid > 0 ? n_valid : 0) * uint32_t(stride));
+}
+// One 1 KB instruction of a tile copy: block blk (1024 / (2 D) rows) into the swizzled LDS tile
+// at dst.
+template <int D>
+__device__ __forceinline__ void copy_block(int32x4_t rs, int stride, uint32_t dst, int blk, int lane) {
+    using TL = Tile<D>;
+    constexpr int ROWS_PER_KB = 1024 / (D * 2);
+    const int row = blk * ROWS_PER_KB + lane / TL::CPR;
+    const int c = (lane % TL::CPR) ^ TL::sw(row);
+    buf_to_lds16(rs, dst + blk * 1024, row * stride + c * 16);
+}
 // Copy `rows` rows of D bf16 (HBM row stride `stride` bytes, rows past n_valid read as zero)
 // into a swizzled LDS tile; the nw waves of the workgroup split the 1 KB instructions.
 template <int D>
 __device__ __forceinline__ void copy_tile(const char *src, int n_valid, int stride, uint32_t dst, int rows,
                                           int wave, int nw, int lane) {
-    using TL = Tile<D>;
     constexpr int ROWS_PER_KB = 1024 / (D * 2);
-    const int32x4_t rs = buf_rsrc(src, uint32_t(n_valid > 0 ? n_valid : 0) * uint32_t(stride));
-    for (int blk = wave; blk < rows / ROWS_PER_KB; blk += nw) {
-        const int row = blk * ROWS_PER_KB + lane / TL::CPR;
-        const int c = (lane % TL::CPR) ^ TL::sw(row);
-        buf_to_lds16(rs, dst + blk * 1024, row * stride + c * 16);
-    }
+    const int32x4_t rs = tile_rsrc(src, n_valid, stride);
+    for (int blk = wave; blk < rows / ROWS_PER_KB; blk += nw) copy_block<D>(rs, stride, dst, blk, lane);
 }
 
 }  // namespace tile
