@@ -47,9 +47,15 @@ constexpr float kGLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------------------------ gdn_conv
 //
-// One workgroup (256 threads) per block of kConvTok tokens; a thread takes 8 consecutive
-// channels of every tensor and keeps their conv weights in registers for the whole block; 16
-// threads cover a head (the L2 norm is a 16-lane sum).
+// One workgroup (256 threads) per (block of kConvTok tokens, tensor q / k / v); a thread takes
+// 8 consecutive channels and keeps their conv weights in registers; 16 threads cover a head
+// (the L2 norm is a 16-lane sum).  The block's input rows, with the 3 rows before it, are
+// loaded once into a register window before any output is stored (stores and loads share one
+// counter, so a load issued after a store would also wait for the store); a tap reads the
+// window when the token-parent chain runs through the previous rows, which it does everywhere
+// except at the first tokens after a join, where the tap row is loaded on its own.  The parent
+// chains of the block are loaded once, all tokens in parallel (lane k of every wave walks
+// token k's chain).
 constexpr int kConvTok = 16;
 
 __global__ __launch_bounds__(256) void gdn_conv(int32_t n_tok, int32_t H, const int32_t *__restrict__ pi,
@@ -58,62 +64,68 @@ __global__ __launch_bounds__(256) void gdn_conv(int32_t n_tok, int32_t H, const 
                                                 float eps, __bf16 *__restrict__ qh, __bf16 *__restrict__ kh,
                                                 __bf16 *__restrict__ vh) {
     const int C = H * kGD;                                 // channels per tensor
-    const float qscale = 0.08838834764831845f;             // 1 / sqrt(128)
-    const int64_t tok_begin = int64_t(blockIdx.x) * kConvTok;
+    const int tsr = blockIdx.y;
+    const __bf16 *x = tsr == 0 ? xq : (tsr == 1 ? xk : xv);
+    __bf16 *out = tsr == 0 ? qh : (tsr == 1 ? kh : vh);
+    const float oscale = tsr == 0 ? 0.08838834764831845f : 1.f;   // q: 1 / sqrt(128)
+    const int tok_begin = int(blockIdx.x) * kConvTok;
+    // chain of token tok_begin + (lane % 16): c0 = pi(tok) (-2: pad or past the end), then
+    // pi^1..pi^3 (-1 past a root's first token)
+    int c0, c1, c2, c3;
+    {
+        const int tk = tok_begin + int(threadIdx.x & (kConvTok - 1));
+        c0 = tk < n_tok ? pi[tk] : -2;
+        c1 = c0 >= 0 ? c0 : -1;
+        c2 = c1 >= 0 ? pi[c1] : -1;
+        c3 = c2 >= 0 ? pi[c2] : -1;
+    }
     for (int c8 = threadIdx.x * 8; c8 < C; c8 += blockDim.x * 8) {
-        // weights of this thread's 8 channels, 3 tensors x 4 taps: [tensor][channel][tap]
-        float wr[3][8][kGW];
+        float wr[8][kGW];                                  // [channel][tap]
 #pragma unroll
-        for (int tsr = 0; tsr < 3; ++tsr)
+        for (int e = 0; e < 8; ++e) {
+            const float4 w4 = *reinterpret_cast<const float4 *>(w + ((int64_t(tsr) * C + c8 + e) * kGW));
+            wr[e][0] = w4.x; wr[e][1] = w4.y; wr[e][2] = w4.z; wr[e][3] = w4.w;
+        }
+        // win[i] = row tok_begin - (kGW - 1) + i (rows outside [0, n_tok) clamped; never used)
+        bf16x8_t win[kConvTok + kGW - 1];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float4 w4 = *reinterpret_cast<const float4 *>(w + ((int64_t(tsr) * C + c8 + e) * kGW));
-                wr[tsr][e][0] = w4.x; wr[tsr][e][1] = w4.y; wr[tsr][e][2] = w4.z; wr[tsr][e][3] = w4.w;
-            }
+        for (int i = 0; i < kConvTok + kGW - 1; ++i) {
+            const int rr = min(max(tok_begin - (kGW - 1) + i, 0), n_tok - 1);
+            win[i] = *reinterpret_cast<const bf16x8_t *>(x + int64_t(rr) * C + c8);
+        }
+#pragma unroll
         for (int k = 0; k < kConvTok; ++k) {
-            const int64_t tok = tok_begin + k;
-            if (tok >= n_tok) break;
-            const int p = __builtin_amdgcn_readfirstlane(pi[tok]);
-            if (p < -1) continue;                          // pad: never read downstream
-            // ch[j] = pi^j(tok) (global token indices; -1 past a root's first token)
-            int64_t ch[kGW];
-            ch[0] = tok;
-            int64_t nxt = p;
+            if (__builtin_amdgcn_readlane(c0, k) < -1) continue;     // pad: never read downstream
+            const int tok = tok_begin + k;
+            const int ch[kGW] = {tok, __builtin_amdgcn_readlane(c1, k), __builtin_amdgcn_readlane(c2, k),
+                                 __builtin_amdgcn_readlane(c3, k)};
+            float y[8];
 #pragma unroll
-            for (int j = 1; j < kGW; ++j) {
-                ch[j] = nxt;
-                nxt = nxt >= 0 ? __builtin_amdgcn_readfirstlane(pi[nxt]) : -1;
+            for (int e = 0; e < 8; ++e) y[e] = 0.f;
+#pragma unroll
+            for (int j = 0; j < kGW; ++j) {
+                if (ch[j] < 0) break;
+                bf16x8_t xv8;
+                if (ch[j] == tok - j) xv8 = win[k + kGW - 1 - j];
+                else xv8 = *reinterpret_cast<const bf16x8_t *>(x + int64_t(ch[j]) * C + c8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = fmaf(wr[e][kGW - 1 - j], float(xv8[e]), y[e]);
             }
 #pragma unroll
-            for (int tsr = 0; tsr < 3; ++tsr) {
-                const __bf16 *x = tsr == 0 ? xq : (tsr == 1 ? xk : xv);
-                float y[8];
+            for (int e = 0; e < 8; ++e) y[e] = y[e] * __builtin_amdgcn_rcpf(1.f + __expf(-y[e]));
+            float scale = 1.f;
+            if (tsr < 2) {
+                float ss = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = 0.f;
+                for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
 #pragma unroll
-                for (int j = 0; j < kGW; ++j) {
-                    if (ch[j] < 0) break;
-                    const bf16x8_t xv8 = *reinterpret_cast<const bf16x8_t *>(x + ch[j] * C + c8);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) y[e] = fmaf(wr[tsr][e][kGW - 1 - j], float(xv8[e]), y[e]);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = y[e] * __builtin_amdgcn_rcpf(1.f + __expf(-y[e]));
-                float scale = 1.f;
-                if (tsr < 2) {
-                    float ss = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
-#pragma unroll
-                    for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 16);
-                    scale = rsqrtf(ss + eps) * (tsr == 0 ? qscale : 1.f);
-                }
-                bf16x8_t o8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o8[e] = static_cast<__bf16>(y[e] * scale);
-                __bf16 *out = tsr == 0 ? qh : (tsr == 1 ? kh : vh);
-                *reinterpret_cast<bf16x8_t *>(out + tok * C + c8) = o8;
+                for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 16);
+                scale = rsqrtf(ss + eps) * oscale;
             }
+            bf16x8_t o8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o8[e] = static_cast<__bf16>(y[e] * scale);
+            *reinterpret_cast<bf16x8_t *>(out + int64_t(tok) * C + c8) = o8;
         }
     }
 }
@@ -226,12 +238,23 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
             const float gam = isk ? __builtin_amdgcn_exp2f(Gs[t] * kGLog2e) : 1.f;
             x[t] = Bs[t] * gam * T128::at(src, t, col);
         }
+        // A^T row s (A_ts for t > s) in 16-byte reads, one row ahead of its use.
+        float ar[2][kGC];
+        auto load_row = [&](auto sc_, float(&dst)[kGC]) __attribute__((always_inline)) {
+            constexpr int s = decltype(sc_)::value;
+            static_for<(kGC - (s + 1) / 4 * 4) / 4>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int t4 = (s + 1) / 4 * 4 + 4 * decltype(qc)::value;
+                const float4 v = *reinterpret_cast<const float4 *>(As + s * kGC + t4);
+                dst[t4] = v.x; dst[t4 + 1] = v.y; dst[t4 + 2] = v.z; dst[t4 + 3] = v.w;
+            });
+        };
+        load_row(std::integral_constant<int, 0>{}, ar[0]);
         static_for<kGC - 1>([&](auto sc) __attribute__((always_inline)) {
             constexpr int s0 = decltype(sc)::value;
-            const float *Acol = As + s0 * kGC;             // A^T row s0: A_ts for every t
+            if constexpr (s0 + 1 < kGC - 1) load_row(std::integral_constant<int, s0 + 1>{}, ar[(s0 + 1) & 1]);
             static_for<kGC - 1 - s0>([&](auto tc) __attribute__((always_inline)) {
                 constexpr int t = s0 + 1 + decltype(tc)::value;
-                x[t] = fmaf(-Acol[t], x[s0], x[t]);
+                x[t] = fmaf(-ar[s0 & 1][t], x[s0], x[t]);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -535,7 +558,7 @@ hipError_t launch_gdn(const GdnShape &sh, const GdnLayout &L, char *gws, const v
     const int64_t n_tok = int64_t(sh.R) * sh.T;
     if (n_tok > INT32_MAX || int64_t(L.n_chunks) * sh.H > INT32_MAX) return hipErrorInvalidValue;
     if (n_tok > 0)
-        gdn_conv<<<int((n_tok + kConvTok - 1) / kConvTok), 256, 0, s>>>(int32_t(n_tok), sh.H, reinterpret_cast<const int32_t *>(gws + L.pi),
+        gdn_conv<<<dim3(unsigned((n_tok + kConvTok - 1) / kConvTok), 3), 256, 0, s>>>(int32_t(n_tok), sh.H, reinterpret_cast<const int32_t *>(gws + L.pi),
                                             static_cast<const __bf16 *>(xq), static_cast<const __bf16 *>(xk),
                                             static_cast<const __bf16 *>(xv), conv_w, sh.eps,
                                             reinterpret_cast<__bf16 *>(gws + L.qh), reinterpret_cast<__bf16 *>(gws + L.kh),
