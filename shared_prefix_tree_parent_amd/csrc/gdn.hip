@@ -132,12 +132,17 @@ __global__ __launch_bounds__(256) void gdn_conv(int32_t n_tok, int32_t H, const 
 
 // ------------------------------------------------------------------------------ gdn_prep
 //
-// LDS: Q, K, V chunk tiles (64 x 128 bf16, swizzled), A (64 x 64 fp32), G and beta (64 fp32).
+// LDS: Q, K, V chunk tiles (64 x 128 bf16, swizzled); a 64 x 64 fp32 array holding A^T in its
+// upper triangle (As[s][t] = A_ts, s < t), then T = (I + A)^-1 (As[t][s] = T_ts); G, beta and
+// gamma (64 fp32 each).  Once the Gram products are done
+// the Q tile's 16 KB take the bf16 operand tiles of T diag(beta) (then of T diag(beta gamma)),
+// high and low parts, and last the -Y tile on its way out.
 struct PrepLds {
     static constexpr int TILE = kGC * kGD * 2;
     static constexpr int Q_OFF = 0, K_OFF = TILE, V_OFF = 2 * TILE, A_OFF = 3 * TILE;
-    static constexpr int G_OFF = A_OFF + kGC * kGC * 4, GB_OFF = G_OFF + kGC * 4;
-    static constexpr int SIZE = GB_OFF + kGC * 4;
+    static constexpr int HI_OFF = Q_OFF, LO_OFF = Q_OFF + kGC * kGC * 2, YS_OFF = Q_OFF;
+    static constexpr int G_OFF = A_OFF + kGC * kGC * 4, GB_OFF = G_OFF + kGC * 4, GM_OFF = GB_OFF + kGC * 4;
+    static constexpr int SIZE = GM_OFF + kGC * 4;
 };
 
 template <class F, int... I>
@@ -196,55 +201,55 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
         Bs[lane] = bv;
         // decay factors for the scan: gamma_t and gamma_C / gamma_t (both <= 1)
         const float gC = __shfl(gv, kGC - 1, 64);
+        const float gam = __builtin_amdgcn_exp2f(gv * kGLog2e);
+        reinterpret_cast<float *>(smem + PrepLds::GM_OFF)[lane] = gam;
         float *Fo = a.F + (int64_t(c) * a.H + h) * 2 * kGC;
-        Fo[lane] = __builtin_amdgcn_exp2f(gv * kGLog2e);
+        Fo[lane] = gam;
         Fo[kGC + lane] = __builtin_amdgcn_exp2f((gC - gv) * kGLog2e);
     }
     wait_loads();
     __syncthreads();
 
-    // Gram K K^T and Q K^T: wave w takes the 32 x 32 block (t block w/2, s block w%2).
+    // Gram and Q K^T: wave w takes the 32 x 32 block (t block w/2, s block w%2).  The Gram
+    // block is computed transposed (rows s, columns t) so that A^T is stored along lanes.
     const char *Qt = smem + PrepLds::Q_OFF, *Kt = smem + PrepLds::K_OFF;
     const int bt = wave >> 1, bs = wave & 1;
-    floatx16 kk = zero16(), qk = zero16();
+    floatx16 kkT = zero16(), qk = zero16();
 #pragma unroll
     for (int ds = 0; ds < kGD / 16; ++ds) {
         const bf16x8_t kb = T128::row_frag(Kt, 32 * bs, lane, ds);
-        kk = mfma(T128::row_frag(Kt, 32 * bt, lane, ds), kb, kk);
+        kkT = mfma(kb, T128::row_frag(Kt, 32 * bt, lane, ds), kkT);
         qk = mfma(T128::row_frag(Qt, 32 * bt, lane, ds), kb, qk);
     }
     float *As = reinterpret_cast<float *>(smem + PrepLds::A_OFF);
     __bf16 *Pout = a.P + (int64_t(c) * a.H + h) * kGC * kGC;
-    const int s = 32 * bs + (lane & 31);
+    {
+        const int tA = 32 * bt + (lane & 31), sP = 32 * bs + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int t = 32 * bt + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
-        const float dec = __builtin_amdgcn_exp2f((Gs[t] - Gs[s]) * kGLog2e);   // gamma_t / gamma_s for s <= t
-        As[s * kGC + t] = s < t ? Bs[t] * dec * kk[i] : 0.f;         // transposed: A^T[s][t]
-        Pout[t * kGC + s] = static_cast<__bf16>(s <= t ? dec * qk[i] : 0.f);
+        for (int i = 0; i < 16; ++i) {
+            const int r8 = 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
+            const int sA = 32 * bs + r8, tP = 32 * bt + r8;
+            // gamma_t / gamma_s for s <= t
+            const float decA = __builtin_amdgcn_exp2f((Gs[tA] - Gs[sA]) * kGLog2e);
+            const float decP = __builtin_amdgcn_exp2f((Gs[tP] - Gs[sP]) * kGLog2e);
+            As[sA * kGC + tA] = sA < tA ? Bs[tA] * decA * kkT[i] : 0.f;       // A^T[s][t]
+            Pout[tP * kGC + sP] = static_cast<__bf16>(sP <= tP ? decP * qk[i] : 0.f);
+        }
     }
     __syncthreads();
 
-    // Forward substitution, one thread per column of [beta V | beta gamma K], the column in
-    // registers: x starts as the right-hand side; once x_s is final every later row takes
-    // its term  x_t -= A_ts x_s  (A^T rows read four at a time).
-    {
-        const int col = tid & 127;
-        const bool isk = tid >= 128;
-        const char *src = isk ? Kt : smem + PrepLds::V_OFF;
+    // T = (I + A)^-1 by forward substitution on the identity's columns: wave 0, lane c takes
+    // column c, A^T rows read one ahead (no barrier inside).
+    if (wave == 0) {
         float x[kGC];
 #pragma unroll
-        for (int t = 0; t < kGC; ++t) {
-            const float gam = isk ? __builtin_amdgcn_exp2f(Gs[t] * kGLog2e) : 1.f;
-            x[t] = Bs[t] * gam * T128::at(src, t, col);
-        }
-        // A^T row s (A_ts for t > s) in 16-byte reads, one row ahead of its use.
+        for (int t = 0; t < kGC; ++t) x[t] = t == lane ? 1.f : 0.f;
         float ar[2][kGC];
         auto load_row = [&](auto sc_, float(&dst)[kGC]) __attribute__((always_inline)) {
-            constexpr int s = decltype(sc_)::value;
-            static_for<(kGC - (s + 1) / 4 * 4) / 4>([&](auto qc) __attribute__((always_inline)) {
-                constexpr int t4 = (s + 1) / 4 * 4 + 4 * decltype(qc)::value;
-                const float4 v = *reinterpret_cast<const float4 *>(As + s * kGC + t4);
+            constexpr int s_ = decltype(sc_)::value;
+            static_for<(kGC - (s_ + 1) / 4 * 4) / 4>([&](auto qc) __attribute__((always_inline)) {
+                constexpr int t4 = (s_ + 1) / 4 * 4 + 4 * decltype(qc)::value;
+                const float4 v = *reinterpret_cast<const float4 *>(As + s_ * kGC + t4);
                 dst[t4] = v.x; dst[t4 + 1] = v.y; dst[t4 + 2] = v.z; dst[t4 + 3] = v.w;
             });
         };
@@ -258,20 +263,85 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
             });
             __builtin_amdgcn_sched_barrier(0);
         });
-        if (!isk) {
-            // accumulator order of the scan: element (t, col) sits with scan wave col/32, lane
-            // 32 ((t/4) % 2) + col % 32, register 4 ((t % 32) / 8) + t % 4 of row block t/32;
-            // four consecutive t are one 16-byte store.
-            float4 *Uo = reinterpret_cast<float4 *>(a.U + (int64_t(c) * a.H + h) * kGC * kGD) +
-                         (col >> 5) * (kGC * 32 / 4) + (col & 31);
+        // all of T: the A^T rows are no longer read
 #pragma unroll
-            for (int k4 = 0; k4 < kGC / 4; ++k4)
-                Uo[(k4 >> 1) * 64 + (k4 & 1) * 32] = make_float4(x[4 * k4], x[4 * k4 + 1], x[4 * k4 + 2], x[4 * k4 + 3]);
-        } else {
-            __bf16 *Yo = a.Yn + (int64_t(c) * a.H + h) * kGC * kGD + col;
+        for (int t = 0; t < kGC; ++t) As[t * kGC + lane] = x[t];
+    }
+    __syncthreads();
+
+    // U = (T diag(beta)) V and Y = (T diag(beta gamma)) K on MFMA.  The left factor is split in
+    // bf16 high and low parts (fp32 accuracy); V and K are bf16 already.  Wave w takes value /
+    // key columns 32 w .. 32 w + 31, both 32-row blocks.
+    using T64 = Tile<kGC>;
+    const float *Gm = reinterpret_cast<const float *>(smem + PrepLds::GM_OFF);
+    char *hi_t = smem + PrepLds::HI_OFF, *lo_t = smem + PrepLds::LO_OFF;
+    auto build_factor = [&](bool with_gamma) __attribute__((always_inline)) {
+        const int t = tid >> 2, q4 = tid & 3;                 // row t, columns 16 q4 .. +15
+        bf16x8_t hv[2], lv[2];
 #pragma unroll
-            for (int t = 0; t < kGC; ++t) Yo[t * kGD] = static_cast<__bf16>(-x[t]);
+        for (int e = 0; e < 16; ++e) {
+            const int sc = 16 * q4 + e;
+            const float f = As[t * kGC + sc] * Bs[sc] * (with_gamma ? Gm[sc] : 1.f);
+            const __bf16 fh = static_cast<__bf16>(f);
+            hv[e / 8][e % 8] = fh;
+            lv[e / 8][e % 8] = static_cast<__bf16>(f - float(fh));
         }
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc) {
+            *reinterpret_cast<bf16x8_t *>(hi_t + T64::chunk_at(t, 2 * q4 + hc)) = hv[hc];
+            *reinterpret_cast<bf16x8_t *>(lo_t + T64::chunk_at(t, 2 * q4 + hc)) = lv[hc];
+        }
+    };
+    auto product = [&](const char *rhs, floatx16 (&acc)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) acc[tb] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8_t bv = T128::tr_frag(rhs, 0, lane, ks, wave);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                acc[tb] = mfma(T64::perm_frag(hi_t, 32 * tb, lane, ks), bv, acc[tb]);
+                acc[tb] = mfma(T64::perm_frag(lo_t, 32 * tb, lane, ks), bv, acc[tb]);
+            }
+        }
+    };
+    const int64_t chh = int64_t(c) * a.H + h;
+    floatx16 acc[2];
+    build_factor(false);
+    __syncthreads();
+    product(smem + PrepLds::V_OFF, acc);
+    {
+        // accumulator order of the scan: wave w's columns, float4 (4 tb + q) * 64 + lane holds
+        // rows 32 tb + 8 q + 4 (lane / 32) + 0..3
+        float4 *Uo = reinterpret_cast<float4 *>(a.U + chh * kGC * kGD) + wave * (kGC * 32 / 4) + lane;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                Uo[(4 * tb + q) * 64] = make_float4(acc[tb][4 * q], acc[tb][4 * q + 1], acc[tb][4 * q + 2],
+                                                    acc[tb][4 * q + 3]);
+    }
+    __syncthreads();
+    build_factor(true);
+    __syncthreads();
+    product(smem + PrepLds::K_OFF, acc);
+    __syncthreads();
+    {
+        // -Y as bf16, row-major [t][128] in the Q tile's space, then out in 16-byte rows
+        __bf16 *Ys = reinterpret_cast<__bf16 *>(smem + PrepLds::YS_OFF);
+        const int colw = 32 * wave + (lane & 31);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                Ys[(32 * tb + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4)) * kGD + colw] = static_cast<__bf16>(-acc[tb][i]);
+    }
+    __syncthreads();
+    {
+        const bf16x8_t *src = reinterpret_cast<const bf16x8_t *>(smem + PrepLds::YS_OFF);
+        bf16x8_t *dst = reinterpret_cast<bf16x8_t *>(a.Yn + chh * kGC * kGD);
+#pragma unroll
+        for (int k4 = 0; k4 < kGC * kGD / 8 / 256; ++k4) dst[tid + 256 * k4] = src[tid + 256 * k4];
     }
 }
 
