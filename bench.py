@@ -364,7 +364,10 @@ def main() -> int:
         gdn_ms = timed(gdn_step, args.steps)
         n_real = int(inp.real_len.sum())
         rec_flops = 8.0 * 128 * 128 * H_g * n_real                  # per token and head: k^T h, update, h^T q
-        chunk_flops = gplan.info.n_chunks * H_g * (2 * 2 * 64 * 64 * 128 + 2 * 64 * 64 * 256 +
+        # per (chunk, head): Gram and Q K^T; T = (I + A)^-1 (forward substitution on the identity);
+        # U = T diag(b) V and Y = T diag(b g) K; the scan's Y H, Q H, P W and K^T W
+        tri = sum((s_ + 1) * (63 - s_) for s_ in range(63))
+        chunk_flops = gplan.info.n_chunks * H_g * (2 * 2 * 64 * 64 * 128 + 2 * tri + 2 * 2 * 64 * 64 * 128 +
                                                     3 * 2 * 64 * 128 * 128 + 2 * 64 * 64 * 128)
         gdn = {"ms": round(gdn_ms, 4), "heads": H_g, "head_dim": 128, "tokens": n_real,
                "chunks": gplan.info.n_chunks, "levels": gplan.info.n_levels,
