@@ -11,11 +11,14 @@
 //   * dq_kernel: one workgroup per forward item (row, q-tile, KV head, chunk of its query
 //     heads), 8 waves of 32 query rows, walking the q-tile's k-tile list with K/V tiles
 //     staged in LDS (direct-to-LDS copies, two tiles ahead);
-//   * dkdv_kernel: one workgroup per (row, pair of k-tiles, KV head), 4 waves of 32 keys whose
-//     K and V fragments stay in registers, walking the pair's list of q-tiles (the transposed
-//     tile lists) and every query head of the group in blocks of 32 queries; each block's Q,
-//     dO, LSE and D are staged in LDS once for all four waves, three blocks ahead.  A wave
-//     whose k-tile does not see a block's q-tile skips it.
+//   * dkdv_kernel: one workgroup per (row, pair of k-tiles, KV head, query slice), 4 waves of
+//     32 keys whose K and V fragments stay in registers, walking the slice's run of the pair's
+//     list of q-tiles (the transposed tile lists) and every query head of the group in blocks
+//     of 32 queries; each block's Q, dO, LSE and D are staged in LDS once for all four waves,
+//     three blocks ahead.  A wave whose k-tile does not see a block's q-tile skips it.  A pair
+//     seen by many q-tiles (a shared prefix's keys are seen by every query after them) is split
+//     into up to kBwdSlices slices so that its work spreads over several CUs;
+//   * dkdv_reduce (only where a pair was split): adds the slices' fp32 partials in slice order.
 // Every result is written exactly once (no atomics); gradients of pads are zero.
 //
 // Orientation (32x32x16 bf16 MFMA, accumulator element i of lane l at row 8(i/4) + 4(l/32) +
@@ -58,6 +61,7 @@ struct BwdArgs {
     const int32_t *qt_ptr, *kt_idx;
     const uint8_t *kt_kind;
     const int32_t *kp_ptr, *kp_list, *kwork;
+    float *part;                   // per-slice dK^T / dV^T partials (BwdLayout::part)
     const int32_t *kend, *work, *n_real, *status;
     int32_t T, Hq, Hkv, G, HCH, nQ, nK, nP, L, BQ;
     float c;       // scale * log2(e)
@@ -130,6 +134,17 @@ struct LaneOffsets {
 __device__ __forceinline__ floatx16 mfma(bf16x8_t a, bf16x8_t b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (register arrays indexed by I stay
+// in registers).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // bf16 operand from accumulator registers 8 ks .. 8 ks + 7.
 __device__ __forceinline__ bf16x8_t acc_frag(const floatx16 &x, int ks) {
     bf16x8_t f;
@@ -456,23 +471,43 @@ __device__ __forceinline__ void kv_block(const char *blk, const LaneOffsets<D> &
     using LD = KvLds<D>;
     const char *Qt = blk + LD::Q_OFF;
     const char *Ot = blk + LD::DO_OFF;
+    // Operand reads run RING MFMAs ahead of their use, from the S / dP products into the dV /
+    // dK ones (whose first operands are read before the softmax).
+    constexpr int NP1 = 2 * TL::NDS, NP2 = 4 * TL::NDB, RING = 4;
+    static_assert(NP1 >= RING && NP2 >= RING, "ring deeper than a phase");
+    // operand i < NP1: row read of Q (even) / dO (odd) for S / dP; NP1 + j: transposed read of
+    // dO (j even, for dV) / Q (j odd, for dK), j = (ks NDB + db) 2 + t
+    auto operand = [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < NP1) {
+            return TL::row_at((i % 2 == 0 ? Qt : Ot) + lo.row[i / 2]);
+        } else {
+            constexpr int j = i - NP1, t = j % 2, db = (j / 2) % TL::NDB, ks = j / 2 / TL::NDB;
+            const char *base = (t == 0 ? Ot : Qt) + 16 * ks * TL::ROWB;
+            return TL::tr_at(base + lo.tr[db][0], base + lo.tr[db][1]);
+        }
+    };
+    bf16x8_t ring[RING];
+    static_for<RING>([&](auto ic) __attribute__((always_inline)) { ring[decltype(ic)::value] = operand(ic); });
     floatx16 s = zero16(), dp = zero16();
-#pragma unroll
-    for (int ds = 0; ds < TL::NDS; ++ds) {
-        s = mfma(TL::row_at(Qt + lo.row[ds]), kf[ds], s);
-        dp = mfma(TL::row_at(Ot + lo.row[ds]), vf[ds], dp);
-    }
+    static_for<NP1>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        const bf16x8_t op = ring[i % RING];
+        ring[i % RING] = operand(std::integral_constant<int, i + RING>{});
+        if constexpr (i % 2 == 0) s = mfma(op, kf[i / 2], s);
+        else dp = mfma(op, vf[i / 2], dp);
+        __builtin_amdgcn_sched_barrier(0);
+    });
     bf16x8_t pf[2], sf[2];
     kv_softmax<D>(s, dp, blk, h, c, partial, key, kend_k, q0 + 4 * h, pf, sf);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const int rofs = 16 * ks * TL::ROWB;
-#pragma unroll
-        for (int db = 0; db < TL::NDB; ++db) {
-            dv[db] = mfma(TL::tr_at(Ot + lo.tr[db][0] + rofs, Ot + lo.tr[db][1] + rofs), pf[ks], dv[db]);
-            dk[db] = mfma(TL::tr_at(Qt + lo.tr[db][0] + rofs, Qt + lo.tr[db][1] + rofs), sf[ks], dk[db]);
-        }
-    }
+    static_for<NP2>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value, t = j % 2, db = (j / 2) % TL::NDB, ks = j / 2 / TL::NDB;
+        const bf16x8_t op = ring[j % RING];
+        if constexpr (j + RING < NP2) ring[j % RING] = operand(std::integral_constant<int, NP1 + j + RING>{});
+        if constexpr (t == 0) dv[db] = mfma(op, pf[ks], dv[db]);
+        else dk[db] = mfma(op, sf[ks], dk[db]);
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 // Position in a pair's sequence of 32-query blocks: list entry, query head of the group,
@@ -490,6 +525,9 @@ struct BlockCursor {
     }
 };
 
+// Query slices of a pair whose q-tile list has n entries.
+__device__ __forceinline__ int kv_slices(int n) { return min(kBwdSlices, max(1, n / kBwdSliceEntries)); }
+
 template <int D>
 __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     using TL = Tile<D>;
@@ -500,8 +538,13 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
-    const int g = blockIdx.x % a.Hkv, item = blockIdx.x / a.Hkv;
+    const int g = blockIdx.x % a.Hkv, slice = (blockIdx.x / a.Hkv) % kBwdSlices;
+    const int item = blockIdx.x / a.Hkv / kBwdSlices;
     const int pitem = a.kwork[item];
+    const int32_t list_begin = a.kp_ptr[pitem];
+    const int NL_pair = a.kp_ptr[pitem + 1] - list_begin;
+    const int n_slices = kv_slices(NL_pair);
+    if (slice >= n_slices) return;
     const int r = pitem / a.nP, pr = pitem % a.nP;
     const int T = a.T;
     const int n_real = a.n_real[r];
@@ -542,15 +585,19 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
 
     // Blocks: (entry of the pair's q-tile list, query head, 32-query chunk), one LDS stage each,
     // copied AHEAD blocks ahead of the one in use.
-    const int32_t l_begin = a.kp_ptr[pitem];
-    const int NL = a.kp_ptr[pitem + 1] - l_begin;
+    const int32_t l_begin = list_begin + NL_pair * slice / n_slices;
+    const int NL = list_begin + NL_pair * (slice + 1) / n_slices - l_begin;
+    // the slice's q-tile entries, staged in LDS once (no scalar load inside the block loop)
+    int32_t *lst = reinterpret_cast<int32_t *>(smem + LD::NS * LD::BLK);
+    for (int e = tid; e < NL; e += kKvWaves * 64) lst[e] = a.kp_list[l_begin + e];
+    __syncthreads();
     const int CH = a.BQ / kQBlk;
     const int NB = NL * a.G * CH;
     const int q_stride = a.Hq * D * 2;
     const uint32_t lds0 = lds_base(smem);
     BlockCursor ci, cc;            // next block to copy / to compute
     auto issue = [&](int n) __attribute__((always_inline)) {
-        const int ent = __builtin_amdgcn_readfirstlane(a.kp_list[l_begin + ci.e]);
+        const int ent = __builtin_amdgcn_readfirstlane(lst[ci.e]);
         const int q0 = (ent >> 4) * a.BQ + ci.ch * kQBlk;
         const int head = g * a.G + ci.hd;
         ci.next(a.G, CH);
@@ -585,7 +632,7 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
         }
         block_barrier();
         if (n + LD::AHEAD < NB) issue(n + LD::AHEAD);
-        const int ent = __builtin_amdgcn_readfirstlane(a.kp_list[l_begin + cc.e]);
+        const int ent = __builtin_amdgcn_readfirstlane(lst[cc.e]);
         const int q0 = (ent >> 4) * a.BQ + cc.ch * kQBlk;
         cc.next(a.G, CH);
         const int cls = (ent >> cls_shift) & 3;
@@ -593,6 +640,21 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
             kv_block<D>(smem + (n % LD::NS) * LD::BLK, lo, kf, vf, a.c, h, key, kend_k, q0, cls == kTilePartial, dk, dv);
     }
 
+    if (n_slices > 1) {
+        // fp32 partial in accumulator order: float4 ((wave NDB + db) 4 + i4) 64 + lane
+        float4 *pp = reinterpret_cast<float4 *>(a.part) +
+                     ((int64_t(pitem) * a.Hkv + g) * kBwdSlices + slice) * 2 * (kKvWaves * TL::NDB * 4 * 64);
+#pragma unroll
+        for (int db = 0; db < TL::NDB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int idx = ((wave * TL::NDB + db) * 4 + i4) * 64 + lane;
+                pp[idx] = make_float4(dk[db][4 * i4], dk[db][4 * i4 + 1], dk[db][4 * i4 + 2], dk[db][4 * i4 + 3]);
+                pp[kKvWaves * TL::NDB * 4 * 64 + idx] =
+                    make_float4(dv[db][4 * i4], dv[db][4 * i4 + 1], dv[db][4 * i4 + 2], dv[db][4 * i4 + 3]);
+            }
+        return;
+    }
     // dK = scale dS^T Q, dV = P^T dO: lane holds its key, 4 consecutive d per register group.
     if (!kin) return;
     const int64_t off = ((int64_t(r) * T + key) * a.Hkv + g) * D;
@@ -617,6 +679,42 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
         }
 }
 
+// Sum of a split pair's slice partials, in slice order, to bf16 dK (times scale) and dV.  One
+// workgroup per (pair item, KV head), as dkdv_kernel without the slice; unsplit pairs return.
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_reduce(BwdArgs a) {
+    using TL = Tile<D>;
+    if (a.status[0] != 0) return;
+    const int g = blockIdx.x % a.Hkv, item = blockIdx.x / a.Hkv;
+    const int pitem = a.kwork[item];
+    const int n_slices = kv_slices(a.kp_ptr[pitem + 1] - a.kp_ptr[pitem]);
+    if (n_slices == 1) return;
+    const int r = pitem / a.nP, pr = pitem % a.nP;
+    const int T = a.T;
+    constexpr int PER = kKvWaves * TL::NDB * 4 * 64;            // float4 per tensor per slice
+    const float4 *base = reinterpret_cast<const float4 *>(a.part) + (int64_t(pitem) * a.Hkv + g) * kBwdSlices * 2 * PER;
+    for (int idx = threadIdx.x; idx < PER; idx += blockDim.x) {
+        const int lane = idx % 64, i4 = (idx / 64) % 4, db = (idx / 256) % TL::NDB, wave = idx / (256 * TL::NDB);
+        float4 sk = base[idx], sv = base[PER + idx];
+        for (int sl = 1; sl < n_slices; ++sl) {
+            const float4 k4 = base[sl * 2 * PER + idx], v4 = base[sl * 2 * PER + PER + idx];
+            sk.x += k4.x; sk.y += k4.y; sk.z += k4.z; sk.w += k4.w;
+            sv.x += v4.x; sv.y += v4.y; sv.z += v4.z; sv.w += v4.w;
+        }
+        const int key = (2 * pr + (wave >> 1)) * kBK + 32 * (wave & 1) + (lane & 31);
+        if (key >= T) continue;
+        const int d0 = 32 * db + 8 * i4 + 4 * (lane >> 5);
+        const int64_t off = ((int64_t(r) * T + key) * a.Hkv + g) * D + d0;
+        bf16x4_t wk, wv;
+        wk[0] = static_cast<__bf16>(sk.x * a.scale); wk[1] = static_cast<__bf16>(sk.y * a.scale);
+        wk[2] = static_cast<__bf16>(sk.z * a.scale); wk[3] = static_cast<__bf16>(sk.w * a.scale);
+        wv[0] = static_cast<__bf16>(sv.x); wv[1] = static_cast<__bf16>(sv.y);
+        wv[2] = static_cast<__bf16>(sv.z); wv[3] = static_cast<__bf16>(sv.w);
+        *reinterpret_cast<bf16x4_t *>(reinterpret_cast<__bf16 *>(a.dk) + off) = wk;
+        *reinterpret_cast<bf16x4_t *>(reinterpret_cast<__bf16 *>(a.dv) + off) = wv;
+    }
+}
+
 template <int D>
 hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, hipStream_t s) {
     const int64_t n_threads = int64_t(R) * a.T * a.Hq * (D / 8);
@@ -634,11 +732,14 @@ hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, hipSt
         dq_kernel<D><<<n_items_q, kDqWaves * 64, smem, s>>>(a);
     }
     if (n_items_k > 0) {
-        const int smem = KvLds<D>::NS * KvLds<D>::BLK;
+        // stages, then one pair's list (at most nQ entries)
+        const int smem = KvLds<D>::NS * KvLds<D>::BLK + 4 * ((a.nQ + 3) & ~3);
+        if (smem > 160 * 1024) return hipErrorInvalidValue;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(dkdv_kernel<D>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return e;
-        dkdv_kernel<D><<<n_items_k, kKvWaves * 64, smem, s>>>(a);
+        dkdv_kernel<D><<<n_items_k * kBwdSlices, kKvWaves * 64, smem, s>>>(a);
+        dkdv_reduce<D><<<n_items_k, 256, 0, s>>>(a);
     }
     return hipGetLastError();
 }
@@ -660,6 +761,7 @@ hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b,
     a.kp_ptr = reinterpret_cast<const int32_t *>(bws + b.kp_ptr);
     a.kp_list = reinterpret_cast<const int32_t *>(bws + b.kp_list);
     a.kwork = reinterpret_cast<const int32_t *>(bws + b.kwork);
+    a.part = reinterpret_cast<float *>(bws + b.part);
     a.kend = reinterpret_cast<const int32_t *>(ws + w.kend);
     a.work = reinterpret_cast<const int32_t *>(ws + w.work);
     a.n_real = reinterpret_cast<const int32_t *>(ws + w.n_real);
@@ -671,7 +773,7 @@ hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b,
     a.c = sh.scale * kLog2e;
     const int64_t n_q = int64_t(sh.R) * w.nQ * a.L;
     const int64_t n_k = int64_t(sh.R) * b.nP * sh.Hkv;
-    if (n_q > INT32_MAX || n_k > INT32_MAX) return hipErrorInvalidValue;
+    if (n_q > INT32_MAX || n_k * kBwdSlices > INT32_MAX) return hipErrorInvalidValue;
     if (sh.dtype != TREE_DT_BF16) return hipErrorInvalidValue;
     if (sh.BQ % kQBlk != 0) return hipErrorInvalidValue;
     if (sh.D == 128) return launch_d<128>(a, sh.R, int(n_q), int(n_k), s);

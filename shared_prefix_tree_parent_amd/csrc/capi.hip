@@ -139,7 +139,7 @@ int bwd_check(const tree_attn_desc *d, WsLayout *w, BwdLayout *b) {
     if (w->BQ != bq || w->BK != bk) return TREE_E_UNSUPPORTED;
     if (d->dtype != TREE_DT_BF16) return TREE_E_UNSUPPORTED;
     if (w->nK > kFwdMaxKTiles) return TREE_E_UNSUPPORTED;
-    *b = make_bwd_layout(*w, d->h_q);
+    *b = make_bwd_layout(*w, d->h_q, d->h_kv, d->head_dim);
     return TREE_OK;
 }
 }  // namespace

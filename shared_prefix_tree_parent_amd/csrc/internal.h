@@ -60,6 +60,13 @@ inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_
 
 // Backward workspace layout (caller-allocated, filled by tree_attn_bwd_plan / tree_attn_bwd).
 // The dK/dV pass works on pairs of k-tiles (k-tiles 2p and 2p+1, 128 keys).
+// dK/dV query slices: a k-tile pair whose q-tile list has n entries is processed as
+// min(kBwdSlices, max(1, n / kBwdSliceEntries)) workgroups per KV head, each over an equal
+// run of the list; when there is more than one, each writes an fp32 partial and a reduce pass
+// adds them in slice order (deterministic).
+constexpr int kBwdSlices = 4;
+constexpr int kBwdSliceEntries = 16;
+
 struct BwdLayout {
     size_t delta = 0;     // float[R*Hq*T]: rowsum(dO * O) per (row, head, token); 0 at pads
     size_t lse2 = 0;      // float[R*Hq*T]: the forward's LSE times log2(e)
@@ -67,11 +74,12 @@ struct BwdLayout {
     size_t kp_list = 0;   // int32[R*nQ*nP]: q-tile*16 + class(2p)*4 + class(2p+1), ascending q-tile
     size_t kwork = 0;     // int32[R*nP]: (row, pair) items, longest list first
     size_t khist = 0;     // int32[nQ + 2]
+    size_t part = 0;      // float[R*nP*Hkv*kBwdSlices*2*128*D]: per-slice dK^T, dV^T partials
     size_t total = 0;
     int32_t nP = 0;       // k-tile pairs per row: ceil(nK / 2)
 };
 
-inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq) {
+inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq, int32_t Hkv, int32_t D) {
     BwdLayout b;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
@@ -82,6 +90,7 @@ inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq) {
     b.kp_list = take(size_t(w.R) * w.nQ * b.nP * sizeof(int32_t));
     b.kwork = take(size_t(w.R) * b.nP * sizeof(int32_t));
     b.khist = take((size_t(w.nQ) + 2) * sizeof(int32_t));
+    b.part = take(size_t(w.R) * b.nP * Hkv * kBwdSlices * 2 * 128 * D * sizeof(float));
     b.total = off;
     return b;
 }
