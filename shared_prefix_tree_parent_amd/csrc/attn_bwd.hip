@@ -260,14 +260,38 @@ __device__ __forceinline__ void dq_tile(const char *Kt, const char *Vt, const in
                                         float lse2, float dlt, bool partial, int dq_, int qpos,
                                         floatx16 (&acc)[D / 32]) {
     using TL = Tile<D>;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        floatx16 s = zero16(), dp = zero16();
-#pragma unroll
-        for (int ds = 0; ds < TL::NDS; ++ds) {
-            s = mfma(TL::row_at(Kt + lo.row[ds] + 32 * kb * TL::ROWB), qf[ds], s);
-            dp = mfma(TL::row_at(Vt + lo.row[ds] + 32 * kb * TL::ROWB), dof[ds], dp);
+    // Operand reads run RING MFMAs ahead of use, across the softmax and the two 32-key halves.
+    // Operand i of half kb = i / PER: r = i % PER < NA a row read of K (even r) or V (odd) for
+    // S^T / dP^T; else the transposed K read of dQ^T's MFMA (ks, db) = ((r - NA) / NDB, % NDB).
+    constexpr int NDB = TL::NDB, NA = 2 * TL::NDS, PER = NA + 2 * NDB, TOT = 2 * PER, RING = 4;
+    auto operand = [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value, kb = i / PER, r = i % PER;
+        if constexpr (r < NA) {
+            return TL::row_at((r % 2 == 0 ? Kt : Vt) + lo.row[r / 2] + 32 * kb * TL::ROWB);
+        } else {
+            constexpr int j = r - NA, ks = j / NDB, db = j % NDB;
+            const int rofs = (32 * kb + 16 * ks) * TL::ROWB;
+            return TL::tr_at(Kt + lo.tr[db][0] + rofs, Kt + lo.tr[db][1] + rofs);
         }
+    };
+    bf16x8_t ring[RING];
+    static_for<RING>([&](auto ic) __attribute__((always_inline)) { ring[decltype(ic)::value] = operand(ic); });
+    auto next = [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        const bf16x8_t op = ring[i % RING];
+        if constexpr (i + RING < TOT) ring[i % RING] = operand(std::integral_constant<int, i + RING>{});
+        return op;
+    };
+    static_for<2>([&](auto kbc) __attribute__((always_inline)) {
+        constexpr int kb = decltype(kbc)::value;
+        floatx16 s = zero16(), dp = zero16();
+        static_for<NA>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            const bf16x8_t op = next(std::integral_constant<int, kb * PER + r>{});
+            if constexpr (r % 2 == 0) s = mfma(op, qf[r / 2], s);
+            else dp = mfma(op, dof[r / 2], dp);
+            __builtin_amdgcn_sched_barrier(0);
+        });
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lse2));
         if (partial) {             // uniform: FULL tiles skip the mask
@@ -284,15 +308,14 @@ __device__ __forceinline__ void dq_tile(const char *Kt, const char *Vt, const in
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = s[i] * (dp[i] - dlt);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8_t dsf = acc_frag(s, ks);
-            const int rofs = (32 * kb + 16 * ks) * TL::ROWB;
-#pragma unroll
-            for (int db = 0; db < TL::NDB; ++db)
-                acc[db] = mfma(TL::tr_at(Kt + lo.tr[db][0] + rofs, Kt + lo.tr[db][1] + rofs), dsf, acc[db]);
-        }
-    }
+        const bf16x8_t dsf[2] = {acc_frag(s, 0), acc_frag(s, 1)};
+        static_for<2 * NDB>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value, ks = j / NDB, db = j % NDB;
+            const bf16x8_t op = next(std::integral_constant<int, kb * PER + NA + j>{});
+            acc[db] = mfma(op, dsf[ks], acc[db]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    });
 }
 
 template <int D>
