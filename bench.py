@@ -202,6 +202,69 @@ def cpu_baseline(inp, pairs_total: int, budget_s: float = 15.0) -> dict:
                       f"workload is {4 * inp.head_dim * inp.h_q * pairs_total / 1e9:.0f} GFLOP"}
 
 
+def unshared_baseline(inp, pairs_shared: int, fwd_ms: float, steps: int, warmup: int, dev: str) -> dict:
+    """Every root-to-leaf path of the workload unpacked as its own one-segment causal row
+    (padded to a multiple of 128), with the same Q/K/V values, through the same kernel: the
+    packed row's trajectories/s over the unpacked batch's, beside the analytic gains (tokens
+    and attention pairs of the unpacked paths over those of the packed rows)."""
+    import torch
+    import shared_prefix_tree_parent_amd as ta
+    rp, st, ln, par = inp.seg_row_ptr, inp.seg_start, inp.seg_len, inp.seg_parent
+    paths = []
+    for r in range(inp.n_rows):
+        a, b = int(rp[r]), int(rp[r + 1])
+        parents = {int(par[s]) for s in range(a, b) if par[s] >= 0}
+        for leaf in range(b - a):
+            if leaf in parents:
+                continue
+            chain, c = [], leaf
+            while c >= 0:
+                chain.append(c)
+                c = int(par[a + c])
+            chain.reverse()
+            pos = np.concatenate([np.arange(st[a + c], st[a + c] + ln[a + c]) for c in chain])
+            paths.append((r, pos))
+    lens = np.array([len(p) for _, p in paths], np.int64)
+    n, T_u = len(paths), int(-(-lens.max() // 128) * 128)
+    vals = {}
+    for name in ("q", "k", "v"):
+        src = getattr(inp, name)
+        dst = np.zeros((n,) + (T_u,) + src.shape[2:], src.dtype)
+        for i, (r, pos) in enumerate(paths):
+            dst[i, :len(pos)] = src[r, pos]
+        vals[name] = dst
+    conv = (lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)) if inp.dtype == "bf16" \
+        else torch.from_numpy
+    q, k, v = (conv(vals[nm]).to(dev) for nm in ("q", "k", "v"))
+    del vals
+    plan = ta.AttnPlan(np.arange(n + 1), np.zeros(n), lens, np.full(n, -1), n, T_u, inp.h_q, inp.h_kv,
+                       inp.head_dim, inp.dtype, getattr(inp, "scale", 0.0), device=dev)
+    if plan.status() != ta.TREE_OK:
+        raise RuntimeError("unpacked segment table rejected")
+    o = torch.empty_like(q)
+    lse = torch.empty((n, inp.h_q, T_u), dtype=torch.float32, device=dev)
+    call = lambda: ta.tree_attn_fwd(plan.desc, plan.ws, q, k, v, o, lse)
+    for _ in range(warmup):
+        call()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        call()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    pairs_u = int((lens * (lens + 1) // 2).sum())
+    return {"rows": n, "row_len": T_u, "fwd_ms": round(ms, 4),
+            "trajectories_per_s": round(n / (ms * 1e-3), 1),
+            "useful_tflops": round(4.0 * inp.head_dim * inp.h_q * pairs_u / (ms * 1e-3) / 1e12, 2),
+            "packed_over_unpacked_traj_per_s": round(ms / fwd_ms, 3),
+            "token_gain": round(float(lens.sum()) / float(inp.real_len.sum()), 3),
+            "attn_pair_gain": round(pairs_u / pairs_shared, 3),
+            "recipe": "each root-to-leaf path as its own one-segment causal row, padded to a multiple "
+                      "of 128, same Q/K/V values, same kernel"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +278,7 @@ def main() -> int:
     ap.add_argument("--no-packing", action="store_true", help="skip the host packing comparisons")
     ap.add_argument("--no-rope", action="store_true", help="skip the tree_rope timing")
     ap.add_argument("--no-gdn", action="store_true", help="skip the tree_gdn_fwd timing")
+    ap.add_argument("--no-unshared", action="store_true", help="skip the unpacked-paths baseline")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -290,6 +354,18 @@ def main() -> int:
     ms_step = timed(step, args.steps)
     fwd_ms = timed(fwd, args.steps)
     cls_ms = timed(classify, args.steps)
+    # per-call distribution of the forward (one event pair per call)
+    per_call = []
+    for _ in range(args.steps):
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record()
+        fwd()
+        e_.record()
+        e_.synchronize()
+        per_call.append(s_.elapsed_time(e_))
+    fwd_dist = {"calls": len(per_call), "median_ms": round(float(np.median(per_call)), 4),
+                "p10_ms": round(float(np.percentile(per_call, 10)), 4),
+                "p90_ms": round(float(np.percentile(per_call, 90)), 4)}
 
     bwd = None
     if inp.dtype == "bf16" and not args.no_bwd:
@@ -401,6 +477,8 @@ def main() -> int:
         "fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tflops, 2),
         "fwd_trajectories_per_s": round(inp.n_paths / (fwd_ms * 1e-3), 1),
         "classify_us": round(cls_ms * 1e3, 2),
+        "fwd_per_call": fwd_dist,
+        "unshared": None,
         "host_plan_ms": None,
         "roofline": roofline,
         "clock_adjusted": None,
@@ -422,11 +500,22 @@ def main() -> int:
         out["host_plan_ms"] = round(host_plan_ms(args.config), 3)
     except Exception as e:  # host planning is reported, not required for the device step
         out["host_plan_ms"] = f"error: {e}"
+    if not args.no_unshared:
+        out["unshared"] = unshared_baseline(inp, pairs, fwd_ms, max(1, min(args.steps, 10)),
+                                            min(args.warmup, 2), dev)
     if not args.no_packing:
         out["packing"] = packing_report()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, pairs, args.cpu_budget)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 5)
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                one = cpu_baseline(inp, pairs, min(5.0, args.cpu_budget))
+            out["cpu_baseline"]["one_thread"] = {"value": round(one["value"], 6), "unit": one["unit"],
+                                                 "sample": one["sample"]}
+        except Exception as e:  # reported beside the baseline, not required
+            out["cpu_baseline"]["one_thread"] = f"error: {e}"
     print(f"# generated inputs in {gen_s:.1f} s", file=sys.stderr)
     print(json.dumps(out), flush=True)
     return 0
