@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb) {
                     W[tb] = mfma(fy[tb], hb[s], W[tb]);
-                    O[tb] = mfma(fq[tb], hb[s], O[tb]);
+                    O[tb] = mfma(hb[s], fq[tb], O[tb]);       // (Q H)^T = H^T Q^T
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (s + 1 < 8) {
@@ -505,19 +505,16 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
                 }
             }
         }
-        // O = diag(gamma) Q H + P W;  accumulator rows t = 32 tb + 8 q + 4 hh + e.  The next
-        // chunk's U rides along two loads a step.
+        // O^T = (Q H)^T diag(gamma) + W^T P^T, O^T[tb] holding value columns 32 wave + 8 (i/4) +
+        // 4 hh + i%4 (rows) of token 32 tb + lane % 32 (column).  The next chunk's U rides along
+        // two loads a step.
         {
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
+            for (int tb = 0; tb < 2; ++tb) {
+                const float gm = Fs[32 * tb + l32];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 gm = *reinterpret_cast<const float4 *>(Fs + 32 * tb + 8 * q + 4 * hh);
-                    O[tb][4 * q + 0] *= gm.x;
-                    O[tb][4 * q + 1] *= gm.y;
-                    O[tb][4 * q + 2] *= gm.z;
-                    O[tb][4 * q + 3] *= gm.w;
-                }
+                for (int i = 0; i < 16; ++i) O[tb][i] *= gm;
+            }
             bf16x8_t wb[4];
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
@@ -538,21 +535,28 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
                     un[(2 * s + 1) / 4][(2 * s + 1) % 4] = nu[(2 * s + 1) * 64];
                 }
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) O[tb] = mfma(fp[tb], wb[s], O[tb]);
+                for (int tb = 0; tb < 2; ++tb) O[tb] = mfma(wb[s], fp[tb], O[tb]);   // (P W)^T = W^T P^T
                 __builtin_amdgcn_sched_barrier(0);
                 if (s + 1 < 4) {
 #pragma unroll
                     for (int tb = 0; tb < 2; ++tb) fp[tb] = np[tb];
                 }
             }
-            __bf16 *og = a.o + (tok0 * a.H + h) * kGD + col;
+            // four consecutive value columns of one token per 8-byte store
+            __bf16 *og = a.o + (tok0 * a.H + h) * kGD + 32 * wave + 4 * hh;
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
+            for (int tb = 0; tb < 2; ++tb) {
+                const int t = 32 * tb + l32;
+                if (t < n) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int t = 32 * tb + 8 * (i / 4) + 4 * hh + (i % 4);
-                    if (t < n) og[int64_t(t) * a.H * kGD] = static_cast<__bf16>(O[tb][i]);
+                    for (int q = 0; q < 4; ++q) {
+                        bf16x4_t v4;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(O[tb][4 * q + e]);
+                        *reinterpret_cast<bf16x4_t *>(og + int64_t(t) * a.H * kGD + 8 * q) = v4;
+                    }
                 }
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         // H <- gamma_C H + K^T diag(gamma_C / gamma) W; step s = (row block tb, k half ks), the
