@@ -542,21 +542,6 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
                     for (int tb = 0; tb < 2; ++tb) fp[tb] = np[tb];
                 }
             }
-            // four consecutive value columns of one token per 8-byte store
-            __bf16 *og = a.o + (tok0 * a.H + h) * kGD + 32 * wave + 4 * hh;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                const int t = 32 * tb + l32;
-                if (t < n) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        bf16x4_t v4;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(O[tb][4 * q + e]);
-                        *reinterpret_cast<bf16x4_t *>(og + int64_t(t) * a.H * kGD + 8 * q) = v4;
-                    }
-                }
-            }
         }
         __builtin_amdgcn_sched_barrier(0);
         // H <- gamma_C H + K^T diag(gamma_C / gamma) W; step s = (row block tb, k half ks), the
@@ -597,6 +582,25 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
                 if (s + 1 < 4) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) fk[j] = nk[j];
+                }
+            }
+        }
+        {
+            // O of the chunk, stored after the state update's MFMAs are issued (a store issued
+            // right behind the next chunk's copies would hold the wave until they drain): four
+            // consecutive value columns of one token per 8-byte store
+            __bf16 *og = a.o + (tok0 * a.H + h) * kGD + 32 * wave + 4 * hh;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const int t = 32 * tb + l32;
+                if (t < n) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        bf16x4_t v4;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(O[tb][4 * q + e]);
+                        *reinterpret_cast<bf16x4_t *>(og + int64_t(t) * a.H * kGD + 8 * q) = v4;
+                    }
                 }
             }
         }
