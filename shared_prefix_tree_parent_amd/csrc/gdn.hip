@@ -210,30 +210,33 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
     wait_loads();
     __syncthreads();
 
-    // Gram and Q K^T: wave w takes the 32 x 32 block (t block w/2, s block w%2).  The Gram
-    // block is computed transposed (rows s, columns t) so that A^T is stored along lanes.
+    // Gram and Q K^T: wave w takes the 32 x 32 block (t block w/2, s block w%2), both computed
+    // transposed (rows s, columns t): A^T is then stored along lanes, and each lane holds four
+    // consecutive s of one t of P (one 8-byte store).
     const char *Qt = smem + PrepLds::Q_OFF, *Kt = smem + PrepLds::K_OFF;
     const int bt = wave >> 1, bs = wave & 1;
-    floatx16 kkT = zero16(), qk = zero16();
+    floatx16 kkT = zero16(), qkT = zero16();
 #pragma unroll
     for (int ds = 0; ds < kGD / 16; ++ds) {
         const bf16x8_t kb = T128::row_frag(Kt, 32 * bs, lane, ds);
         kkT = mfma(kb, T128::row_frag(Kt, 32 * bt, lane, ds), kkT);
-        qk = mfma(T128::row_frag(Qt, 32 * bt, lane, ds), kb, qk);
+        qkT = mfma(kb, T128::row_frag(Qt, 32 * bt, lane, ds), qkT);
     }
     float *As = reinterpret_cast<float *>(smem + PrepLds::A_OFF);
-    __bf16 *Pout = a.P + (int64_t(c) * a.H + h) * kGC * kGC;
     {
-        const int tA = 32 * bt + (lane & 31), sP = 32 * bs + (lane & 31);
+        const int t = 32 * bt + (lane & 31);
+        __bf16 *Pout = a.P + ((int64_t(c) * a.H + h) * kGC + t) * kGC + 32 * bs + 4 * (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r8 = 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
-            const int sA = 32 * bs + r8, tP = 32 * bt + r8;
-            // gamma_t / gamma_s for s <= t
-            const float decA = __builtin_amdgcn_exp2f((Gs[tA] - Gs[sA]) * kGLog2e);
-            const float decP = __builtin_amdgcn_exp2f((Gs[tP] - Gs[sP]) * kGLog2e);
-            As[sA * kGC + tA] = sA < tA ? Bs[tA] * decA * kkT[i] : 0.f;       // A^T[s][t]
-            Pout[tP * kGC + sP] = static_cast<__bf16>(sP <= tP ? decP * qk[i] : 0.f);
+        for (int i4 = 0; i4 < 4; ++i4) {
+            bf16x4_t p4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * i4 + e, sv = 32 * bs + 8 * i4 + 4 * (lane >> 5) + e;
+                const float dec = __builtin_amdgcn_exp2f((Gs[t] - Gs[sv]) * kGLog2e);   // gamma_t / gamma_s
+                As[sv * kGC + t] = sv < t ? Bs[t] * dec * kkT[i] : 0.f;                  // A^T[s][t]
+                p4[e] = static_cast<__bf16>(sv <= t ? dec * qkT[i] : 0.f);             // P[t][s]
+            }
+            *reinterpret_cast<bf16x4_t *>(Pout + 8 * i4) = p4;
         }
     }
     __syncthreads();

@@ -101,13 +101,16 @@ __device__ __forceinline__ int32x4_t buf_rsrc(const void *base, uint32_t num_rec
     r[3] = kBufFlags;
     return r;
 }
+// The LDS address is wave-uniform; readfirstlane keeps it in an SGPR for the "s" operand.
 __device__ __forceinline__ void buf_to_lds16(int32x4_t r, uint32_t lds, int voff) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %0, 0 offen lds"
-                 :: "s"(r), "s"(lds), "v"(voff) : "memory", "m0");
+                 :: "s"(r), "s"(m), "v"(voff) : "memory", "m0");
 }
 __device__ __forceinline__ void buf_to_lds4(int32x4_t r, uint32_t lds, int voff) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %0, 0 offen lds"
-                 :: "s"(r), "s"(lds), "v"(voff) : "memory", "m0");
+                 :: "s"(r), "s"(m), "v"(voff) : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_base(const char *p) {
     return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
