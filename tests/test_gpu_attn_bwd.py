@@ -110,6 +110,25 @@ def test_bwd_one_segment_and_singletons():
     _full_check(inp, "singleton roots")
 
 
+def test_bwd_split_pairs_d64():
+    """A long shared root at D = 64: its k-tile pairs are seen by >= 32 q-tiles, so the dK/dV
+    pass splits them into query slices whose fp32 partials a reduce pass adds (the slice path
+    at the other head size than config 2's)."""
+    rng = np.random.default_rng(64)
+    inp = _random_inputs(rng, 1, 4160, 4, 1, 64)
+    inp.seg_row_ptr = np.array([0, 5], np.int32)
+    inp.seg_start = np.array([0, 3900, 3960, 4020, 4080], np.int32)
+    inp.seg_len = np.array([3900, 60, 60, 60, 60], np.int32)
+    inp.seg_parent = np.array([-1, 0, 0, 0, 0], np.int32)
+    inp.seg_pos0 = np.array([0, 3900, 3900, 3900, 3900], np.int32)
+    inp.real_len = np.array([4140])
+    plan = ta.attn_plan(inp)
+    BQ, BK = ta.tree_attn_blocks(plan.desc)
+    ptr, _ = _fetch_pairs(plan, (inp.row_len // BK + 1) // 2)
+    assert int(np.diff(ptr).max()) >= 32, "no pair long enough to be split"
+    _full_check(inp, "split pairs D64")
+
+
 @pytest.mark.parametrize("T,Hq,Hkv,D", [(576, 8, 2, 128), (320, 4, 1, 64)])
 def test_bwd_odd_ktile_count(T, Hq, Hkv, D):
     """Rows of an odd number of 64-key tiles: the last k-tile pair has one tile."""
