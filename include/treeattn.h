@@ -212,10 +212,12 @@ int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const 
  *
  * tree_attn_bwd_workspace_size: bytes of the caller-allocated backward workspace `bws`
  *   (256-byte aligned): per-token row terms D and log2-scaled LSE ([R, Hq, T] fp32 each),
- *   the per-pair q-tile lists below, and room for up to 4 fp32 partials of dK and dV per
- *   (pair, KV head) (2 x 4 x 128 x head_dim x 4 bytes): a pair seen by many q-tiles is split
- *   over up to 4 workgroups along its list so that the long pairs of a shared prefix do not
- *   serialize, and the partials are added in a fixed order (results do not depend on timing).
+ *   the per-pair q-tile lists below, and a pool of at most 1024 fp32 partial slots of dK and
+ *   dV per KV head (each 2 x 128 x head_dim x 4 bytes; 128 MiB per KV head at head_dim 128,
+ *   whatever the batch size and row length): a
+ *   pair seen by many q-tiles is split over up to 4 workgroups along its list, so that the
+ *   long pairs of a shared prefix do not serialize, as long as slots remain (longest pairs
+ *   first); the partials are added in a fixed order (results do not depend on timing).
  * tree_attn_bwd_plan: from the forward plan in `ws`, build into `bws`, for every pair of
  *   k-tiles (2p, 2p+1) of a row, the list of q-tiles that see either of them (ascending, entry =
  *   q_tile * 16 + class(2p) * 4 + class(2p+1), classes as in tree_tile_view, a missing k-tile

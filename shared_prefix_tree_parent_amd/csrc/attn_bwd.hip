@@ -62,6 +62,7 @@ struct BwdArgs {
     const uint8_t *kt_kind;
     const int32_t *kp_ptr, *kp_list, *kwork;
     float *part;                   // per-slice dK^T / dV^T partials (BwdLayout::part)
+    const int2 *pslot;             // per pair: (query slices, first partial slot)
     const int32_t *kend, *work, *n_real, *status;
     int32_t T, Hq, Hkv, G, HCH, nQ, nK, nP, L, BQ;
     float c;       // scale * log2(e)
@@ -548,9 +549,6 @@ struct BlockCursor {
     }
 };
 
-// Query slices of a pair whose q-tile list has n entries.
-__device__ __forceinline__ int kv_slices(int n) { return min(kBwdSlices, max(1, n / kBwdSliceEntries)); }
-
 template <int D>
 __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     using TL = Tile<D>;
@@ -566,7 +564,8 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     const int pitem = a.kwork[item];
     const int32_t list_begin = a.kp_ptr[pitem];
     const int NL_pair = a.kp_ptr[pitem + 1] - list_begin;
-    const int n_slices = kv_slices(NL_pair);
+    const int2 ps = a.pslot[pitem];
+    const int n_slices = ps.x;
     if (slice >= n_slices) return;
     const int r = pitem / a.nP, pr = pitem % a.nP;
     const int T = a.T;
@@ -666,7 +665,7 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     if (n_slices > 1) {
         // fp32 partial in accumulator order: float4 ((wave NDB + db) 4 + i4) 64 + lane
         float4 *pp = reinterpret_cast<float4 *>(a.part) +
-                     ((int64_t(pitem) * a.Hkv + g) * kBwdSlices + slice) * 2 * (kKvWaves * TL::NDB * 4 * 64);
+                     (int64_t(ps.y + slice) * a.Hkv + g) * 2 * (kKvWaves * TL::NDB * 4 * 64);
 #pragma unroll
         for (int db = 0; db < TL::NDB; ++db)
 #pragma unroll
@@ -710,17 +709,20 @@ __global__ __launch_bounds__(256) void dkdv_reduce(BwdArgs a) {
     if (a.status[0] != 0) return;
     const int g = blockIdx.x % a.Hkv, item = blockIdx.x / a.Hkv;
     const int pitem = a.kwork[item];
-    const int n_slices = kv_slices(a.kp_ptr[pitem + 1] - a.kp_ptr[pitem]);
+    const int2 ps = a.pslot[pitem];
+    const int n_slices = ps.x;
     if (n_slices == 1) return;
     const int r = pitem / a.nP, pr = pitem % a.nP;
     const int T = a.T;
     constexpr int PER = kKvWaves * TL::NDB * 4 * 64;            // float4 per tensor per slice
-    const float4 *base = reinterpret_cast<const float4 *>(a.part) + (int64_t(pitem) * a.Hkv + g) * kBwdSlices * 2 * PER;
+    // slot (first + sl) of head g: float4 ((first + sl) Hkv + g) 2 PER, dK then dV
+    const float4 *base = reinterpret_cast<const float4 *>(a.part) + (int64_t(ps.y) * a.Hkv + g) * 2 * PER;
     for (int idx = threadIdx.x; idx < PER; idx += blockDim.x) {
         const int lane = idx % 64, i4 = (idx / 64) % 4, db = (idx / 256) % TL::NDB, wave = idx / (256 * TL::NDB);
         float4 sk = base[idx], sv = base[PER + idx];
         for (int sl = 1; sl < n_slices; ++sl) {
-            const float4 k4 = base[sl * 2 * PER + idx], v4 = base[sl * 2 * PER + PER + idx];
+            const float4 k4 = base[int64_t(sl) * a.Hkv * 2 * PER + idx];
+            const float4 v4 = base[int64_t(sl) * a.Hkv * 2 * PER + PER + idx];
             sk.x += k4.x; sk.y += k4.y; sk.z += k4.z; sk.w += k4.w;
             sv.x += v4.x; sv.y += v4.y; sv.z += v4.z; sv.w += v4.w;
         }
@@ -785,6 +787,7 @@ hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b,
     a.kp_list = reinterpret_cast<const int32_t *>(bws + b.kp_list);
     a.kwork = reinterpret_cast<const int32_t *>(bws + b.kwork);
     a.part = reinterpret_cast<float *>(bws + b.part);
+    a.pslot = reinterpret_cast<const int2 *>(bws + b.pslot);
     a.kend = reinterpret_cast<const int32_t *>(ws + w.kend);
     a.work = reinterpret_cast<const int32_t *>(ws + w.work);
     a.n_real = reinterpret_cast<const int32_t *>(ws + w.n_real);

@@ -314,6 +314,46 @@ __global__ void fill_pairs(int32_t nQ, int32_t nK, int32_t nP, int32_t n_items, 
     }
 }
 
+// One workgroup of 1024 threads: query slices and partial slots of every pair, in the
+// longest-first order of kwork.  A pair that splits (bwd_slices > 1) asks for as many slots as
+// slices; slots go out in that order while the running total stays within n_slots, so the
+// granted ranges are disjoint; a pair past the pool runs unsplit.  pslot[item] = (slices,
+// first slot).
+__global__ __launch_bounds__(1024) void assign_slices(int32_t n_items, int32_t n_slots,
+                                                      const int32_t *__restrict__ kp_ptr,
+                                                      const int32_t *__restrict__ kwork, int2 *__restrict__ pslot) {
+    __shared__ int32_t scan[1024];
+    __shared__ int32_t s_base;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_base = 0;
+    __syncthreads();
+    for (int32_t c0 = 0; c0 < n_items; c0 += 1024) {
+        const int32_t t = c0 + tid;
+        int32_t item = -1, sl = 1;
+        if (t < n_items) {
+            item = kwork[t];
+            sl = bwd_slices(kp_ptr[item + 1] - kp_ptr[item]);
+        }
+        const int32_t want = sl > 1 ? sl : 0;
+        scan[tid] = want;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {          // inclusive scan of the requests
+            const int32_t add = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        const int32_t base = s_base + scan[tid] - want;
+        if (item >= 0) {
+            const bool granted = want > 0 && base + want <= n_slots;
+            pslot[item] = granted ? make_int2(sl, base) : make_int2(1, 0);
+        }
+        __syncthreads();
+        if (tid == 1023) s_base += scan[1023];
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, const char *ws, char *bws, hipStream_t s) {
@@ -326,8 +366,10 @@ hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, const char *ws
     if (n_items > 0)
         count_pairs<<<(n_items + 3) / 4, 256, 0, s>>>(w.nQ, w.nK, b.nP, n_items, cmap, kp_ptr);
     finish_pairs<<<1, 1024, 0, s>>>(w.nQ, n_items, kp_ptr, khist, kwork);
-    if (n_items > 0)
+    if (n_items > 0) {
         fill_pairs<<<(n_items + 3) / 4, 256, 0, s>>>(w.nQ, w.nK, b.nP, n_items, cmap, kp_ptr, kp_list);
+        assign_slices<<<1, 1024, 0, s>>>(n_items, b.n_slots, kp_ptr, kwork, reinterpret_cast<int2 *>(bws + b.pslot));
+    }
     return hipGetLastError();
 }
 

@@ -63,9 +63,16 @@ inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_
 // dK/dV query slices: a k-tile pair whose q-tile list has n entries is processed as
 // min(kBwdSlices, max(1, n / kBwdSliceEntries)) workgroups per KV head, each over an equal
 // run of the list; when there is more than one, each writes an fp32 partial and a reduce pass
-// adds them in slice order (deterministic).
+// adds them in slice order (deterministic).  Partials take slots from a pool of at most
+// kBwdMaxSlots (per KV head), handed out to the longest pairs first; a pair that does not fit
+// runs unsplit.
 constexpr int kBwdSlices = 4;
 constexpr int kBwdSliceEntries = 16;
+constexpr int kBwdMaxSlots = 1024;
+__host__ __device__ inline int bwd_slices(int n) {
+    const int k = n / kBwdSliceEntries;
+    return k < 1 ? 1 : (k > kBwdSlices ? kBwdSlices : k);
+}
 
 struct BwdLayout {
     size_t delta = 0;     // float[R*Hq*T]: rowsum(dO * O) per (row, head, token); 0 at pads
@@ -74,9 +81,11 @@ struct BwdLayout {
     size_t kp_list = 0;   // int32[R*nQ*nP]: q-tile*16 + class(2p)*4 + class(2p+1), ascending q-tile
     size_t kwork = 0;     // int32[R*nP]: (row, pair) items, longest list first
     size_t khist = 0;     // int32[nQ + 2]
-    size_t part = 0;      // float[R*nP*Hkv*kBwdSlices*2*128*D]: per-slice dK^T, dV^T partials
+    size_t pslot = 0;     // int2[R*nP]: per pair (query slices, first partial slot)
+    size_t part = 0;      // float[n_slots*Hkv*2*128*D]: per-slice dK^T, dV^T partials
     size_t total = 0;
     int32_t nP = 0;       // k-tile pairs per row: ceil(nK / 2)
+    int32_t n_slots = 0;  // partial slots: min(R*nP*kBwdSlices, kBwdMaxSlots)
 };
 
 inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -90,7 +99,10 @@ inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq, int32_t Hkv, int
     b.kp_list = take(size_t(w.R) * w.nQ * b.nP * sizeof(int32_t));
     b.kwork = take(size_t(w.R) * b.nP * sizeof(int32_t));
     b.khist = take((size_t(w.nQ) + 2) * sizeof(int32_t));
-    b.part = take(size_t(w.R) * b.nP * Hkv * kBwdSlices * 2 * 128 * D * sizeof(float));
+    const int64_t want = int64_t(w.R) * b.nP * kBwdSlices;
+    b.n_slots = static_cast<int32_t>(want < kBwdMaxSlots ? want : kBwdMaxSlots);
+    b.pslot = take(size_t(w.R) * b.nP * 2 * sizeof(int32_t));
+    b.part = take(size_t(b.n_slots) * Hkv * 2 * 128 * D * sizeof(float));
     b.total = off;
     return b;
 }
