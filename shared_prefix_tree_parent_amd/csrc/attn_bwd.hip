@@ -17,7 +17,8 @@
 //     of 32 queries; each block's Q, dO, LSE and D are staged in LDS once for all four waves,
 //     three blocks ahead.  A wave whose k-tile does not see a block's q-tile skips it.  A pair
 //     seen by many q-tiles (a shared prefix's keys are seen by every query after them) is split
-//     into up to kBwdSlices slices so that its work spreads over several CUs;
+//     into up to kBwdSlices slices so that its work spreads over several CUs, as long as the
+//     bounded pool of partial slots lasts (the plan hands the slots to the longest pairs first);
 //   * dkdv_reduce (only where a pair was split): adds the slices' fp32 partials in slice order.
 // Every result is written exactly once (no atomics); gradients of pads are zero.
 //
