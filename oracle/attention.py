@@ -15,7 +15,8 @@ Pads see nothing: O = 0 and LSE = -inf there (reading R7).  Pad Q/K/V contents n
 enter any result.
 
 Two implementations of the same definition:
-  * ``attention_brute`` / ``attention_at``: query by query over anc*(i) from the parent walk;
+  * ``attention_brute`` / ``attention_at``: query by query over anc*(i) from the parent walk
+    (``attention_walk_at`` walks the pointers per query, for rows too long for a bit matrix);
   * ``attention_segment_blocked``: per segment, the keys are all tokens of the segment's
     ancestor segments followed by the segment's own tokens under a causal mask — the
     "one fully visible block per ancestor segment plus a causal triangle over its own
@@ -26,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .mask import PAD, row_parents, visibility_bits
+from .mask import PAD, ancestors, descendants, row_parents, visibility_bits
 
 
 def _get(inp, k):
@@ -96,6 +97,38 @@ def attention_at(inp, samples, max_elems: int = 1 << 24):
             o = np.matmul(P.reshape(Hkv, nq * G, nk), v).reshape(Hkv, nq, G, D) / l_[..., None]
             O[idx[live]] = o.transpose(1, 0, 2, 3).reshape(nq, Hq, D)
             L[idx[live]] = (m_ + np.log(l_)).transpose(1, 0, 2).reshape(nq, Hq)
+    return O, L
+
+
+def attention_walk_at(inp, samples):
+    """O and LSE at chosen (row, position) pairs, all heads, for rows too long for a bit matrix.
+
+    Each query's visible set anc*(i) comes from walking the parent pointers
+    (``mask.ancestors``), then the same softmax and PV as ``attention_at``, one query at a
+    time; memory is O(row length).  Returns (O [n, Hq, D], LSE [n, Hq]) in float64.
+    """
+    Hq, Hkv = int(_get(inp, "h_q")), int(_get(inp, "h_kv"))
+    D, scale = int(_get(inp, "head_dim")), float(_get(inp, "scale"))
+    G = Hq // Hkv
+    O = np.zeros((len(samples), Hq, D))
+    L = np.full((len(samples), Hq), -np.inf)
+    parents: dict = {}
+    for n, (r, i) in enumerate(samples):
+        r, i = int(r), int(i)
+        if r not in parents:
+            parents[r] = row_parents(inp, r)
+        keys = ancestors(parents[r], i)
+        if len(keys) == 0:
+            continue
+        q = _f64(inp, "q", (r, i))                                  # [Hq, D]
+        k = _f64(inp, "k", (r, keys))                               # [nk, Hkv, D]
+        v = _f64(inp, "v", (r, keys))
+        for h in range(Hq):
+            g = h // G
+            s = scale * (k[:, g, :] @ q[h])                         # [nk]
+            m_, l_, p = _softmax_rows(s)
+            O[n, h] = (p @ v[:, g, :]) / l_
+            L[n, h] = m_ + np.log(l_)
     return O, L
 
 
@@ -252,13 +285,17 @@ def attention_backward_blocked(inp, dO, rows=None, dtype=np.float64):
     return dq, dk, dv
 
 
-def attention_grad_at(inp, dO, q_samples=(), k_samples=()):
+def attention_grad_at(inp, dO, q_samples=(), k_samples=(), walk=None):
     """Gradients at chosen positions, for inputs too large for whole rows.
 
-    dQ at (row, query) pairs: the query's own softmax over anc*(i) (parent walk), then
-    dS and dQ as in the closed form.  dK, dV at (row, key) pairs: every query i whose anc*(i)
-    holds the key (a column of the parent-walk bit matrix) contributes; each such query's O and
-    LSE come from ``attention_at``.  Returns (dQ [nq, Hq, D], dK [nk, Hkv, D], dV [nk, Hkv, D]).
+    dQ at (row, query) pairs: the query's own softmax over anc*(i) (walking the parent
+    pointers, so memory stays O(row length)), then dS and dQ as in the closed form.  dK, dV
+    at (row, key) pairs: every query i whose anc*(i) holds the key contributes; each such
+    query's O and LSE come from the forward definition.  The queries of a key are a column of
+    the parent-walk bit matrix, with O / LSE from ``attention_at`` (``walk`` false), or, for
+    rows too long for that matrix, the key's descendants by a forward sweep
+    (``mask.descendants``) with O / LSE from ``attention_walk_at`` (``walk`` true; the default
+    above 32768 tokens).  Returns (dQ [nq, Hq, D], dK [nk, Hkv, D], dV [nk, Hkv, D]).
     """
     Hq, Hkv = int(_get(inp, "h_q")), int(_get(inp, "h_kv"))
     D, scale = int(_get(inp, "head_dim")), float(_get(inp, "scale"))
@@ -273,12 +310,11 @@ def attention_grad_at(inp, dO, q_samples=(), k_samples=()):
         return np.asarray(a, np.float64)
 
     dq = np.zeros((len(q_samples), Hq, D))
-    row_bits: dict = {}
+    row_pi: dict = {}
     for n, (r, i) in enumerate(q_samples):
-        if r not in row_bits:
-            row_bits[r] = visibility_bits(row_parents(inp, r))
-        bits = row_bits[r]
-        keys = np.flatnonzero(np.unpackbits(bits[i])[:T])
+        if r not in row_pi:
+            row_pi[r] = row_parents(inp, r)
+        keys = ancestors(row_pi[r], int(i))
         if len(keys) == 0:
             continue
         qi = _f64(inp, "q", (r, i))                                    # [Hq, D]
@@ -298,12 +334,19 @@ def attention_grad_at(inp, dO, q_samples=(), k_samples=()):
     dk = np.zeros((len(k_samples), Hkv, D))
     dv = np.zeros((len(k_samples), Hkv, D))
     cols, fwd = {}, {}                     # per row: visibility columns, O / LSE of the queries needed
+    if walk is None:
+        walk = T > 32768
     for r in sorted({int(r) for r, _ in k_samples}):
-        bits = visibility_bits(row_parents(inp, r))
-        cols[r] = {int(j): np.flatnonzero(bits[:, int(j) >> 3] & np.uint8(0x80 >> (int(j) & 7)))
-                   for rr, j in k_samples if rr == r}
+        pi = row_parents(inp, r)
+        if walk:
+            cols[r] = {int(j): descendants(pi, int(j)) for rr, j in k_samples if rr == r}
+        else:
+            bits = visibility_bits(pi)
+            cols[r] = {int(j): np.flatnonzero(bits[:, int(j) >> 3] & np.uint8(0x80 >> (int(j) & 7)))
+                       for rr, j in k_samples if rr == r}
         need = np.unique(np.concatenate([np.zeros(0, np.int64)] + list(cols[r].values())))
-        O, L = attention_at(inp, [(r, int(i)) for i in need]) if len(need) else (None, None)
+        at_fn = attention_walk_at if walk else attention_at
+        O, L = at_fn(inp, [(r, int(i)) for i in need]) if len(need) else (None, None)
         fwd[r] = (need, O, L)
     for n, (r, j) in enumerate(k_samples):
         queries = cols[int(r)][int(j)]

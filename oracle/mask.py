@@ -74,6 +74,23 @@ def ancestors(pi: np.ndarray, i: int) -> np.ndarray:
     return np.asarray(out[::-1], np.int64)
 
 
+def descendants(pi: np.ndarray, j: int) -> np.ndarray:
+    """Every i with j in anc*(i), ascending (j itself included unless it is a pad).
+
+    A sweep forward from j: parents precede children, so i descends from j exactly when its
+    parent is j or already marked."""
+    T = len(pi)
+    if pi[j] == PAD:
+        return np.zeros(0, np.int64)
+    mark = np.zeros(T, bool)
+    mark[j] = True
+    for i in range(j + 1, T):
+        p = int(pi[i])
+        if p >= j and mark[p]:
+            mark[i] = True
+    return np.flatnonzero(mark)
+
+
 def row_parents(inp_or_arrays, r: int):
     """pi for row r of a workload (``workloads.RowInputs`` or a plan dict)."""
     g = inp_or_arrays

@@ -4,7 +4,10 @@ import sys
 import numpy as np
 
 import shared_prefix_tree_parent_amd as ta
-from workloads import RowInputs
+from workloads import RowInputs, bf16_bits_from_f32
+
+# The longest row the attention kernels take: 7936 k-tiles of 64 keys.
+LONGEST_ROW = 64 * 7936
 
 
 def log(*a):
@@ -167,3 +170,20 @@ def check_grad(got, ref, real_mask, what, extra=None):
     if pad.any():
         assert np.all(got[pad] == 0), f"{what}: pad gradient not zero"
     return worst, mean_rel
+
+
+def longest_row_inputs(seed=0, Hq=2, Hkv=1, D=128, pads=4):
+    """One bf16 row of LONGEST_ROW tokens: a 300,000-token root, a 32-token child that shares a
+    k-tile with the root's end, and a second child that fills the row but for `pads` pads.  The
+    last real q-tile's tile list holds every k-tile of the row (the longest list there is), with
+    the first child's tile PARTIAL for it."""
+    T = LONGEST_ROW
+    lens = [300_000, 32, T - 300_032 - pads]
+    starts = [0, 300_000, 300_032]
+    inp = RowInputs("longest row", 1, T, Hq, Hkv, D, "bf16", 1 / np.sqrt(D), np.array([0, 3], np.int32),
+                    np.asarray(starts, np.int32), np.asarray(lens, np.int32), np.array([-1, 0, 0], np.int32),
+                    np.array([0, 300_000, 300_000], np.int32), 2, real_len=np.array([T - pads]))
+    rng = np.random.default_rng(seed)
+    for name, H in (("q", Hq), ("k", Hkv), ("v", Hkv)):
+        setattr(inp, name, bf16_bits_from_f32(rng.standard_normal((1, T, H, D), dtype=np.float32)))
+    return inp

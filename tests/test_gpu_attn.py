@@ -13,7 +13,7 @@ import pytest
 import shared_prefix_tree_parent_amd as ta
 from oracle import attention as A
 from oracle import packer as P
-from tests.gpu_util import check_close, log, rows_view, run_fwd
+from tests.gpu_util import LONGEST_ROW, check_close, fetch_tiles, log, longest_row_inputs, rows_view, run_fwd
 from workloads import RowInputs, bf16_bits_from_f32, fill_pads, make_config, random_forest_row
 
 pytestmark = pytest.mark.gpu
@@ -183,3 +183,37 @@ def test_deterministic():
     O1, L1, plan = run_fwd(inp)
     O2, L2, _ = run_fwd(inp, plan=plan, repeats=2)
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_longest_supported_row():
+    # 507,904 tokens: the last real q-tile lists all 7936 k-tiles, the most the forward keeps
+    # in LDS.  Positions are checked one by one by the oracle's parent walk (a bit matrix of
+    # this row would take 32 GB).
+    inp = longest_row_inputs(seed=41)
+    log(f"longest row: {inp.row_len} tokens")
+    O, L, plan = run_fwd(inp)
+    t = fetch_tiles(plan, 1)
+    assert int(np.diff(t["qt_ptr"]).max()) == inp.row_len // t["block_k"] == 7936
+    smp = _samples(inp, np.random.default_rng(41), 12)
+    Oref, Lref = A.attention_walk_at(inp, smp)
+    idx_t = np.array([s[1] for s in smp])
+    check_close(O[0, idx_t], L[0, :, idx_t], Oref, Lref, "bf16", idx_t < inp.real_len[0], "longest row")
+
+
+def test_row_past_the_limit_is_rejected():
+    # Four k-tiles more than the longest supported row (a row length every q-tile size still
+    # divides): the plan is valid, but the forward and the backward refuse it before any launch.
+    import torch
+    T = LONGEST_ROW + 256
+    desc = dict(seg_row_ptr=np.array([0, 1], np.int32), seg_start=np.array([0], np.int32),
+                seg_len=np.array([T], np.int32), seg_parent=np.array([-1], np.int32))
+    plan = ta.AttnPlan(desc["seg_row_ptr"], desc["seg_start"], desc["seg_len"], desc["seg_parent"], 1, T,
+                       2, 1, 128, "bf16", 0.0, 0, 0, "cuda")
+    q = torch.zeros((1, T, 2, 128), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((1, T, 1, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ta.TreeError) as e:
+        ta.attn_fwd(q, kv, kv, plan)
+    assert e.value.code == ta.TREE_E_UNSUPPORTED
+    with pytest.raises(ta.TreeError) as e:
+        plan.bwd_plan()
+    assert e.value.code == ta.TREE_E_UNSUPPORTED

@@ -17,7 +17,7 @@ import shared_prefix_tree_parent_amd as ta
 from oracle import attention as A
 from oracle import mask as M
 from oracle import packer as P
-from tests.gpu_util import check_grad, log, row_term_bound, run_bwd
+from tests.gpu_util import check_grad, log, longest_row_inputs, row_term_bound, run_bwd
 from workloads import RowInputs, bf16_bits_from_f32, draw_grad, f32_from_bf16_bits, make_config, \
     random_forest_row
 
@@ -355,3 +355,34 @@ def test_bwd_fp32_is_unsupported():
     with pytest.raises(ta.TreeError) as e:
         bws_bytes = ta.tree_attn_bwd_workspace_size(plan.desc)
     assert e.value.code == ta.TREE_E_UNSUPPORTED and bws_bytes is None
+
+
+def test_bwd_longest_supported_row():
+    # 507,904 tokens (7936 k-tiles; the dK/dV kernel keeps each pair's q-tile list of up to
+    # 3968 entries in LDS).  dQ at sampled queries and dK / dV at keys of the 32-token child
+    # and of the second child's tail, by the oracle's parent walk and descendant sweep (a bit
+    # matrix of this row would take 32 GB); the identities cover every key.
+    inp = longest_row_inputs(seed=43)
+    log(f"backward longest row: {inp.row_len} tokens")
+    dO = draw_grad(inp, 43)
+    (dq, dk, dv), _ = run_bwd(inp, dO)
+    used = int(inp.real_len[0])
+    qs = [(0, i) for i in (0, 299_999, 300_000, 300_031, 300_032, used - 1, used)]
+    qs += [(0, int(i)) for i in np.random.default_rng(43).integers(0, used, 5)]
+    ks = [(0, j) for j in (300_024, 300_031, used - 5, used - 1, used + 1)]
+    gq, gk, gv = A.attention_grad_at(inp, dO, qs, ks, walk=True)
+    qi, ki = np.array([i for _, i in qs]), np.array([j for _, j in ks])
+    O, _ = A.attention_walk_at(inp, qs)
+    PK, _ = A.attention_walk_at(_with_v_as_k(inp), qs)
+    c_q = row_term_bound(f32_from_bf16_bits(dO[0, qi]), O)
+    pi = M.row_parents(inp, 0)
+    seen = np.unique(np.concatenate([M.descendants(pi, int(j)) for j in ki]))
+    Os, _ = A.attention_walk_at(inp, [(0, int(i)) for i in seen])
+    f = _as_float(inp)
+    up = np.zeros(dO.shape, np.float32)
+    up[0, seen] = row_term_bound(f32_from_bf16_bits(dO[0, seen]), Os) * np.abs(f.q[0, seen])
+    _, _, cq = A.attention_grad_at(f, up, [], ks, walk=True)
+    check_grad(dq[0, qi], gq, qi < used, "longest row dQ", extra=2 * inp.scale * c_q * np.abs(PK))
+    check_grad(dk[0, ki], gk, ki < used, "longest row dK", extra=2 * inp.scale * cq)
+    check_grad(dv[0, ki], gv, ki < used, "longest row dV")
+    _identities(inp, dO, dk, dv, "longest row")

@@ -231,3 +231,43 @@ def test_attention_at_matches_blocked_on_config2_sample():
             assert np.abs(L[n] - Lb[0, :, p]).max() < 1e-10
         else:
             assert np.all(L[n] == -np.inf) and np.all(Lb[0, :, p] == -np.inf)
+
+
+def test_walk_at_is_causal_attention_along_each_path():
+    # Root 0..29, children 30..49 and 50..74 of the root, a grandchild 75..84 under the first
+    # child, pads 85..95: every root-to-leaf path must equal torch's causal attention over the
+    # path's tokens, and pads see nothing.
+    T = 96
+    inp = _row([0, 30, 50, 75], [30, 20, 25, 10], [-1, 0, 0, 1], [0, 30, 30, 50], T, Hq=4, Hkv=2, D=16,
+               seed=11)
+    O, L = A.attention_walk_at(inp, [(0, i) for i in range(T)])
+    for path in (list(range(30)) + list(range(30, 50)) + list(range(75, 85)),
+                 list(range(30)) + list(range(50, 75))):
+        o, l = _torch_causal(inp.q[0, path].astype(np.float64), inp.k[0, path].astype(np.float64),
+                             inp.v[0, path].astype(np.float64), inp.scale)
+        assert np.abs(O[path] - o).max() < 1e-10
+        assert np.abs(L[path].T - l).max() < 1e-10
+    assert np.all(O[85:] == 0) and np.all(L[85:] == -np.inf)
+
+
+def test_walk_at_matches_attention_at_on_config2_sample():
+    inp = make_config(2)
+    rng = np.random.default_rng(1)
+    used = int(inp.real_len[0])
+    smp = [(0, p) for p in sorted(set(rng.integers(0, used, 12).tolist()) | {0, used - 1, used})]
+    Ow, Lw = A.attention_walk_at(inp, smp)
+    Oa, La = A.attention_at(inp, smp)
+    assert np.abs(Ow - Oa).max() < 1e-10
+    real = np.isfinite(La)
+    assert np.array_equal(real, np.isfinite(Lw)) and np.abs(Lw[real] - La[real]).max() < 1e-10
+
+
+def test_descendants_is_the_bit_matrix_column():
+    rng = np.random.default_rng(12)
+    for _ in range(4):
+        st_, ln, par, p0, used = random_forest_row(rng, 256, max_segs=12, max_len=40, fill=0.8)
+        pi = M.token_parents(st_, ln, par, 256)
+        bits = M.visibility_bits(pi)
+        for j in list(rng.integers(0, 256, 20)) + [0, used - 1, 255]:
+            col = np.flatnonzero(bits[:, j >> 3] & np.uint8(0x80 >> (j & 7)))
+            assert np.array_equal(M.descendants(pi, int(j)), col)

@@ -186,9 +186,10 @@ def test_sampled_form_matches_whole_rows():
     dq, dk, dv = A.attention_backward_blocked(inp, dO)
     qs = [(0, int(i)) for i in rng.integers(0, used, 6)] + [(0, used)]
     ks = [(0, int(j)) for j in rng.integers(0, used, 6)] + [(0, 0), (0, used + 3)]
-    gq, gk, gv = A.attention_grad_at(inp, dO, qs, ks)
-    for n, (_, i) in enumerate(qs):
-        assert np.abs(gq[n] - dq[0, i]).max() < 1e-9
-    for n, (_, j) in enumerate(ks):
-        assert np.abs(gk[n] - dk[0, j]).max() < 1e-9
-        assert np.abs(gv[n] - dv[0, j]).max() < 1e-9
+    for walk in (False, True):          # key columns from the bit matrix, then by the sweep
+        gq, gk, gv = A.attention_grad_at(inp, dO, qs, ks, walk=walk)
+        for n, (_, i) in enumerate(qs):
+            assert np.abs(gq[n] - dq[0, i]).max() < 1e-9
+        for n, (_, j) in enumerate(ks):
+            assert np.abs(gk[n] - dk[0, j]).max() < 1e-9
+            assert np.abs(gv[n] - dv[0, j]).max() < 1e-9
