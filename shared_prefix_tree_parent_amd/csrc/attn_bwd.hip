@@ -18,7 +18,9 @@
 //     three blocks ahead.  A wave whose k-tile does not see a block's q-tile skips it.  A pair
 //     seen by many q-tiles (a shared prefix's keys are seen by every query after them) is split
 //     into up to kBwdSlices slices so that its work spreads over several CUs, as long as the
-//     bounded pool of partial slots lasts (the plan hands the slots to the longest pairs first);
+//     bounded pool of partial slots lasts (the plan hands the slots to the longest pairs first).
+//     The grid follows the plan's list of (pair, slice) units, so no workgroup is launched for
+//     a slice that does not exist; only a short surplus at the end of the grid exits at once;
 //   * dkdv_reduce (only where a pair was split): adds the slices' fp32 partials in slice order.
 // Every result is written exactly once (no atomics); gradients of pads are zero.
 //
@@ -64,6 +66,8 @@ struct BwdArgs {
     const int32_t *kp_ptr, *kp_list, *kwork;
     float *part;                   // per-slice dK^T / dV^T partials (BwdLayout::part)
     const int2 *pslot;             // per pair: (query slices, first partial slot)
+    const int2 *units;             // (pair item, slice) of every dK/dV workgroup, work order
+    const int32_t *n_units;        // units in use; workgroups past them exit
     const int32_t *kend, *work, *n_real, *status;
     int32_t T, Hq, Hkv, G, HCH, nQ, nK, nP, L, BQ;
     float c;       // scale * log2(e)
@@ -560,14 +564,14 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
-    const int g = blockIdx.x % a.Hkv, slice = (blockIdx.x / a.Hkv) % kBwdSlices;
-    const int item = blockIdx.x / a.Hkv / kBwdSlices;
-    const int pitem = a.kwork[item];
+    const int g = blockIdx.x % a.Hkv, unit = blockIdx.x / a.Hkv;
+    if (unit >= a.n_units[0]) return;                    // the grid's surplus (end of the grid)
+    const int2 us = a.units[unit];
+    const int pitem = us.x, slice = us.y;
     const int32_t list_begin = a.kp_ptr[pitem];
     const int NL_pair = a.kp_ptr[pitem + 1] - list_begin;
     const int2 ps = a.pslot[pitem];
     const int n_slices = ps.x;
-    if (slice >= n_slices) return;
     const int r = pitem / a.nP, pr = pitem % a.nP;
     const int T = a.T;
     const int n_real = a.n_real[r];
@@ -742,7 +746,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce(BwdArgs a) {
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, hipStream_t s) {
+hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, int n_units_k, hipStream_t s) {
     const int64_t n_threads = int64_t(R) * a.T * a.Hq * (D / 8);
     if (n_threads > 0) {
         row_terms<D><<<int((n_threads + 255) / 256), 256, 0, s>>>(
@@ -764,7 +768,7 @@ hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, hipSt
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(dkdv_kernel<D>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return e;
-        dkdv_kernel<D><<<n_items_k * kBwdSlices, kKvWaves * 64, smem, s>>>(a);
+        dkdv_kernel<D><<<n_units_k, kKvWaves * 64, smem, s>>>(a);
         dkdv_reduce<D><<<n_items_k, 256, 0, s>>>(a);
     }
     return hipGetLastError();
@@ -789,6 +793,8 @@ hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b,
     a.kwork = reinterpret_cast<const int32_t *>(bws + b.kwork);
     a.part = reinterpret_cast<float *>(bws + b.part);
     a.pslot = reinterpret_cast<const int2 *>(bws + b.pslot);
+    a.units = reinterpret_cast<const int2 *>(bws + b.units);
+    a.n_units = reinterpret_cast<const int32_t *>(bws + b.n_units);
     a.kend = reinterpret_cast<const int32_t *>(ws + w.kend);
     a.work = reinterpret_cast<const int32_t *>(ws + w.work);
     a.n_real = reinterpret_cast<const int32_t *>(ws + w.n_real);
@@ -800,11 +806,12 @@ hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b,
     a.c = sh.scale * kLog2e;
     const int64_t n_q = int64_t(sh.R) * w.nQ * a.L;
     const int64_t n_k = int64_t(sh.R) * b.nP * sh.Hkv;
-    if (n_q > INT32_MAX || n_k * kBwdSlices > INT32_MAX) return hipErrorInvalidValue;
+    const int64_t n_u = b.max_units * sh.Hkv;
+    if (n_q > INT32_MAX || n_k > INT32_MAX || n_u > INT32_MAX) return hipErrorInvalidValue;
     if (sh.dtype != TREE_DT_BF16) return hipErrorInvalidValue;
     if (sh.BQ % kQBlk != 0) return hipErrorInvalidValue;
-    if (sh.D == 128) return launch_d<128>(a, sh.R, int(n_q), int(n_k), s);
-    if (sh.D == 64) return launch_d<64>(a, sh.R, int(n_q), int(n_k), s);
+    if (sh.D == 128) return launch_d<128>(a, sh.R, int(n_q), int(n_k), int(n_u), s);
+    if (sh.D == 64) return launch_d<64>(a, sh.R, int(n_q), int(n_k), int(n_u), s);
     return hipErrorInvalidValue;
 }
 

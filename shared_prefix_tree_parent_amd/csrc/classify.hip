@@ -269,7 +269,9 @@ __global__ void count_pairs(int32_t nQ, int32_t nK, int32_t nP, int32_t n_items,
     if (lane == 0) kp_ptr[item + 1] = cnt;
 }
 
-// One workgroup: scan of the pair counts and the longest-first work list.
+// One workgroup: scan of the pair counts and the longest-first work list.  The scatter into
+// the length buckets is stable (pairs of equal length keep their index order), so the work
+// order, and with it the split pairs and their partial slots, is the same on every run.
 __global__ void finish_pairs(int32_t nQ, int32_t n_items, int32_t *__restrict__ kp_ptr,
                              int32_t *__restrict__ khist, int32_t *__restrict__ kwork) {
     __shared__ int32_t part[1024 / 64];
@@ -287,9 +289,35 @@ __global__ void finish_pairs(int32_t nQ, int32_t n_items, int32_t *__restrict__ 
     block_scan(nQ + 1, khist, part, &carry);
     __threadfence_block();
     __syncthreads();
-    for (int32_t t = threadIdx.x; t < n_items; t += blockDim.x) {
-        const int32_t c = kp_ptr[t + 1] - kp_ptr[t];
-        kwork[atomicAdd(&khist[nQ - c], 1)] = t;
+    // khist[b] is now the first position of bucket b = nQ - length.  Chunks of blockDim.x
+    // pairs in index order; inside a chunk, a lane's rank among the earlier lanes of its wave
+    // with the same bucket comes from ballots, and the waves take their positions one after
+    // another.
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int32_t c0 = 0; c0 < n_items; c0 += blockDim.x) {
+        const int32_t t = c0 + threadIdx.x;
+        const bool valid = t < n_items;
+        const int32_t key = valid ? nQ - (kp_ptr[t + 1] - kp_ptr[t]) : -1;
+        int32_t rank = 0, cnt = 0;
+        uint64_t left = __ballot(valid);
+        while (left) {                                   // one pass per distinct bucket
+            const int32_t k = __shfl(key, __ffsll(static_cast<unsigned long long>(left)) - 1, 64);
+            const uint64_t m = __ballot(valid && key == k);
+            if (valid && key == k) {
+                rank = __popcll(m & below);
+                cnt = __popcll(m);
+            }
+            left &= ~m;
+        }
+        for (int w2 = 0; w2 < nw; ++w2) {
+            if (wv == w2 && valid) kwork[khist[key] + rank] = t;
+            __threadfence_block();
+            __syncthreads();
+            if (wv == w2 && valid && rank == cnt - 1) khist[key] += cnt;
+            __threadfence_block();
+            __syncthreads();
+        }
     }
 }
 
@@ -314,18 +342,38 @@ __global__ void fill_pairs(int32_t nQ, int32_t nK, int32_t nP, int32_t n_items, 
     }
 }
 
+// Inclusive scan of one value per thread over a workgroup of 1024 threads (LDS array `buf`).
+__device__ int32_t scan1024(int32_t v, int32_t *buf) {
+    const int tid = threadIdx.x;
+    buf[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int32_t add = tid >= off ? buf[tid - off] : 0;
+        __syncthreads();
+        buf[tid] += add;
+        __syncthreads();
+    }
+    return buf[tid];
+}
+
 // One workgroup of 1024 threads: query slices and partial slots of every pair, in the
 // longest-first order of kwork.  A pair that splits (bwd_slices > 1) asks for as many slots as
 // slices; slots go out in that order while the running total stays within n_slots, so the
 // granted ranges are disjoint; a pair past the pool runs unsplit.  pslot[item] = (slices,
-// first slot).
-__global__ __launch_bounds__(1024) void assign_slices(int32_t n_items, int32_t n_slots,
+// first slot).  units lists (item, slice) for every slice of every pair in the same order, one
+// dK/dV workgroup each; n_units[0] = their number (at most max_units: the slices beyond the
+// first belong to granted pairs and so fit in the n_slots pool).
+__global__ __launch_bounds__(1024) void assign_slices(int32_t n_items, int32_t n_slots, int64_t max_units,
                                                       const int32_t *__restrict__ kp_ptr,
-                                                      const int32_t *__restrict__ kwork, int2 *__restrict__ pslot) {
+                                                      const int32_t *__restrict__ kwork, int2 *__restrict__ pslot,
+                                                      int2 *__restrict__ units, int32_t *__restrict__ n_units) {
     __shared__ int32_t scan[1024];
-    __shared__ int32_t s_base;
+    __shared__ int32_t s_base, s_extra;
     const int tid = threadIdx.x;
-    if (tid == 0) s_base = 0;
+    if (tid == 0) {
+        s_base = 0;
+        s_extra = 0;
+    }
     __syncthreads();
     for (int32_t c0 = 0; c0 < n_items; c0 += 1024) {
         const int32_t t = c0 + tid;
@@ -335,22 +383,30 @@ __global__ __launch_bounds__(1024) void assign_slices(int32_t n_items, int32_t n
             sl = bwd_slices(kp_ptr[item + 1] - kp_ptr[item]);
         }
         const int32_t want = sl > 1 ? sl : 0;
-        scan[tid] = want;
+        const int32_t req = scan1024(want, scan);            // inclusive scan of the requests
+        const int32_t base = s_base + req - want;
+        const bool granted = item >= 0 && want > 0 && base + want <= n_slots;
+        const int32_t S = granted ? sl : 1;
+        const int32_t req_all = scan[1023];
         __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {          // inclusive scan of the requests
-            const int32_t add = tid >= off ? scan[tid - off] : 0;
-            __syncthreads();
-            scan[tid] += add;
-            __syncthreads();
-        }
-        const int32_t base = s_base + scan[tid] - want;
+        const int32_t ext = scan1024(S - 1, scan);          // inclusive scan of the extra slices
+        const int64_t first = int64_t(t) + s_extra + ext - (S - 1);
         if (item >= 0) {
-            const bool granted = want > 0 && base + want <= n_slots;
             pslot[item] = granted ? make_int2(sl, base) : make_int2(1, 0);
+            for (int32_t j = 0; j < S; ++j)
+                if (first + j < max_units) units[first + j] = make_int2(item, j);
+        }
+        const int32_t ext_all = scan[1023];
+        __syncthreads();
+        if (tid == 0) {
+            s_base += req_all;
+            s_extra += ext_all;
         }
         __syncthreads();
-        if (tid == 1023) s_base += scan[1023];
-        __syncthreads();
+    }
+    if (tid == 0) {
+        const int64_t n = int64_t(n_items) + s_extra;
+        n_units[0] = static_cast<int32_t>(n < max_units ? n : max_units);
     }
 }
 
@@ -368,8 +424,11 @@ hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, const char *ws
     finish_pairs<<<1, 1024, 0, s>>>(w.nQ, n_items, kp_ptr, khist, kwork);
     if (n_items > 0) {
         fill_pairs<<<(n_items + 3) / 4, 256, 0, s>>>(w.nQ, w.nK, b.nP, n_items, cmap, kp_ptr, kp_list);
-        assign_slices<<<1, 1024, 0, s>>>(n_items, b.n_slots, kp_ptr, kwork, reinterpret_cast<int2 *>(bws + b.pslot));
     }
+    // Always: an empty batch still needs n_units = 0 for the dK/dV launch.
+    assign_slices<<<1, 1024, 0, s>>>(n_items, b.n_slots, b.max_units, kp_ptr, kwork,
+                                     reinterpret_cast<int2 *>(bws + b.pslot), reinterpret_cast<int2 *>(bws + b.units),
+                                     reinterpret_cast<int32_t *>(bws + b.n_units));
     return hipGetLastError();
 }
 

@@ -65,7 +65,10 @@ inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_
 // run of the list; when there is more than one, each writes an fp32 partial and a reduce pass
 // adds them in slice order (deterministic).  Partials take slots from a pool of at most
 // kBwdMaxSlots (per KV head), handed out to the longest pairs first; a pair that does not fit
-// runs unsplit.
+// runs unsplit.  The plan lists the (pair, slice) units in work order, so the dK/dV launch
+// has one workgroup per unit and KV head (plus a surplus at the end of the grid that exits at
+// once): at most R*nP + min(3*R*nP, kBwdMaxSlots) units, since only granted pairs have more
+// than one slice and their slices fit in the pool.
 constexpr int kBwdSlices = 4;
 constexpr int kBwdSliceEntries = 16;
 constexpr int kBwdMaxSlots = 1024;
@@ -82,10 +85,13 @@ struct BwdLayout {
     size_t kwork = 0;     // int32[R*nP]: (row, pair) items, longest list first
     size_t khist = 0;     // int32[nQ + 2]
     size_t pslot = 0;     // int2[R*nP]: per pair (query slices, first partial slot)
+    size_t units = 0;     // int2[max_units]: (pair item, slice) in work order
+    size_t n_units = 0;   // int32[1]: units in use
     size_t part = 0;      // float[n_slots*Hkv*2*128*D]: per-slice dK^T, dV^T partials
     size_t total = 0;
     int32_t nP = 0;       // k-tile pairs per row: ceil(nK / 2)
     int32_t n_slots = 0;  // partial slots: min(R*nP*kBwdSlices, kBwdMaxSlots)
+    int64_t max_units = 0;   // R*nP + min(3*R*nP, kBwdMaxSlots)
 };
 
 inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -102,6 +108,10 @@ inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq, int32_t Hkv, int
     const int64_t want = int64_t(w.R) * b.nP * kBwdSlices;
     b.n_slots = static_cast<int32_t>(want < kBwdMaxSlots ? want : kBwdMaxSlots);
     b.pslot = take(size_t(w.R) * b.nP * 2 * sizeof(int32_t));
+    const int64_t n_items = int64_t(w.R) * b.nP;
+    b.max_units = n_items + (3 * n_items < kBwdMaxSlots ? 3 * n_items : kBwdMaxSlots);
+    b.units = take(size_t(b.max_units) * 2 * sizeof(int32_t));
+    b.n_units = take(sizeof(int32_t));
     b.part = take(size_t(b.n_slots) * Hkv * 2 * 128 * D * sizeof(float));
     b.total = off;
     return b;

@@ -348,6 +348,30 @@ def test_bwd_deterministic():
         assert np.array_equal(a, b)
 
 
+def test_bwd_slot_pool_overflow():
+    # Fourteen causal rows of 4096 tokens with 8 query heads per KV head (32-position q-tiles):
+    # most k-tile pairs ask for 4 query slices, more than the 1024 partial slots in all, so the
+    # pairs past the pool run unsplit.  Two plans built independently must give bit-identical
+    # gradients (which pairs split may not depend on run-to-run ordering), and sampled
+    # positions must match the oracle.
+    rng = np.random.default_rng(61)
+    R, T, used = 14, 4096, 4000
+    inp = RowInputs("pool overflow", R, T, 8, 1, 64, "bf16", 1 / 8.0, np.arange(R + 1, dtype=np.int32),
+                    np.zeros(R, np.int32), np.full(R, used, np.int32), np.full(R, -1, np.int32),
+                    np.zeros(R, np.int32), R, real_len=np.full(R, used))
+    for name, H in (("q", 8), ("k", 1), ("v", 1)):
+        setattr(inp, name, bf16_bits_from_f32(rng.standard_normal((R, T, H, 64), dtype=np.float32)))
+    ptr, _ = _want_pairs(inp, 32, 64)
+    wants = sum(min(4, n // 16) for n in np.diff(ptr) if n // 16 > 1)
+    assert wants > 1024, wants
+    dO = draw_grad(inp, 61)
+    g1, _ = run_bwd(inp, dO)
+    g2, _ = run_bwd(inp, dO)
+    for a, b in zip(g1, g2):
+        assert np.array_equal(a, b)
+    _sampled_bwd(inp, inp, "pool overflow", seed=61, n_q=96, n_k=4, max_queries=512)
+
+
 def test_bwd_fp32_is_unsupported():
     inp = make_config(1)
     plan = ta.attn_plan(inp)
