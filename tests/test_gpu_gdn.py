@@ -130,6 +130,28 @@ def test_gdn_config4_planner_rows():
     check(got[sel], want[sel], real[sel], "config 4 rows (planner)")
 
 
+def test_gdn_empty_row_and_sixteen_heads():
+    """Three rows, the middle one empty (no segments: every position a pad), at the 16 heads
+    the benchmark runs."""
+    rng = np.random.default_rng(21)
+    starts, lens, pars, pos0, rp, used = [], [], [], [], [0], []
+    for r in range(3):
+        if r == 1:
+            rp.append(rp[-1]); used.append(0)
+            continue
+        st, ln, par, p0, u = random_forest_row(rng, 512, max_segs=10, max_len=150, fill=0.9)
+        starts.append(st); lens.append(ln); pars.append(par); pos0.append(p0)
+        rp.append(rp[-1] + len(st)); used.append(u)
+    cat = lambda xs: np.concatenate(xs).astype(np.int32)
+    rows = RowInputs("gdn", 3, 512, 1, 1, 128, "bf16", 0.0, np.asarray(rp, np.int32), cat(starts), cat(lens),
+                     cat(pars), cat(pos0), 0, real_len=np.asarray(used))
+    gin = draw_gdn(rows, heads=16, seed=21)
+    got, _ = run_gdn(gin, sentinel=7.0)
+    real = _real(rows)
+    assert np.all(got[1] == 7.0) and np.all(got[~real] == 7.0)
+    check(got, Gd.gdn_forward(gin), real, "empty middle row, 16 heads")
+
+
 def test_gdn_pads_untouched_and_isolated():
     rng = np.random.default_rng(5)
     rows = _forest_rows(rng, 2, 256, 8, 60, 0.6)
