@@ -354,9 +354,9 @@ def main() -> int:
     ms_step = timed(step, args.steps)
     fwd_ms = timed(fwd, args.steps)
     cls_ms = timed(classify, args.steps)
-    # per-call distribution of the forward (one event pair per call)
+    # per-call distribution of the forward (one event pair per call, at least 100 calls)
     per_call = []
-    for _ in range(args.steps):
+    for _ in range(max(100, args.steps)):
         s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s_.record()
         fwd()
