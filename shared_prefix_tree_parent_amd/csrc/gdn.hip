@@ -241,34 +241,87 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
     }
     __syncthreads();
 
-    // T = (I + A)^-1 by forward substitution on the identity's columns: wave 0, lane c takes
-    // column c, A^T rows read one ahead (no barrier inside).
-    if (wave == 0) {
-        float x[kGC];
+    // T = (I + A)^-1 in 16 x 16 blocks, all four waves.  As holds A^T in its strict upper
+    // triangle (As[s][t] = A[t][s], s < t); T is built in row-major form (As[t][c] = T[t][c]) in
+    // the lower triangle, which A^T does not use.
+    //  1. Wave b inverts the diagonal block: D_b = (I + A_bb)^-1 by forward substitution (lane
+    //     c < 16 takes column c, A^T rows read one ahead) and stores the whole 16 x 16 block
+    //     (the block's A^T entries are read by no one else).
+    //  2. Below the diagonal, by distance d = i - j = 1, 2, 3 (one barrier each), wave j takes
+    //     block (i, j): M = sum_{k=j}^{i-1} A_ik T_kj (T_jj = D_j), staged in the free Q tile,
+    //     then T_ij = -D_i M.  Lane (r, q) computes row r, columns 4q .. 4q + 3.
+    //  3. The blocks above the diagonal, still A^T, are cleared.
+    {
+        constexpr int NB16 = kGC / 16;
+        if (lane < 16) {
+            const int b0 = 16 * wave;
+            float x[16];
 #pragma unroll
-        for (int t = 0; t < kGC; ++t) x[t] = t == lane ? 1.f : 0.f;
-        float ar[2][kGC];
-        auto load_row = [&](auto sc_, float(&dst)[kGC]) __attribute__((always_inline)) {
-            constexpr int s_ = decltype(sc_)::value;
-            static_for<(kGC - (s_ + 1) / 4 * 4) / 4>([&](auto qc) __attribute__((always_inline)) {
-                constexpr int t4 = (s_ + 1) / 4 * 4 + 4 * decltype(qc)::value;
-                const float4 v = *reinterpret_cast<const float4 *>(As + s_ * kGC + t4);
-                dst[t4] = v.x; dst[t4 + 1] = v.y; dst[t4 + 2] = v.z; dst[t4 + 3] = v.w;
+            for (int t = 0; t < 16; ++t) x[t] = t == lane ? 1.f : 0.f;
+            float ar[2][16];
+            auto load_row = [&](auto sc_, float(&dst)[16]) __attribute__((always_inline)) {
+                constexpr int s_ = decltype(sc_)::value;
+                static_for<(16 - (s_ + 1) / 4 * 4) / 4>([&](auto qc) __attribute__((always_inline)) {
+                    constexpr int t4 = (s_ + 1) / 4 * 4 + 4 * decltype(qc)::value;
+                    const float4 v = *reinterpret_cast<const float4 *>(As + (b0 + s_) * kGC + b0 + t4);
+                    dst[t4] = v.x; dst[t4 + 1] = v.y; dst[t4 + 2] = v.z; dst[t4 + 3] = v.w;
+                });
+            };
+            load_row(std::integral_constant<int, 0>{}, ar[0]);
+            static_for<15>([&](auto sc) __attribute__((always_inline)) {
+                constexpr int s0 = decltype(sc)::value;
+                if constexpr (s0 + 1 < 15) load_row(std::integral_constant<int, s0 + 1>{}, ar[(s0 + 1) & 1]);
+                static_for<15 - s0>([&](auto tc) __attribute__((always_inline)) {
+                    constexpr int t = s0 + 1 + decltype(tc)::value;
+                    x[t] = fmaf(-ar[s0 & 1][t], x[s0], x[t]);
+                });
             });
-        };
-        load_row(std::integral_constant<int, 0>{}, ar[0]);
-        static_for<kGC - 1>([&](auto sc) __attribute__((always_inline)) {
-            constexpr int s0 = decltype(sc)::value;
-            if constexpr (s0 + 1 < kGC - 1) load_row(std::integral_constant<int, s0 + 1>{}, ar[(s0 + 1) & 1]);
-            static_for<kGC - 1 - s0>([&](auto tc) __attribute__((always_inline)) {
-                constexpr int t = s0 + 1 + decltype(tc)::value;
-                x[t] = fmaf(-ar[s0 & 1][t], x[s0], x[t]);
-            });
-            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) As[(b0 + t) * kGC + b0 + lane] = x[t];
+        }
+        float *Ms = reinterpret_cast<float *>(smem + PrepLds::Q_OFF) + wave * 256;   // 16 x 16 per wave
+        const int r = lane >> 2, c0 = 4 * (lane & 3);
+        static_for<NB16 - 1>([&](auto dc) __attribute__((always_inline)) {
+            constexpr int d = decltype(dc)::value + 1;
+            __syncthreads();
+            if (wave < NB16 - d) {
+                const int j = wave, i = wave + d;
+                float m[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < d; ++kk) {
+                    const int k = j + kk;
+#pragma unroll
+                    for (int mm = 0; mm < 16; ++mm) {
+                        const float aik = As[(16 * k + mm) * kGC + 16 * i + r];              // A[16i + r][16k + mm]
+                        const float4 tk = *reinterpret_cast<const float4 *>(As + (16 * k + mm) * kGC + 16 * j + c0);
+                        m[0] = fmaf(aik, tk.x, m[0]); m[1] = fmaf(aik, tk.y, m[1]);
+                        m[2] = fmaf(aik, tk.z, m[2]); m[3] = fmaf(aik, tk.w, m[3]);
+                    }
+                }
+                *reinterpret_cast<float4 *>(Ms + r * 16 + c0) = make_float4(m[0], m[1], m[2], m[3]);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                float t4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int mm = 0; mm < 16; ++mm) {
+                    const float di = As[(16 * i + r) * kGC + 16 * i + mm];                  // D_i[r][mm]
+                    const float4 mr = *reinterpret_cast<const float4 *>(Ms + mm * 16 + c0);
+                    t4[0] = fmaf(di, mr.x, t4[0]); t4[1] = fmaf(di, mr.y, t4[1]);
+                    t4[2] = fmaf(di, mr.z, t4[2]); t4[3] = fmaf(di, mr.w, t4[3]);
+                }
+                *reinterpret_cast<float4 *>(As + (16 * i + r) * kGC + 16 * j + c0) =
+                    make_float4(-t4[0], -t4[1], -t4[2], -t4[3]);
+            }
         });
-        // all of T: the A^T rows are no longer read
-#pragma unroll
-        for (int t = 0; t < kGC; ++t) As[t * kGC + lane] = x[t];
+        __syncthreads();
+        // clear the blocks above the diagonal (i < j): 6 blocks x 64 float4
+        for (int e = tid; e < 6 * 64; e += 256) {
+            const int blk = e >> 6, w = e & 63, rr = w >> 2, cc = 4 * (w & 3);
+            const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+            const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+            *reinterpret_cast<float4 *>(As + (16 * bi + rr) * kGC + 16 * bj + cc) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
     __syncthreads();
 
