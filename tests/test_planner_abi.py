@@ -185,3 +185,12 @@ def test_no_oracle_import_in_product():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # One GPU is measured; asking for more exits with a message before any device work.
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run(["python3", os.path.join(root, "bench.py"), "--gpus", "2"], cwd=root,
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=300)
+    assert p.returncode == 2
+    assert "one GPU" in p.stdout
