@@ -18,15 +18,16 @@ namespace {
 constexpr int kStatusLayout = 1;
 constexpr int kMaxLdsSegs = 2048;   // segments of one row kept in LDS while validating
 
-// One workgroup per row: thread 0 checks that the table is a pre-order forest laid out from
-// token 0 and writes every segment's subtree end (the row's segments are staged in LDS when
-// they fit).  A row that fails the check gets n_real = -1 (then kend[j] = j: all skipped).
+// One workgroup per row: checks that the table is a pre-order forest laid out from token 0 and
+// writes every segment's subtree end.  With the row's segments in LDS (up to kMaxLdsSegs),
+// every segment is checked by its own thread; otherwise one thread walks them in global
+// memory.  A row that fails the check gets n_real = -1 (then kend[j] = j: all skipped).
 __global__ void validate_rows(int32_t R, int32_t T, int32_t n_segs, const int32_t *__restrict__ rp,
                               const int32_t *__restrict__ st, const int32_t *__restrict__ ln,
                               const int32_t *__restrict__ par, int32_t *__restrict__ n_real,
                               int32_t *__restrict__ seg_end) {
-    __shared__ int32_t s_st[kMaxLdsSegs], s_len[kMaxLdsSegs], s_par[kMaxLdsSegs];
-    __shared__ int32_t s_a, s_n;
+    __shared__ int32_t s_st[kMaxLdsSegs], s_len[kMaxLdsSegs], s_par[kMaxLdsSegs], s_dep[kMaxLdsSegs];
+    __shared__ int32_t s_a, s_n, s_bad;
     const int32_t r = blockIdx.x;
     const int tid = threadIdx.x;
     if (tid == 0) {
@@ -34,33 +35,78 @@ __global__ void validate_rows(int32_t R, int32_t T, int32_t n_segs, const int32_
         const bool ok = a >= 0 && a <= b && b <= n_segs && (r != 0 || a == 0) && (r != R - 1 || b == n_segs);
         s_a = ok ? a : 0;
         s_n = ok ? b - a : -1;
+        s_bad = ok ? 0 : 1;
     }
     __syncthreads();
     const int32_t a = s_a, n = s_n;
-    const bool in_lds = n >= 0 && n <= kMaxLdsSegs;
-    if (in_lds) {
+    if (n >= 0 && n <= kMaxLdsSegs) {
+        // The row's segments in LDS; every segment checked by its own thread.  The checks are
+        // the serial ones (positive length, starts that tile the row from token 0, a parent
+        // before the child on the path from the root to the previous segment), so a table
+        // passes exactly when every segment passes.
         for (int32_t i = tid; i < n; i += blockDim.x) {
             s_st[i] = st[a + i];
             s_len[i] = ln[a + i];
             s_par[i] = par[a + i];
         }
+        __syncthreads();
+        for (int32_t sg = tid; sg < n; sg += blockDim.x) {
+            const int32_t p = s_par[sg];
+            bool ok = s_len[sg] >= 1 && s_st[sg] == (sg == 0 ? 0 : s_st[sg - 1] + s_len[sg - 1]);
+            if (ok && p != -1) {
+                ok = p >= 0 && p < sg;
+                if (ok) {
+                    // walk up from sg - 1; a parent that does not precede its child ends the
+                    // walk (that segment fails its own check)
+                    int32_t x = sg - 1;
+                    while (x > p) {
+                        const int32_t nx = s_par[x];
+                        if (nx >= x || nx < -1) break;
+                        x = nx;
+                    }
+                    ok = x == p;
+                }
+            }
+            // depth: number of ancestors (the walk stops early on an invalid parent)
+            int32_t d = 0, x = sg;
+            while (true) {
+                const int32_t nx = s_par[x];
+                if (nx < 0 || nx >= x) break;
+                x = nx;
+                ++d;
+            }
+            s_dep[sg] = d;
+            if (!ok) s_bad = 1;
+        }
+        __syncthreads();
+        const int32_t total = n > 0 ? s_st[n - 1] + s_len[n - 1] : 0;
+        const bool ok = s_bad == 0 && total <= T;
+        if (ok) {
+            // pre-order: a segment's subtree is the run of segments after it that are deeper,
+            // and the segments tile the row, so the subtree ends where the next segment at its
+            // depth or above starts (or at the row's last real token)
+            for (int32_t sg = tid; sg < n; sg += blockDim.x) {
+                int32_t x = sg + 1;
+                while (x < n && s_dep[x] > s_dep[sg]) ++x;
+                seg_end[a + sg] = x < n ? s_st[x] : total;
+            }
+        }
+        if (tid == 0) n_real[r] = ok ? total : -1;
+        return;
     }
-    __syncthreads();
+    // More segments than fit in LDS (or a bad row pointer): one thread, reading global memory.
     if (tid != 0) return;
-    auto P = [&](int32_t i) { return in_lds ? s_par[i] : par[a + i]; };
     bool ok = n >= 0;
     int64_t off = 0;
-    for (int32_t s = 0; s < n && ok; ++s) {
-        const int32_t len = in_lds ? s_len[s] : ln[a + s];
-        const int32_t start = in_lds ? s_st[s] : st[a + s];
-        const int32_t p = P(s);
+    for (int32_t sg = 0; sg < n && ok; ++sg) {
+        const int32_t len = ln[a + sg], start = st[a + sg], p = par[a + sg];
         if (len < 1 || start != off) { ok = false; break; }
         if (p != -1) {
-            if (p < 0 || p >= s) { ok = false; break; }
+            if (p < 0 || p >= sg) { ok = false; break; }
             // In pre-order the parent lies on the path from the root to the previous segment:
-            // walk up from s-1 (indices strictly decrease; their parents were checked).
-            int32_t x = s - 1;
-            while (x > p) x = P(x);
+            // walk up from sg-1 (indices strictly decrease; their parents were checked).
+            int32_t x = sg - 1;
+            while (x > p) x = par[a + x];
             if (x != p) { ok = false; break; }
         }
         off += len;
@@ -68,18 +114,11 @@ __global__ void validate_rows(int32_t R, int32_t T, int32_t n_segs, const int32_
     }
     if (ok) {
         // subtree ends: children come after their parent, so one reverse sweep suffices
-        for (int32_t s = 0; s < n; ++s) {
-            const int32_t e = in_lds ? s_st[s] + s_len[s] : st[a + s] + ln[a + s];
-            if (in_lds) s_len[s] = e; else seg_end[a + s] = e;
+        for (int32_t sg = 0; sg < n; ++sg) seg_end[a + sg] = st[a + sg] + ln[a + sg];
+        for (int32_t sg = n - 1; sg >= 0; --sg) {
+            const int32_t p = par[a + sg];
+            if (p >= 0) seg_end[a + p] = max(seg_end[a + p], seg_end[a + sg]);
         }
-        for (int32_t s = n - 1; s >= 0; --s) {
-            const int32_t p = P(s);
-            if (p < 0) continue;
-            if (in_lds) s_len[p] = max(s_len[p], s_len[s]);
-            else seg_end[a + p] = max(seg_end[a + p], seg_end[a + s]);
-        }
-        if (in_lds)
-            for (int32_t s = 0; s < n; ++s) seg_end[a + s] = s_len[s];
     }
     n_real[r] = ok ? static_cast<int32_t>(off) : -1;
 }
