@@ -212,7 +212,7 @@ int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const 
  *
  * tree_attn_bwd_workspace_size: bytes of the caller-allocated backward workspace `bws`
  *   (256-byte aligned): per-token row terms D and log2-scaled LSE ([R, Hq, T] fp32 each),
- *   the per-pair q-tile lists below, and a pool of at most 1024 fp32 partial slots of dK and
+ *   the per-pair q-tile lists and unit list below, and a pool of at most 1024 fp32 partial slots of dK and
  *   dV per KV head (each 2 x 128 x head_dim x 4 bytes; 128 MiB per KV head at head_dim 128,
  *   whatever the batch size and row length): a
  *   pair seen by many q-tiles is split over up to 4 workgroups along its list, so that the
@@ -221,7 +221,9 @@ int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const 
  * tree_attn_bwd_plan: from the forward plan in `ws`, build into `bws`, for every pair of
  *   k-tiles (2p, 2p+1) of a row, the list of q-tiles that see either of them (ascending, entry =
  *   q_tile * 16 + class(2p) * 4 + class(2p+1), classes as in tree_tile_view, a missing k-tile
- *   2p+1 counting as SKIP) and the order of the pair work.  Once per batch, like
+ *   2p+1 counting as SKIP), the order of the pair work (longest list first, equal lengths in
+ *   pair order, so the same on every run), the partial slots of the split pairs and the list
+ *   of (pair, slice) units the dK/dV pass launches one workgroup for.  Once per batch, like
  *   tree_attn_plan; asynchronous.
  * tree_attn_bwd_tiles: device pointers (into bws) of those lists, for tests:
  *   kp_ptr[R * ceil(n_ktiles / 2) + 1] CSR over (row, pair), kp_list the entries.
