@@ -102,6 +102,10 @@ __device__ __forceinline__ int32x4_t buf_rsrc(const void *base, uint32_t num_rec
     return r;
 }
 // The LDS address is wave-uniform; readfirstlane keeps it in an SGPR for the "s" operand.
+// The asm writes M0 and names it as clobbered.  The compiler warns that it does not save a
+// reserved register around such a statement; nothing needs saving, because no code in these
+// kernels keeps a value in M0 across them (on gfx950 M0 is read only by LDS-DMA, GWS, message
+// and interpolation instructions, and the only LDS-DMA loads are these).
 __device__ __forceinline__ void buf_to_lds16(int32x4_t r, uint32_t lds, int voff) {
     const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %0, 0 offen lds"
