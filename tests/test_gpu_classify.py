@@ -110,6 +110,19 @@ def test_classify_random_trees():
             _interval_mask_matches_walk(inp, got["kend"])
 
 
+def test_classify_row_with_more_segments_than_lds():
+    """A row of 2600 segments (more than the 2048 the row check keeps in LDS) takes the
+    one-thread path of the segment check; its tiles and kend must still match the oracle."""
+    rng = np.random.default_rng(77)
+    inp = _random_batch(rng, 1, 8192, max_segs=2600, max_len=4)
+    assert len(inp.seg_start) > 2048
+    plan = ta.attn_plan(inp, block_q=128, block_k=64)
+    assert plan.status() == ta.TREE_OK
+    got = fetch_tiles(plan, 1)
+    _check_tiles(inp, got, 128, 64)
+    _interval_mask_matches_walk(inp, got["kend"])
+
+
 def _table(rp, st, ln, par, T=64, R=None):
     R = len(rp) - 1 if R is None else R
     return RowInputs("bad", R, T, 16, 2, 64, "f32", 0.125, np.asarray(rp, np.int32), np.asarray(st, np.int32),
