@@ -150,6 +150,24 @@ def test_bwd_empty_middle_row():
     _full_check(inp, "empty middle row")
 
 
+def test_bwd_all_pad_batch():
+    # Two rows with no segments at all: every k-tile pair has an empty list (one unit each,
+    # no blocks), and every gradient must be exactly zero, also with NaN in the pad inputs.
+    rng = np.random.default_rng(23)
+    R, T = 2, 256
+    inp = RowInputs("all pads", R, T, 8, 2, 128, "bf16", 1 / np.sqrt(128), np.zeros(R + 1, np.int32),
+                    np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32),
+                    0, real_len=np.zeros(R, np.int64))
+    for name, H in (("q", 8), ("k", 2), ("v", 2)):
+        x = rng.standard_normal((R, T, H, 128), dtype=np.float32)
+        x[:, ::7] = np.nan
+        setattr(inp, name, bf16_bits_from_f32(x))
+    dO = draw_grad(inp, 23)
+    (dq, dk, dv), _ = run_bwd(inp, dO)
+    for g in (dq, dk, dv):
+        assert np.all(g == 0)
+
+
 # ------------------------------------------------------------------ full sizes, sampled
 
 def _subtree_tokens(inp, r):
