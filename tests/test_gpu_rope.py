@@ -124,6 +124,24 @@ def test_rope_random_forests(dtype, D, theta):
     _compare(inp, pos, f"random {dtype} D{D} theta {theta:g}", theta=theta)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope_large_positions(dtype):
+    # Positions up to 2^24 (rows hold up to 507,904 tokens, and a sequence's positions keep
+    # counting across rows): the angles pos * theta^(-2i/D) are taken in fp64, so the rotation
+    # stays within the same rounding bound as at small positions.
+    rng = np.random.default_rng(91)
+    R, T, Hq, Hkv, D = 1, 512, 4, 2, 128
+    inp = RowInputs("rope", R, T, Hq, Hkv, D, dtype, 1 / np.sqrt(D), np.array([0, 1], np.int32),
+                    np.array([0], np.int32), np.array([T], np.int32), np.array([-1], np.int32),
+                    np.array([0], np.int32), 0, real_len=np.array([T]))
+    for name, H in (("q", Hq), ("k", Hkv), ("v", Hkv)):
+        x = rng.standard_normal((R, T, H, D), dtype=np.float32) * 3
+        setattr(inp, name, bf16_bits_from_f32(x) if dtype == "bf16" else x)
+    pos = rng.integers(0, 1 << 24, (R, T)).astype(np.int32)
+    pos[0, :4] = [507_903, (1 << 24) - 1, 1 << 20, 0]
+    _compare(inp, pos, f"large positions {dtype}", theta=1e6)
+
+
 def test_rope_inverse_pads_and_single_tensor():
     import torch
     inp = make_config(2)
