@@ -7,6 +7,9 @@
     for s < t, numpy.linalg.solve; O = diag(gamma) Q H + (M o Q K^T) W; H' = gamma_C H +
     K^T diag(gamma_C/gamma) W) equals the token-by-token recurrence;
   * the short convolution on an unpacked sequence equals scipy.signal.lfilter per channel;
+  * the normalisation step against library routines: v^ = torch silu of the lfilter conv, k^ and
+    sqrt(D) q^ parallel to it with |k^|^2 = |y|^2 / (|y|^2 + eps), also where |y|^2 is of the order
+    of eps, and equal to torch normalize at full scale;
   * [PTP]'s GDN passage / [AOM]'s correctness requirement: every root-to-leaf path of a packed
     row gives the outputs of that path run on its own (state forked at each join, conv
     context carried across it, reset at roots);
@@ -152,3 +155,53 @@ def test_pads_zero_and_ignored():
     gin.beta[0, used:] = np.nan
     o2 = Gd.gdn_forward(gin)
     assert np.array_equal(o1, o2) and np.all(o1[0, used:] == 0)
+
+
+def _silu_conv_lib(gin, ch_tensor, T_used):
+    """Causal width-W conv over an unpacked one-segment row by scipy.signal.lfilter, then SiLU by
+    torch.nn.functional.silu: the activation a query/key/value head sees before normalisation."""
+    import torch
+    T, H, D = gin.rows.row_len, gin.heads, gin.head_dim
+    x = Gd._f64_bits(getattr(gin, ("x_q", "x_k", "x_v")[ch_tensor])[0]).reshape(T, H * D)
+    w = np.asarray(gin.conv_w[ch_tensor], np.float64)
+    y = np.stack([scipy.signal.lfilter(w[c, ::-1], [1.0], x[:T_used, c]) for c in range(H * D)], axis=1)
+    return torch.nn.functional.silu(torch.from_numpy(y)).numpy().reshape(T_used, H, D)
+
+
+@pytest.mark.parametrize("scale", [1.0, 3e-3])
+def test_conv_normalize_against_library_silu_and_unit_norm(scale):
+    """q^ and k^ against library routines and the unit-norm property of the published rule.
+
+    With y the SiLU of the conv (scipy lfilter + torch silu, neither from the oracle):
+      * v^ = y exactly (no normalisation of the value channel);
+      * k^ is parallel to y_k and |k^|^2 = |y_k|^2 / (|y_k|^2 + eps): an eps inside the square
+        root, eps = 1e-6 (reading R23 of the published L2 normalisation);
+      * q^ is parallel to y_q and |q^|^2 * D = |y_q|^2 / (|y_q|^2 + eps): the same norm times the
+        1/sqrt(D) query scale;
+      * for large |y| both reduce to torch.nn.functional.normalize.
+    ``scale`` shrinks the inputs until |y|^2 is of the order of eps (the conv is linear, SiLU is
+    about y/2 near 0), so a misplaced eps changes the norms by far more than the tolerance."""
+    import torch
+    T, H, D = 96, 2, 16
+    rows = _one_row([80], [-1], [0], T)
+    gin = draw_gdn(rows, heads=H, head_dim=D, seed=7)
+    for name in ("x_q", "x_k", "x_v"):
+        a = getattr(gin, name)
+        a[:] = bf16_bits_from_f32((Gd._f64_bits(a) * scale).astype(np.float32))
+    qh, kh, vh = Gd.conv_normalize(gin, 0)
+    yq, yk, yv = (_silu_conv_lib(gin, c, 80) for c in range(3))
+    assert np.abs(vh[:80] - yv).max() <= 1e-12 * max(1.0, np.abs(yv).max())
+    n2 = lambda a: (a * a).sum(-1)
+    eps = 1e-6
+    if scale < 1:
+        assert np.median(n2(yk)) < 1e3 * eps        # the regime where eps matters
+    for got, y, mult in ((kh[:80], yk, 1.0), (qh[:80], yq, float(D))):
+        want_n2 = n2(y) / (n2(y) + eps)
+        assert np.abs(n2(got) * mult - want_n2).max() <= 1e-12
+        cos = (got * y).sum(-1) / np.sqrt(n2(got) * n2(y))
+        assert np.abs(cos - 1.0).max() <= 1e-12
+        if scale == 1.0:
+            ref = torch.nn.functional.normalize(torch.from_numpy(y), dim=-1).numpy()
+            assert np.abs(got * np.sqrt(mult) - ref).max() <= 1e-5
+    # pads stay zero
+    assert np.all(qh[80:] == 0) and np.all(kh[80:] == 0)

@@ -1,5 +1,7 @@
 """Pins of the oracle's rotary embedding at tree positions (CPU only).
 
+  * the frequency schedule and the rotation against values worked by hand from the published
+    rotate-half definition (base^(-2i/D) per pair);
   * the defining property of rotary embeddings: the score of a rotated query and key depends
     only on the difference of their positions, <R(p) q, R(s) k> = <R(p - s) q, k>;
   * the same rotation as multiplication of the complex numbers x[i] + i x[i + D/2] by
@@ -113,3 +115,22 @@ def _on_path(plan, r, t, s):
             return True
         x = int(par[a + x])
     return False
+
+
+def test_frequency_schedule_hand_worked():
+    """The frequency schedule against values worked by hand from the published rotate-half
+    definition (rotary position embedding, Su et al.): pair i of a D-dimensional head turns by
+    pos * base^(-2i/D), i = 0 .. D/2 - 1.
+
+    D = 4, base 10^4, pos = 100: the exponents are 0 and -2/4, so the angles are 100 * 1 = 100
+    rad and 100 * 10^-2 = 1 rad.  D = 8, base 10^4, pos = 1: 1, 10^-1, 10^-2, 10^-3 rad.  A
+    schedule with exponent -i/D would give 10 rad for the second pair at D = 4, and one with a
+    missing factor 2 in the numerator would give 10^-1 at D = 8's last pair."""
+    assert np.allclose(Ro.angles(np.array(100), 4, 1e4), [100.0, 1.0], rtol=1e-14, atol=0)
+    assert np.allclose(Ro.angles(np.array(1), 8, 1e4), [1.0, 1e-1, 1e-2, 1e-3], rtol=1e-14, atol=0)
+    # the rotation itself, worked by hand for x = (1, 2, 3, 4) at D = 4, pos = 100:
+    # pairs (x0, x2) = (1, 3) turn by 100 rad and (x1, x3) = (2, 4) by 1 rad
+    c0, s0, c1, s1 = np.cos(100.0), np.sin(100.0), np.cos(1.0), np.sin(1.0)
+    want = [1 * c0 - 3 * s0, 2 * c1 - 4 * s1, 3 * c0 + 1 * s0, 4 * c1 + 2 * s1]
+    got = Ro.rotate(np.array([[1.0, 2.0, 3.0, 4.0]]), np.array(100), theta=1e4)[0]
+    assert np.abs(got - want).max() <= 1e-12
