@@ -155,9 +155,9 @@ int tree_attn_blocks(const tree_attn_desc *d, int32_t *block_q, int32_t *block_k
 int tree_attn_workspace_size(const tree_attn_desc *d, size_t *bytes);
 
 /*
- * tree_attn_plan — tile classification on the device ([PTP] mask passage: one fully visible
- * block per ancestor segment plus a causal triangle over the own segment; blocks are full,
- * partial or skipped).  Validates the table into a device status word, computes for every
+ * tree_attn_plan — tile classification on the device ([PTP] mask passage: a token sees whole
+ * ancestor segments and the lower triangle of its own segment, so a (q-tile, k-tile) block is
+ * fully visible, partly visible or empty, and empty blocks are skipped).  Validates the table into a device status word, computes for every
  * token the end of its segment's subtree, classifies every (q-tile, k-tile) by its exact
  * visible-pair count, builds the per-q-tile CSR lists and a longest-first work list.
  * `ws` must hold tree_attn_workspace_size bytes (256-byte aligned).  Asynchronous.
@@ -242,7 +242,8 @@ int tree_attn_bwd(const tree_attn_desc *d, const void *ws, void *bws, const void
 
 /*
  * Gated delta rule (GDN) threaded along the token tree ([PTP] GDN passage: a recurrent layer
- * needs no mask but a running state, forked once per branch point and reset at every root;
+ * carries a state along each path instead of a mask; a child segment starts from its parent's
+ * final state, a root from zero;
  * the conv context is carried across the join).  Per head (head_dim 128, width-4 conv):
  *   y_c(t) = SiLU(sum_j conv_w[c][ch][3 - j] * x_c(pi^j(t)))   c = q, k, v; pi = token parent,
  *            zero input past a root's first token

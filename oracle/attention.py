@@ -18,9 +18,9 @@ Two implementations of the same definition:
   * ``attention_brute`` / ``attention_at``: query by query over anc*(i) from the parent walk
     (``attention_walk_at`` walks the pointers per query, for rows too long for a bit matrix);
   * ``attention_segment_blocked``: per segment, the keys are all tokens of the segment's
-    ancestor segments followed by the segment's own tokens under a causal mask — the
-    "one fully visible block per ancestor segment plus a causal triangle over its own
-    segment" decomposition of [PTP]'s mask passage.  It is the fast path used for whole
+    ancestor segments followed by the segment's own tokens under a causal mask: [PTP]'s
+    mask passage splits a token's visible keys into whole ancestor segments and the lower
+    triangle of its own segment.  It is the fast path used for whole
     rows and for CPU timing; tests cross-check the two on random forests.
 """
 from __future__ import annotations

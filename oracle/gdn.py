@@ -1,8 +1,8 @@
 """Gated delta rule over tree-packed rows — TEST INFRASTRUCTURE (see ``oracle/__init__``).
 
 [PTP] ("Prefix tree packing", furtherai.github.io), GDN passage: the layer is recurrent, so
-instead of a mask a running state is threaded token by token, forked once per branch point
-(a child starts from its parent's final state) and reset at every tree root; a short causal
+it carries a state along each path instead of using a mask: a child segment starts from the
+state its parent segment ended with, and every root starts from zero; a short causal
 convolution precedes the recurrence, and its context is carried across the join as well.
 [AOM] ("ART-Optimized Megatron", "How do we implement shared prefix?"): a rollout that started
 from another rollout's state instead of the shared prefix's would be wrong.  So every token

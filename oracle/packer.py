@@ -3,10 +3,11 @@
 TEST INFRASTRUCTURE (see ``oracle/__init__``): never imported by the product path.
 
 Follows [PTP] ("Prefix tree packing", furtherai.github.io):
-  * the tree-building passage: find the longest run every active sequence agrees on,
-    emit it once, split the rest by next token and recurse;
-  * the two refinements after it: a configurable minimum shared-segment length
-    (64 by default) and no sharing of trainable tokens;
+  * the tree-building passage: the longest common run of the sequences still in play
+    becomes one segment; the remainder is partitioned by the following token and each
+    part is handled the same way;
+  * the two refinements after it: a minimum length for a shared segment (configurable,
+    64 tokens by default) and no sharing of trainable tokens;
   * the off-by-one note: each branch keeps its own copy of the non-trainable join token;
   * the scope passage: one global tree over every queued sequence, no group boundary (and,
     for the comparison that passage draws, one tree per group);
@@ -143,70 +144,84 @@ def build_tree(seqs, trainable, min_shared: int, scopes=None) -> Tree:
     return tree
 
 
+def path_tokens(path) -> int:
+    """Full unshared length of a leaf: the sum of its root-to-leaf segment lengths."""
+    return sum(length for _, length in path)
+
+
+def marginal_tokens(occupied: set, path) -> int:
+    """Tokens a leaf adds to a row already holding the segments ``occupied``: the lengths of
+    the path segments outside that set ([PTP] bin-packing passage: a row holds every segment
+    that any of its leaves uses, each once)."""
+    return sum(length for sid, length in path if sid not in occupied)
+
+
 @dataclass
-class Bin:
+class OpenRow:
+    """A row under construction: its leaves in placement order, the union of their path
+    segments, and that union's token count."""
     leaves: list = field(default_factory=list)
     occupied: set = field(default_factory=set)
     token_count: int = 0
 
-    def insertion_delta(self, path) -> int:
-        """Tokens a leaf adds to this bin: its path segments the bin does not hold yet."""
-        return sum(length for sid, length in path if sid not in self.occupied)
+    def marginal(self, path) -> int:
+        return marginal_tokens(self.occupied, path)
 
-    def add(self, s, path) -> None:
-        self.token_count += self.insertion_delta(path)
-        self.occupied.update(sid for sid, _ in path)
+    def place(self, s, path) -> None:
+        self.token_count += self.marginal(path)
+        self.occupied |= {sid for sid, _ in path}
         self.leaves.append(s)
 
 
 def placement_order(paths, groups) -> list:
-    """Reading R3 of [PTP]'s placement listing: groups in order of first appearance, stably
+    """Reading R3 of [PTP]'s placement step: groups in order of first appearance, stably
     sorted by their most expensive leaf (full unshared length), descending; leaves of a
     group in input order."""
-    order, members = [], {}
+    first_seen: dict = {}
     for s, g in enumerate(groups):
-        if g not in members:
-            members[g] = []
-            order.append(g)
-        members[g].append(s)
-    cost = [sum(length for _, length in p) for p in paths]
-    ranked = sorted(order, key=lambda g: max(cost[s] for s in members[g]), reverse=True)
-    return [s for g in ranked for s in members[g]]
+        first_seen.setdefault(g, []).append(s)
+    heaviest = {g: max(path_tokens(paths[s]) for s in m) for g, m in first_seen.items()}
+    ranked = sorted(first_seen, key=lambda g: -heaviest[g])      # sorted() is stable
+    return [s for g in ranked for s in first_seen[g]]
 
 
 def best_fit_decreasing(paths, groups, capacity: int) -> list:
-    """Tree-aware best-fit-decreasing of [PTP]'s bin-packing passage (reading R4 for
-    leaves longer than a row)."""
-    bins: list = []
+    """Best-fit-decreasing with the tree-aware marginal cost ([PTP] bin-packing passage).
+
+    Textbook best fit: a leaf goes to the open row that it fits in and that has the least room
+    left once it is placed; among rows with equal room the one opened first wins; with no such
+    row a new one is opened.  The only change from bin packing of sizes is that a leaf's size
+    in a row is its marginal token count there.  Reading R4: a leaf longer than a row is an
+    error."""
+    rows: list = []
     for s in placement_order(paths, groups):
-        cost = sum(length for _, length in paths[s])
-        if cost > capacity:
-            raise TooLong(f"sequence {s} has {cost} tokens > row capacity {capacity}")
-        best, best_remaining = None, capacity + 1
-        for b in bins:
-            count = b.token_count + b.insertion_delta(paths[s])
-            if count <= capacity and capacity - count < best_remaining:
-                best, best_remaining = b, capacity - count
-        if best is None:
-            best = Bin()
-            bins.append(best)
-        best.add(s, paths[s])
-    return bins
+        path = paths[s]
+        if path_tokens(path) > capacity:
+            raise TooLong(f"sequence {s} has {path_tokens(path)} tokens > row capacity {capacity}")
+        # (room left after placing, index of creation) for every row that can take the leaf
+        fits = [(capacity - row.token_count - row.marginal(path), idx) for idx, row in enumerate(rows)
+                if row.token_count + row.marginal(path) <= capacity]
+        if fits:
+            target = rows[min(fits)[1]]
+        else:
+            target = OpenRow()
+            rows.append(target)
+        target.place(s, path)
+    return rows
 
 
 def in_order_fill(paths, capacity: int) -> list:
     """The earlier in-order placement [PTP] compares against in its historical section:
     leaves in input order, appended to the current row (whose tree is the union of its
     leaves' paths); a new row is started for good when the next leaf does not fit."""
-    bins: list = []
+    rows: list = []
     for s, path in enumerate(paths):
-        cost = sum(length for _, length in path)
-        if cost > capacity:
-            raise TooLong(f"sequence {s} has {cost} tokens > row capacity {capacity}")
-        if not bins or bins[-1].token_count + bins[-1].insertion_delta(path) > capacity:
-            bins.append(Bin())
-        bins[-1].add(s, path)
-    return bins
+        if path_tokens(path) > capacity:
+            raise TooLong(f"sequence {s} has {path_tokens(path)} tokens > row capacity {capacity}")
+        if not rows or rows[-1].token_count + rows[-1].marginal(path) > capacity:
+            rows.append(OpenRow())
+        rows[-1].place(s, path)
+    return rows
 
 
 def group_members(groups) -> list:

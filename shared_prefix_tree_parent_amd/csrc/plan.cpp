@@ -2,8 +2,8 @@
 //
 // Integers only ("Prefix tree packing", furtherai.github.io, integer-planning passage):
 // nothing here touches a tensor.  The method, by passage of that page:
-//   * tree-building passage: emit the run every active sequence agrees on once, split the
-//     rest by next token, recurse;
+//   * tree-building passage: the longest common run of the sequences still in play becomes one
+//     segment; the remainder is partitioned by the following token and each part recursed on;
 //   * refinements: minimum shared-segment length; trainable tokens are never shared;
 //     each branch keeps its own copy of the non-trainable join token;
 //   * scope passage: one global tree over every sequence of the batch;

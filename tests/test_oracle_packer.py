@@ -76,7 +76,8 @@ def test_pack32_global_and_in_order(golden_dir):
 
 
 def test_pack32_join_token_accounting(golden_dir):
-    # 11,999 shared group-prefix tokens plus completion + 1 per rollout.
+    # a 12,000-token group prefix costs 11,999 shared tokens; each rollout adds its completion
+    # and one join token.
     g = _load(golden_dir, "pack32.json")
     seqs, trains, groups, _ = _pack32_batch(g)
     tree = P.build_tree(seqs, trains, 64)
@@ -184,11 +185,11 @@ def test_insertion_delta_monotone_submodular(seed):
     seqs = [b.seq(s) for s in range(b.n)]
     tree = P.build_tree(seqs, [b.train(s) for s in range(b.n)], 2)
     probe = int(rng.integers(0, b.n))
-    bin_ = P.Bin()
-    last_delta, last_load = bin_.insertion_delta(tree.paths[probe]), 0
+    bin_ = P.OpenRow()
+    last_delta, last_load = bin_.marginal(tree.paths[probe]), 0
     for s in rng.permutation(b.n):
-        bin_.add(int(s), tree.paths[int(s)])
-        d = bin_.insertion_delta(tree.paths[probe])
+        bin_.place(int(s), tree.paths[int(s)])
+        d = bin_.marginal(tree.paths[probe])
         assert d <= last_delta and bin_.token_count >= last_load
         last_delta, last_load = d, bin_.token_count
         assert bin_.token_count == sum(tree.segments[i].length for i in bin_.occupied)
