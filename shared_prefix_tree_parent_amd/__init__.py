@@ -54,6 +54,15 @@ class TreeError(RuntimeError):
         self.code = code
 
 
+class ArgError(TreeError, ValueError):
+    """A tensor or array that does not match the descriptor, refused before any call into the
+    library (code TREE_E_INVAL)."""
+
+    def __init__(self, what: str):
+        RuntimeError.__init__(self, f"invalid argument: {what}")
+        self.code = TREE_E_INVAL
+
+
 class PackParams(ctypes.Structure):
     _fields_ = [("row_len", ctypes.c_int32), ("min_shared", ctypes.c_int32),
                 ("pad_multiple", ctypes.c_int32), ("placement", ctypes.c_int32),
@@ -148,6 +157,50 @@ def _ptr(a) -> int:
     return int(a.data_ptr())
 
 
+_DT_NAMES = {TREE_DT_BF16: "bfloat16", TREE_DT_F32: "float32"}
+
+
+def _expect(t, name, shape, dtype_name, device=None) -> None:
+    """Refuse a tensor whose shape, element type, device or layout differs from what the
+    descriptor implies: the kernels take bare pointers and would read or write out of bounds."""
+    if t is None:
+        raise ArgError(f"{name} is required")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ArgError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if str(t.dtype).replace("torch.", "") != dtype_name:
+        raise ArgError(f"{name} has dtype {t.dtype}, expected {dtype_name}")
+    if not t.is_contiguous():
+        raise ArgError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ArgError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ArgError(f"{name} is on {t.device}, expected {device}")
+
+
+def _expect_bytes(t, name, nbytes) -> None:
+    if t is None or not t.is_cuda or not t.is_contiguous() or t.numel() * t.element_size() < nbytes:
+        raise ArgError(f"{name} must be a contiguous device buffer of at least {nbytes} bytes")
+
+
+def _check_attn_tensors(desc, q, k, v, o=None, lse=None, **grads) -> None:
+    """Shapes of the attention tensors against the descriptor: q/o/dout/dq [R, T, Hq, D],
+    k/v/dk/dv [R, T, Hkv, D] in the descriptor's dtype, lse [R, Hq, T] float32, one device."""
+    R, T, Hq, Hkv, D = desc.n_rows, desc.row_len, desc.h_q, desc.h_kv, desc.head_dim
+    dt = _DT_NAMES.get(desc.dtype)
+    if dt is None:
+        raise ArgError(f"unknown descriptor dtype {desc.dtype}")
+    dev = q.device
+    _expect(q, "q", (R, T, Hq, D), dt, dev)
+    _expect(k, "k", (R, T, Hkv, D), dt, dev)
+    _expect(v, "v", (R, T, Hkv, D), dt, dev)
+    if o is not None:
+        _expect(o, "o", (R, T, Hq, D), dt, dev)
+    if lse is not None:
+        _expect(lse, "lse", (R, Hq, T), "float32", dev)
+    for name, t in grads.items():
+        _expect(t, name, (R, T, Hq if name in ("dout", "dq") else Hkv, D), dt, dev)
+
+
 # ------------------------------------------------------------------------------ host planning
 
 _PLAN_ARRAYS = {
@@ -161,11 +214,17 @@ _PLAN_ARRAYS = {
 def tree_pack_plan(tokens, seq_offsets, trainable=None, group_ids=None, row_len=4096, min_shared=64,
                    pad_multiple=0, placement=TREE_PLACE_BFD, tree_scope=TREE_SCOPE_GLOBAL) -> dict:
     """Run the host planner; returns the plan's scalars and copies of its arrays."""
-    tok = np.ascontiguousarray(tokens, dtype=np.int32)
-    off = np.ascontiguousarray(seq_offsets, dtype=np.int64)
-    tr = None if trainable is None else np.ascontiguousarray(trainable, dtype=np.uint8)
-    gr = None if group_ids is None else np.ascontiguousarray(group_ids, dtype=np.int32)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+    off = np.ascontiguousarray(seq_offsets, dtype=np.int64).reshape(-1)
     n = len(off) - 1
+    if n < 0 or off[0] != 0 or np.any(np.diff(off) < 0) or off[-1] != len(tok):
+        raise ArgError("seq_offsets must start at 0, not decrease, and end at len(tokens)")
+    tr = None if trainable is None else np.ascontiguousarray(trainable, dtype=np.uint8).reshape(-1)
+    gr = None if group_ids is None else np.ascontiguousarray(group_ids, dtype=np.int32).reshape(-1)
+    if tr is not None and len(tr) != len(tok):
+        raise ArgError(f"trainable has {len(tr)} flags for {len(tok)} tokens")
+    if gr is not None and len(gr) != n:
+        raise ArgError(f"group_ids has {len(gr)} entries for {n} sequences")
     p = PackParams(row_len, min_shared, pad_multiple, placement, tree_scope)
     h = ctypes.c_void_p()
     _check(lib().tree_pack_plan(_ptr(tok), _ptr(off), n, _ptr(tr), _ptr(gr), ctypes.byref(p),
@@ -225,6 +284,7 @@ def tree_attn_workspace_size(desc: AttnDesc) -> int:
 
 
 def tree_attn_plan(desc: AttnDesc, ws, stream=None) -> None:
+    _expect_bytes(ws, "ws", tree_attn_workspace_size(desc))
     _check(lib().tree_attn_plan(ctypes.byref(desc), _ptr(ws), _stream(stream)), "tree_attn_plan")
 
 
@@ -243,6 +303,8 @@ def tree_attn_tiles(desc: AttnDesc, ws) -> dict:
 
 
 def tree_attn_fwd(desc: AttnDesc, ws, q, k, v, o, lse, stream=None) -> None:
+    _expect_bytes(ws, "ws", tree_attn_workspace_size(desc))
+    _check_attn_tensors(desc, q, k, v, o, lse)
     _check(lib().tree_attn_fwd(ctypes.byref(desc), _ptr(ws), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                _stream(stream)), "tree_attn_fwd")
 
@@ -255,6 +317,8 @@ def tree_attn_bwd_workspace_size(desc: AttnDesc) -> int:
 
 
 def tree_attn_bwd_plan(desc: AttnDesc, ws, bws, stream=None) -> None:
+    _expect_bytes(ws, "ws", tree_attn_workspace_size(desc))
+    _expect_bytes(bws, "bws", tree_attn_bwd_workspace_size(desc))
     _check(lib().tree_attn_bwd_plan(ctypes.byref(desc), _ptr(ws), _ptr(bws), _stream(stream)),
            "tree_attn_bwd_plan")
 
@@ -267,6 +331,9 @@ def tree_attn_bwd_tiles(desc: AttnDesc, bws):
 
 
 def tree_attn_bwd(desc: AttnDesc, ws, bws, q, k, v, o, lse, dout, dq, dk, dv, stream=None) -> None:
+    _expect_bytes(ws, "ws", tree_attn_workspace_size(desc))
+    _expect_bytes(bws, "bws", tree_attn_bwd_workspace_size(desc))
+    _check_attn_tensors(desc, q, k, v, o, lse, dout=dout, dq=dq, dk=dk, dv=dv)
     _check(lib().tree_attn_bwd(ctypes.byref(desc), _ptr(ws), _ptr(bws), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
            "tree_attn_bwd")
@@ -293,11 +360,29 @@ def tree_gdn_plan(desc: AttnDesc, seg_row_ptr, seg_start, seg_len, seg_parent, g
 
 
 def tree_gdn_fwd(desc: AttnDesc, info: GdnInfo, gws, x_q, x_k, x_v, conv_w, g, beta, o, stream=None) -> None:
+    R, T, H = desc.n_rows, desc.row_len, desc.h_q
+    dev = x_q.device
+    for name, t in (("x_q", x_q), ("x_k", x_k), ("x_v", x_v), ("o", o)):
+        _expect(t, name, (R, T, H, 128), "bfloat16", dev)
+    _expect(conv_w, "conv_w", (3, H * 128, 4), "float32", dev)
+    _expect(g, "g", (R, T, H), "float32", dev)
+    _expect(beta, "beta", (R, T, H), "float32", dev)
     _check(lib().tree_gdn_fwd(ctypes.byref(desc), ctypes.byref(info), _ptr(gws), _ptr(x_q), _ptr(x_k), _ptr(x_v),
                               _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(o), _stream(stream)), "tree_gdn_fwd")
 
 
 def tree_rope(desc: AttnDesc, pos_ids, theta, inverse, q, k, stream=None) -> None:
+    R, T, D = desc.n_rows, desc.row_len, desc.head_dim
+    dt = _DT_NAMES.get(desc.dtype)
+    dev = (q if q is not None else k).device if (q is not None or k is not None) else None
+    if q is not None:
+        _expect(q, "q", (R, T, desc.h_q, D), dt, dev)
+    if k is not None:
+        _expect(k, "k", (R, T, desc.h_kv, D), dt, dev)
+    if pos_ids is not None and pos_ids.numel() != R * T:
+        raise ArgError(f"pos_ids has {pos_ids.numel()} entries, expected {R * T}")
+    if pos_ids is not None:
+        _expect(pos_ids.view(-1), "pos_ids", (R * T,), "int32", dev)
     _check(lib().tree_rope(ctypes.byref(desc), _ptr(pos_ids), float(theta), int(inverse), _ptr(q), _ptr(k),
                            _stream(stream)), "tree_rope")
 
@@ -308,7 +393,10 @@ class AttnPlan:
     """Device segment table + workspace for one batch (reused by every layer)."""
 
     def __init__(self, seg_row_ptr, seg_start, seg_len, seg_parent, n_rows, row_len, h_q, h_kv,
-                 head_dim, dtype="bf16", scale=0.0, block_q=0, block_k=0, device="cuda"):
+                 head_dim, dtype="bf16", scale=0.0, block_q=0, block_k=0, device="cuda", check_status=True):
+        """``check_status``: read the device status word once (a stream synchronisation) and
+        raise ``TreeError(TREE_E_LAYOUT)`` if the segment table is invalid; the forward writes
+        nothing for an invalid table, so unchecked use would return unwritten outputs."""
         import torch
         as_dev = lambda a: torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32)).to(device)
         self.seg = [as_dev(seg_row_ptr), as_dev(seg_start), as_dev(seg_len), as_dev(seg_parent)]
@@ -317,6 +405,8 @@ class AttnPlan:
         nbytes = tree_attn_workspace_size(self.desc)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         tree_attn_plan(self.desc, self.ws)
+        if check_status:
+            _check(self.status(), "tree_attn_plan")
 
     def status(self) -> int:
         return tree_attn_plan_status(self.desc, self.ws)

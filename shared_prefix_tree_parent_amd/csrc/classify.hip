@@ -1,9 +1,10 @@
 // Tile classifier: segment table -> per-token subtree ends -> FULL / PARTIAL / SKIP class of
 // every (q-tile, k-tile) -> per-q-tile CSR lists -> longest-first work list.
 //
-// "Prefix tree packing" (furtherai.github.io), attention-mask passage: a token's visible set
-// is one fully visible block per ancestor segment plus a causal triangle over its own segment,
-// and most blocks of a packed row are empty and skipped.  The same page's indexer passage
+// "Prefix tree packing" (furtherai.github.io), attention-mask passage: the keys a token sees
+// are whole ancestor segments (every pair visible) and the lower triangle of its own segment,
+// so in a packed row the bulk of the (query block, key block) pairs hold no visible pair at all
+// and need no work.  The same page's indexer passage
 // tests ancestry with a depth-first [enter, exit] interval; with segments laid out in
 // pre-order that interval becomes, in token coordinates:
 //     key j is visible to query i  <=>  j <= i < kend[j],
@@ -52,7 +53,10 @@ __global__ void validate_rows(int32_t R, int32_t T, int32_t n_segs, const int32_
         __syncthreads();
         for (int32_t sg = tid; sg < n; sg += blockDim.x) {
             const int32_t p = s_par[sg];
-            bool ok = s_len[sg] >= 1 && s_st[sg] == (sg == 0 ? 0 : s_st[sg - 1] + s_len[sg - 1]);
+            // lengths and starts bounded by the row, the sum in 64 bits: no int32 wrap can make
+            // a table that overruns the row look contiguous
+            const int64_t prev_end = sg == 0 ? 0 : int64_t(s_st[sg - 1]) + s_len[sg - 1];
+            bool ok = s_len[sg] >= 1 && s_len[sg] <= T && s_st[sg] >= 0 && int64_t(s_st[sg]) == prev_end;
             if (ok && p != -1) {
                 ok = p >= 0 && p < sg;
                 if (ok) {
@@ -79,8 +83,9 @@ __global__ void validate_rows(int32_t R, int32_t T, int32_t n_segs, const int32_
             if (!ok) s_bad = 1;
         }
         __syncthreads();
-        const int32_t total = n > 0 ? s_st[n - 1] + s_len[n - 1] : 0;
-        const bool ok = s_bad == 0 && total <= T;
+        const int64_t total64 = n > 0 ? int64_t(s_st[n - 1]) + s_len[n - 1] : 0;
+        const bool ok = s_bad == 0 && total64 <= T;
+        const int32_t total = static_cast<int32_t>(ok ? total64 : 0);
         if (ok) {
             // pre-order: a segment's subtree is the run of segments after it that are deeper,
             // and the segments tile the row, so the subtree ends where the next segment at its

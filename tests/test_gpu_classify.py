@@ -139,6 +139,9 @@ def _table(rp, st, ln, par, T=64, R=None):
     ("too long", ([0, 1], [0], [65], [-1])),
     ("row ptr", ([0, 3], [0, 10], [10, 5], [-1, 0])),
     ("first start", ([0, 1], [3], [10], [-1])),
+    # lengths whose int32 sum wraps: 0 + (2^31 - 1) = start 1, and (2^31 - 1) + (2^31 - 1)
+    # wraps to -2 = start 2, so a 32-bit contiguity check would accept a table that overruns
+    ("int32 wrap", ([0, 3], [0, 2 ** 31 - 1, -2], [2 ** 31 - 1, 2 ** 31 - 1, 3], [-1, -1, -1])),
 ])
 def test_layout_errors_are_reported_and_fwd_writes_nothing(name, tab):
     import torch
@@ -146,7 +149,11 @@ def test_layout_errors_are_reported_and_fwd_writes_nothing(name, tab):
     n_segs_ok = len(st)
     inp = _table(rp, st, ln, par)
     plan = ta.AttnPlan(inp.seg_row_ptr, inp.seg_start, inp.seg_len, inp.seg_parent, inp.n_rows, inp.row_len,
-                       16, 2, 64, "f32")
+                       16, 2, 64, "f32", check_status=False)
+    with pytest.raises(ta.TreeError) as e:          # the checked constructor refuses the table
+        ta.AttnPlan(inp.seg_row_ptr, inp.seg_start, inp.seg_len, inp.seg_parent, inp.n_rows, inp.row_len,
+                    16, 2, 64, "f32")
+    assert e.value.code == ta.TREE_E_LAYOUT
     if name == "row ptr":
         assert rp[-1] != n_segs_ok
     assert plan.status() == ta.TREE_E_LAYOUT, name
