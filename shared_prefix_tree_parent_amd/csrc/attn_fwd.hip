@@ -15,8 +15,8 @@
 //     shared by all HCH heads of the group (grouped-query reuse);
 //   * 8 waves, one 32-row block each, two waves per SIMD: while one wave runs its softmax on
 //     the VALU the other's MFMAs issue (the template also allows 4 waves of two blocks);
-//   * K/V tiles (64 keys) are copied HBM -> LDS with direct-to-LDS loads into a double
-//     buffer, so the copy of tile t+1 runs under the compute of tile t with no registers.
+//   * K/V tiles (64 keys) are copied HBM -> LDS with direct-to-LDS loads into four buffer
+//     slots, two tiles ahead, so the copies run under the compute with no registers.
 // MFMA orientation: S^T = K Q^T and O^T = V^T P^T, so each lane owns one query (column) of
 // every 32x32 accumulator: row max / row sum are in-lane plus one exchange with lane^32
 // (v_permlane32_swap), and the P^T operand of the second product is the first product's
@@ -32,12 +32,13 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "tile_ops.h"
 
 namespace treeattn {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
+using tile::bf16x8_t;
+using tile::floatx16;
 
 struct FwdArgs {
     const void *q, *k, *v;
@@ -51,23 +52,15 @@ struct FwdArgs {
     float scale;   // softmax scale (for the natural-log LSE)
 };
 
-// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1: compile-time indices, so register
-// arrays indexed by them stay in registers.
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-__device__ __forceinline__ floatx16 zero16() {
-    floatx16 z;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = 0.f;
-    return z;
-}
+using tile::block_barrier;
+using tile::buf_rsrc;
+using tile::buf_to_lds16;
+using tile::buf_to_lds4;
+using tile::int32x4_t;
+using tile::static_for;
+using tile::wait_loads;
+using tile::wait_loads_but;
+using tile::zero16;
 
 // ----------------------------------------------------------------------------- element traits
 //
@@ -227,46 +220,6 @@ struct Lds {
 #endif
 constexpr int kNBlk = TREEATTN_FWD_BLOCKS_PER_WAVE;   // 32-row blocks per wave
 constexpr int kWaves = 8 / kNBlk;                     // 256 rows per workgroup
-constexpr int kBufFlags = 0x00020000;
-
-// Wait until this wave's loads (including the ones into LDS) have landed, or all but the
-// newest n of them (vmcnt(n); the counter's low 4 bits, lgkmcnt / expcnt not waited for).
-__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-template <int N>
-__device__ __forceinline__ void wait_loads_but() {
-    static_assert(N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
-}
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Direct-to-LDS buffer loads (no VGPRs): lane l's 16 (or 4) bytes from rsrc + voff land at LDS
-// address lds + 16 l (4 l).  They are issued from inline asm on purpose: the compiler then
-// does not see an LDS write in flight and does not put a wait for all vector loads in front of
-// every later LDS read; the kernel orders the copies itself with counted vmcnt waits and
-// barriers.  The asm has no register outputs; M0 holds the LDS base (one wait state after
-// writing it).  Offsets past num_records read as zeros.
-typedef int int32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ int32x4_t buf_rsrc(const void *base, uint32_t num_records) {
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    int32x4_t r;
-    r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b)));
-    r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32) & 0xffffu));
-    r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(num_records));
-    r[3] = kBufFlags;
-    return r;
-}
-__device__ __forceinline__ void buf_to_lds16(int32x4_t r, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %0, 0 offen lds"
-                 :: "s"(r), "s"(lds), "v"(voff) : "memory", "m0");
-}
-__device__ __forceinline__ void buf_to_lds4(int32x4_t r, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %0, 0 offen lds"
-                 :: "s"(r), "s"(lds), "v"(voff) : "memory", "m0");
-}
 
 // Maxima use IEEE maximum (NaN-propagating; v_maximum3_f32 on gfx950), which needs no
 // canonicalizing moves in front of each operand, unlike fmaxf in IEEE mode.
@@ -288,9 +241,10 @@ __device__ __forceinline__ float max8(const floatx16 &x, int i) {
 
 // ------------------------------------------------------------------------------------ kernel
 //
-// One workgroup = one item = 256 (query head, position) rows = 8 blocks of 32; 4 waves, one
-// per SIMD, wave w owning blocks 2w and 2w+1.  Every K / V fragment a wave reads from LDS
-// feeds two MFMAs (one per block), which halves the LDS read traffic per MFMA.
+// One workgroup = one item = 256 (query head, position) rows = 8 blocks of 32.  By default 8
+// waves own one block each, two waves per SIMD; built with TREEATTN_FWD_BLOCKS_PER_WAVE=2 it
+// is 4 waves of two blocks (one per SIMD), where every K / V fragment read from LDS feeds two
+// MFMAs.
 //
 // Software pipeline over 32-key steps.  Step u covers block u % 2 (32 keys) of the u / 2-th
 // k-tile of the q-tile's list.  In step u a wave issues the MFMAs of S(u+1) = K Q^T and of

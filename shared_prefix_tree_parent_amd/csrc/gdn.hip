@@ -1,8 +1,8 @@
 // Gated delta rule over tree-packed rows for gfx950 (CDNA4), head_dim 128, bf16 in and out.
 //
-// "Prefix tree packing" (furtherai.github.io), GDN passage: the layer is recurrent, so a
-// running state is threaded token by token, forked once per branch point and reset at every
-// root; the planner walks the tree depth by depth and runs one causal-conv pass and one
+// "Prefix tree packing" (furtherai.github.io), GDN passage: the layer is recurrent, so it
+// carries a state along each path instead of using a mask: a child segment starts from the
+// state its parent segment ended with, and a root starts from zero; the planner takes one tree depth at a time and runs one causal-conv pass and one
 // chunked delta-rule pass per depth, a child starting from its parent's final state.  The
 // layer itself (not printed on the page) is the published gated delta rule with a width-4
 // depthwise causal convolution, per head:
@@ -11,15 +11,17 @@
 //   h_t = a_t (h_pi(t) - b_t k^_t (k^_t^T h_pi(t))) + b_t k^_t v^_t^T,  o_t = h_t^T q^_t.
 //
 // Launches (all on the caller's stream):
-//   * gdn_conv: one workgroup per token; the conv follows the token-parent chain, so a child's
-//     first tokens convolve with its parent's last ones (the context carried across the join).
+//   * gdn_conv: one workgroup per (16 tokens, tensor q / k / v); the conv follows the
+//     token-parent chain, so a child's first tokens convolve with its parent's last ones (the
+//     context carried across the join).
 //   * gdn_prep: one workgroup per (chunk, head), chunk-parallel.  Chunks are 64 tokens of one
 //     segment, counted from the segment's start (the last one ragged), so every segment ends
 //     on a chunk boundary and its exact final state is available to its children: no tail is
 //     replayed.  With G the cumulative log-decay inside the chunk, gamma = exp(G):
 //       A_ts = b_t gamma_t/gamma_s k_t.k_s (s < t),  P_ts = gamma_t/gamma_s q_t.k_s (s <= t),
 //       U = (I + A)^-1 diag(b) V,  Y = (I + A)^-1 diag(b gamma) K      (forward substitution)
-//     Gram and QK^T on MFMA; the solves in fp32 (one thread per column of [V | K]).  Prep
+//     Gram and QK^T on MFMA; (I + A)^-1 in fp32 by 16 x 16 blocks over the four waves (the
+//     diagonal blocks by forward substitution, the others from them), U and Y on MFMA.  Prep
 //     also writes the decay factors gamma_t and gamma_C / gamma_t, and U in the order the
 //     scan's accumulators hold it, so the scan computes no exponential and reads U as whole
 //     16-byte lanes.

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
+#include <utility>
 
 namespace treeattn {
 namespace tile {
@@ -37,6 +39,17 @@ __device__ __forceinline__ floatx16 mfma(bf16x8_t a, bf16x8_t b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1: compile-time indices, so register
+// arrays indexed by them stay in registers.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // bf16 operand from accumulator registers 8 ks .. 8 ks + 7.
 __device__ __forceinline__ bf16x8_t acc_frag(const floatx16 &x, int ks) {
     bf16x8_t f;
@@ -49,6 +62,8 @@ template <int D>
 struct Tile {
     static constexpr int CPR = D / 8;                 // 16-byte chunks per row
     static constexpr int ROWB = D * 2;                // bytes per row
+    static constexpr int NDS = D / 16;                // k-steps over D per 32x32x16 MFMA
+    static constexpr int NDB = D / 32;                // 32-wide column blocks
     static __device__ __forceinline__ int sw(int row) {
         if constexpr (CPR == 16) return (row & 15) ^ ((row & 3) << 2);
         else return ((row >> 1) & 7) ^ (((row >> 1) & 1) << 2);
@@ -86,6 +101,45 @@ struct Tile {
     static __device__ __forceinline__ float at(const char *tile, int row, int col) {
         return float(*reinterpret_cast<const __bf16 *>(tile + chunk_at(row, col >> 3) + (col & 7) * 2));
     }
+    // Split forms of row_frag / tr_frag for kernels that keep the lane part of every address
+    // in a register and add the rest as an instruction immediate.
+    // Row operand: lane part for block row 0; add 32 * block * ROWB.
+    static __device__ __forceinline__ int row_lane(int lane, int ds) {
+        return chunk_at(lane & 31, 2 * ds + (lane >> 5));
+    }
+    // Transposed operand, read r (0, 1) of the two: in each 16-lane group, lane j points at row
+    // 8 r + 4 h + j/4, columns 4(j%4) .. +3 of a 16-column group and receives one column of 4
+    // rows.  Lane part for block row 0, ks = 0; add (32 * block + 16 ks) * ROWB.
+    static __device__ __forceinline__ int tr_lane(int lane, int db, int r) {
+        const int grp = lane >> 4, j = lane & 15, h = grp >> 1;
+        const int col = 32 * db + 16 * (grp & 1) + 4 * (j & 3);
+        return chunk_at(8 * r + 4 * h + (j >> 2), col >> 3) + (col & 7) * 2;
+    }
+    static __device__ __forceinline__ bf16x8_t row_at(const char *p) {
+        return *reinterpret_cast<const bf16x8_t *>(p);
+    }
+    static __device__ __forceinline__ bf16x8_t tr_at(const char *p0, const char *p1) {
+        typedef shortx4 __attribute__((address_space(3))) *lds_p;
+        const bf16x4_t y0 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(p0)));
+        const bf16x4_t y1 = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(p1)));
+        return __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+// Per-lane parts of the fragment addresses of a Tile<D> (computed once per kernel).
+template <int D>
+struct LaneOffsets {
+    int row[Tile<D>::NDS];
+    int tr[Tile<D>::NDB][2];
+    __device__ __forceinline__ explicit LaneOffsets(int lane) {
+#pragma unroll
+        for (int ds = 0; ds < Tile<D>::NDS; ++ds) row[ds] = Tile<D>::row_lane(lane, ds);
+#pragma unroll
+        for (int db = 0; db < Tile<D>::NDB; ++db) {
+            tr[db][0] = Tile<D>::tr_lane(lane, db, 0);
+            tr[db][1] = Tile<D>::tr_lane(lane, db, 1);
+        }
+    }
 };
 
 // Direct-to-LDS buffer loads, issued as inline asm so that the compiler does not wait for them
@@ -120,7 +174,19 @@ __device__ __forceinline__ uint32_t lds_base(const char *p) {
     return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char *)p)));
 }
+// Wait until this wave's vector loads (including the ones into LDS) have landed, or all but
+// the newest N of them (vmcnt; lgkmcnt and expcnt are not waited for).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+    static_assert(N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // Resource for a tile of rows with HBM row stride `stride` bytes whose rows past n_valid read
 // as zero.
