@@ -151,50 +151,61 @@ def segment_ancestors(seg_parent, s):
     return chain[::-1]
 
 
+def segment_block(inp, r, s, q, k, v, O, L, dtype=np.float64) -> int:
+    """Outputs of the queries of segment ``s`` (row-local index) of row ``r`` into O [R, T, Hq,
+    D] and L [R, Hq, T]; q, k, v are that row's [T, H, D] arrays in ``dtype``.  The keys are
+    every token of the segment's ancestor segments followed by its own tokens under a causal
+    mask.  Returns the number of visible (query, key) pairs."""
+    Hq, Hkv = int(_get(inp, "h_q")), int(_get(inp, "h_kv"))
+    D, scale = int(_get(inp, "head_dim")), float(_get(inp, "scale"))
+    G = Hq // Hkv
+    a = int(_get(inp, "seg_row_ptr")[r])
+    st = _get(inp, "seg_start")[a:]
+    ln = _get(inp, "seg_len")[a:]
+    par = _get(inp, "seg_parent")[a:int(_get(inp, "seg_row_ptr")[r + 1])]
+    own = np.arange(st[s], st[s] + ln[s])
+    keys = np.concatenate([np.arange(st[p], st[p] + ln[p]) for p in segment_ancestors(par, s)] + [own])
+    n_anc = len(keys) - len(own)
+    # visible[a, c]: own query a sees key c if c is an ancestor-segment key or an own key at or
+    # before a.
+    vis = np.ones((len(own), len(keys)), bool)
+    vis[:, n_anc:] = np.tril(np.ones((len(own), len(own)), bool))
+    n, lo, hi = len(own), int(st[s]), int(st[s] + ln[s])
+    for g in range(Hkv):
+        # the G query heads of KV head g, rows ordered (head, query): one product
+        qg = q[lo:hi, g * G:(g + 1) * G, :].transpose(1, 0, 2).reshape(G * n, D)
+        kg = k[keys, g, :]                                       # [m, D]
+        vg = v[keys, g, :]
+        S = (scale * (qg @ kg.T)).reshape(G, n, len(keys))       # [G, n, m]
+        S = np.where(vis[None, :, :], S, -np.inf)
+        m = S.max(axis=-1, keepdims=True)
+        P = np.exp(S - m)
+        l = P.sum(axis=-1, keepdims=True)
+        Og = (P.reshape(G * n, len(keys)) @ vg).reshape(G, n, D) / l
+        O[r, lo:hi, g * G:(g + 1) * G, :] = Og.transpose(1, 0, 2)
+        L[r, g * G:(g + 1) * G, lo:hi] = (m + np.log(l))[..., 0]
+    return n_anc * n + n * (n + 1) // 2
+
+
 def attention_segment_blocked(inp, rows=None, dtype=np.float64):
     """Whole rows by the segment decomposition; returns O [R, T, Hq, D], LSE [R, Hq, T].
 
     ``dtype`` is the arithmetic type (float64 for parity; the CPU baseline times it as is).
     """
     R, T = int(_get(inp, "n_rows")), int(_get(inp, "row_len"))
-    Hq, Hkv = int(_get(inp, "h_q")), int(_get(inp, "h_kv"))
-    D, scale = int(_get(inp, "head_dim")), float(_get(inp, "scale"))
-    G = Hq // Hkv
+    Hq, D = int(_get(inp, "h_q")), int(_get(inp, "head_dim"))
     rows = range(R) if rows is None else rows
     rp = _get(inp, "seg_row_ptr")
     O = np.zeros((R, T, Hq, D), dtype)
     L = np.full((R, Hq, T), -np.inf, dtype)
     for r in rows:
-        a, b = int(rp[r]), int(rp[r + 1])
-        st = _get(inp, "seg_start")[a:b]
-        ln = _get(inp, "seg_len")[a:b]
-        par = _get(inp, "seg_parent")[a:b]
-        if b == a:
+        if int(rp[r + 1]) == int(rp[r]):
             continue
         q = _f64(inp, "q", r).astype(dtype)
         k = _f64(inp, "k", r).astype(dtype)
         v = _f64(inp, "v", r).astype(dtype)
-        for s in range(b - a):
-            own = np.arange(st[s], st[s] + ln[s])
-            keys = np.concatenate([np.arange(st[p], st[p] + ln[p]) for p in segment_ancestors(par, s)]
-                                  + [own])
-            n_anc = len(keys) - len(own)
-            # visible[a, c]: own query a sees key c if c is an ancestor-segment key or an
-            # own key at or before a.
-            vis = np.ones((len(own), len(keys)), bool)
-            vis[:, n_anc:] = np.tril(np.ones((len(own), len(own)), bool))
-            for g in range(Hkv):
-                qg = q[own][:, g * G:(g + 1) * G, :]                    # [n, G, D]
-                kg = k[keys, g, :]                                       # [m, D]
-                vg = v[keys, g, :]
-                S = scale * np.matmul(qg, kg.T)                          # [n, G, m]
-                S = np.where(vis[:, None, :], S, -np.inf)
-                m = S.max(axis=-1, keepdims=True)
-                P = np.exp(S - m)
-                l = P.sum(axis=-1, keepdims=True)
-                lo, hi = int(st[s]), int(st[s] + ln[s])
-                O[r, lo:hi, g * G:(g + 1) * G, :] = np.matmul(P, vg) / l
-                L[r, g * G:(g + 1) * G, lo:hi] = (m + np.log(l))[..., 0].T
+        for s in range(int(rp[r + 1]) - int(rp[r])):
+            segment_block(inp, r, s, q, k, v, O, L, dtype)
     return O, L
 
 
@@ -263,25 +274,26 @@ def attention_backward_blocked(inp, dO, rows=None, dtype=np.float64):
             n_anc = len(keys) - len(own)
             vis = np.ones((len(own), len(keys)), bool)
             vis[:, n_anc:] = np.tril(np.ones((len(own), len(own)), bool))
+            n, m_, lo, hi = len(own), len(keys), int(st[s]), int(st[s] + ln[s])
             for g in range(Hkv):
                 hs = slice(g * G, (g + 1) * G)
-                qg = q[own][:, hs, :]                                  # [n, G, D]
-                dog = g_o[own][:, hs, :]                               # [n, G, D]
+                # rows ordered (head, query) over the G query heads of KV head g
+                qg = q[lo:hi, hs, :].transpose(1, 0, 2).reshape(G * n, D)
+                dog = g_o[lo:hi, hs, :].transpose(1, 0, 2).reshape(G * n, D)
                 kg = k[keys, g, :]                                     # [m, D]
                 vg = v[keys, g, :]
-                S = scale * np.matmul(qg, kg.T)                        # [n, G, m]
-                S = np.where(vis[:, None, :], S, -np.inf)
+                S = (scale * (qg @ kg.T)).reshape(G, n, m_)
+                S = np.where(vis[None, :, :], S, -np.inf)
                 m = S.max(axis=-1, keepdims=True)
                 P = np.exp(S - m)
                 P /= P.sum(axis=-1, keepdims=True)                     # softmax, 0 where masked
-                O = np.matmul(P, vg)                                   # [n, G, D]
-                Dl = (dog * O).sum(axis=-1, keepdims=True)             # [n, G, 1]
-                dP = np.matmul(dog, vg.T)                              # [n, G, m]
-                dS = P * (dP - Dl)
-                dq[r, own, hs, :] = scale * np.matmul(dS, kg)
-                n, m_ = len(own), len(keys)                            # sums over (query, head)
-                dk[r, keys, g, :] += scale * (dS.reshape(n * G, m_).T @ qg.reshape(n * G, D))
-                dv[r, keys, g, :] += P.reshape(n * G, m_).T @ dog.reshape(n * G, D)
+                P = P.reshape(G * n, m_)
+                O = P @ vg                                             # [G n, D]
+                Dl = (dog * O).sum(axis=-1, keepdims=True)             # [G n, 1]
+                dS = P * ((dog @ vg.T) - Dl)                           # dP = dO V^T
+                dq[r, lo:hi, hs, :] = (scale * (dS @ kg)).reshape(G, n, D).transpose(1, 0, 2)
+                dk[r, keys, g, :] += scale * (dS.T @ qg)               # sums over (head, query)
+                dv[r, keys, g, :] += P.T @ dog
     return dq, dk, dv
 
 

@@ -1,9 +1,10 @@
 """GPU: tree_attn_fwd against the float64 oracle, element by element.
 
-Whole-row comparisons where the oracle finishes in seconds (config 1, config 2, random
-multi-tile forests with ragged tails); at the full sizes of configs 3-5, in the launch
-configuration the benchmark times, on sampled query positions the oracle computes one by
-one (all heads), always including segment starts/ends, the last real token and pads.
+Whole-output comparisons on every config: configs 1 and 2 and random multi-tile forests with
+ragged tails against the float64 oracle, the full-size configs 3-5 against the segment-blocked
+oracle in float32 (whole rows, all heads; the launch configuration the benchmark times), plus
+the float64 per-query oracle at sampled positions of configs 3-5 (segment starts/ends, the
+last real token, pads) and of the longest supported row.
 Tolerances (bf16): O max-abs 2e-2 and mean-abs 2e-3, LSE max-abs 1e-3; (f32): O 1e-4 /
 1e-5, LSE 1e-4; pads exact.
 """
@@ -77,16 +78,47 @@ def test_config2_full():
     _full_check(make_config(2), "config 2")
 
 
+def _config4_pair():
+    """Config 4 packed by the library's planner (what the GPU runs) and by the oracle's; the
+    tables must be identical, and the oracle side then takes the same Q/K/V draws."""
+    gpu_inp = make_config(4, packer=lambda b, C, m: ta.pack_batch(b, C, m))
+    ref_inp = make_config(4, packer=lambda b, C, m: P.pack_batch(b, C, m), with_qkv=False)
+    for k in ("n_rows", "row_len", "seg_row_ptr", "seg_start", "seg_len", "seg_parent"):
+        assert np.array_equal(getattr(gpu_inp, k), getattr(ref_inp, k))
+    # Q/K/V are the generator's draws for this (R, T); identical plans give identical draws.
+    ref_inp.q, ref_inp.k, ref_inp.v = gpu_inp.q, gpu_inp.k, gpu_inp.v
+    return gpu_inp, ref_inp
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_full_size_configs_whole(cfg):
+    """Every real token x query head x head_dim element of the full-size configs against the
+    segment-blocked oracle in float32 (the precision the tolerance is stated against), in the
+    launch configuration the benchmark times; max-abs and mean-abs over the whole output, LSE
+    of every (token, head), pads exact."""
+    import time
+    log(f"config {cfg} whole output at full size")
+    if cfg == 4:
+        gpu_inp, ref_inp = _config4_pair()
+    else:
+        gpu_inp = ref_inp = make_config(cfg)
+    O, L, _ = run_fwd(gpu_inp)
+    t0 = time.time()
+    Oref, Lref = A.attention_segment_blocked(ref_inp, dtype=np.float32)
+    log(f"  oracle (segment-blocked, float32): {time.time() - t0:.1f} s")
+    o, l = rows_view(O, L)
+    orf, lrf = rows_view(Oref, Lref)
+    del O, L, Oref, Lref
+    check_close(o, l, orf, lrf, "bf16", _real_mask(ref_inp).reshape(-1), f"config {cfg} whole")
+
+
 @pytest.mark.parametrize("cfg,n", [(3, 384), (4, 384), (5, 256)])
 def test_full_size_configs_sampled(cfg, n):
+    """The float64 per-query oracle at sampled positions (segment starts and ends, the last
+    real token, pads, random tokens): independent of the segment-blocked form."""
     log(f"config {cfg} sampled at full size")
     if cfg == 4:
-        gpu_inp = make_config(4, packer=lambda b, C, m: ta.pack_batch(b, C, m))
-        ref_inp = make_config(4, packer=lambda b, C, m: P.pack_batch(b, C, m), with_qkv=False)
-        for k in ("n_rows", "row_len", "seg_row_ptr", "seg_start", "seg_len", "seg_parent"):
-            assert np.array_equal(getattr(gpu_inp, k), getattr(ref_inp, k))
-        # Q/K/V are the generator's draws for this (R, T); identical plans give identical draws.
-        ref_inp.q, ref_inp.k, ref_inp.v = gpu_inp.q, gpu_inp.k, gpu_inp.v
+        gpu_inp, ref_inp = _config4_pair()
         O, L, _ = run_fwd(gpu_inp)
         smp = _samples(ref_inp, np.random.default_rng(cfg), n)
         Oref, Lref = A.attention_at(ref_inp, smp)

@@ -49,15 +49,17 @@ def _as_float(inp):
     return alt
 
 
-def _full_check(inp, what, seed=0):
+def _full_check(inp, what, seed=0, dtype=np.float64):
     dO = draw_grad(inp, seed)
     (dq, dk, dv), _ = run_bwd(inp, dO)
-    rq, rk, rv = A.attention_backward_blocked(inp, dO)
-    O, _ = A.attention_segment_blocked(inp)
-    PK, _ = A.attention_segment_blocked(_with_v_as_k(inp))
+    rq, rk, rv = A.attention_backward_blocked(inp, dO, dtype=dtype)
+    log(f"  {what}: oracle gradients done")
+    O, _ = A.attention_segment_blocked(inp, dtype=dtype)
+    PK, _ = A.attention_segment_blocked(_with_v_as_k(inp), dtype=dtype)
     f = _as_float(inp)
     c = row_term_bound(f32_from_bf16_bits(dO), O)                          # [R, T, Hq, 1]
-    _, _, cq = A.attention_backward_blocked(f, c * np.abs(f.q))            # sum_i P_ij c_i |q_i|
+    _, _, cq = A.attention_backward_blocked(f, (c * np.abs(f.q)).astype(np.float32), dtype=dtype)
+    log(f"  {what}: oracle bound terms done")                              # sum_i P_ij c_i |q_i|
     m = _real_mask(inp).reshape(-1)
     flat = lambda x: x.reshape(-1, x.shape[2], x.shape[3])
     check_grad(flat(dq), flat(rq), m, f"{what} dQ", extra=flat(2 * inp.scale * c * np.abs(PK)))
@@ -83,6 +85,13 @@ def _random_inputs(rng, R, T, Hq, Hkv, D, max_segs=14, max_len=160):
 def test_bwd_config2_full():
     log("backward config 2 full")
     _full_check(make_config(2), "config 2", seed=2)
+
+
+def test_bwd_config3_whole():
+    """Every real token's dQ and every key's dK / dV of the long-prefix row (5000-token root,
+    16 rollouts, 32/8 heads) against the segment-blocked oracle gradients in float32."""
+    log("backward config 3 whole output")
+    _full_check(make_config(3), "config 3 whole", seed=3, dtype=np.float32)
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(8, 8, 128), (8, 4, 128), (8, 2, 128), (32, 8, 128), (16, 2, 128),
