@@ -12,17 +12,19 @@
  *      builds the radix segment tree, packs its leaves into fixed-length rows and emits
  *      the per-row segment/parent table, position ids and a gather map.
  *   2. Device attention: tree_attn_plan turns a segment table (device copy) into tile
- *      lists once per batch ([PTP] mask passage: most blocks of a packed row are empty and
- *      skipped; [AReaL] "Lazy Block Mask Conversion"), and tree_attn_fwd runs the masked
- *      attention forward on Q/K/V, reusing that plan for every layer.
+ *      lists once per batch ([PTP] mask passage: in a packed row most key blocks hold no key
+ *      a query block sees, and they are not visited; [AReaL] "Lazy Block Mask Conversion"),
+ *      and tree_attn_fwd runs the masked attention forward on Q/K/V, reusing that plan for
+ *      every layer.
  *
  * Conventions.
  *   - Every call returns int32: TREE_OK (0) or a negative TREE_E_* code;
  *     tree_status_str(code) gives a static text.
  *   - Argument errors are detected and returned synchronously, before any launch.
- *   - The library never allocates device memory and holds no global mutable state; the
- *     caller owns every device buffer (inputs, outputs, workspace).  The host plan is
- *     library-owned until tree_plan_free.
+ *   - The library never allocates device memory; the caller owns every device buffer
+ *     (inputs, outputs, workspace).  The one exception to "no global mutable state" is
+ *     tree_attn_fwd_noalloc's fixed per-device buffer.  The host plan is library-owned until
+ *     tree_plan_free.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Device calls
  *     are asynchronous on that stream unless stated otherwise.
  */
@@ -156,9 +158,9 @@ int tree_attn_workspace_size(const tree_attn_desc *d, size_t *bytes);
 
 /*
  * tree_attn_plan — tile classification on the device ([PTP] mask passage: a token sees whole
- * ancestor segments and the lower triangle of its own segment, so a (q-tile, k-tile) block is
- * fully visible, partly visible or empty, and empty blocks are skipped).  Validates the table into a device status word, computes for every
- * token the end of its segment's subtree, classifies every (q-tile, k-tile) by its exact
+ * ancestor segments and the lower triangle of its own segment, so a (q-tile, k-tile) block
+ * is fully visible, partly visible or empty, and empty blocks are skipped).  Validates the
+ * table into a device status word, computes for every token the end of its segment's subtree, classifies every (q-tile, k-tile) by its exact
  * visible-pair count, builds the per-q-tile CSR lists and a longest-first work list.
  * `ws` must hold tree_attn_workspace_size bytes (256-byte aligned).  Asynchronous.
  * Errors: TREE_E_INVAL (sizes, tiles not dividing row_len), TREE_E_HIP.
@@ -200,6 +202,26 @@ int tree_attn_tiles(const tree_attn_desc *d, const void *ws, tree_tile_view *out
  */
 int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const void *k,
                   const void *v, void *o, float *lse, void *stream);
+
+/*
+ * tree_attn_fwd_noalloc — for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): tree_attn_plan followed by
+ * tree_attn_fwd on the same stream, with the tile plan kept in a fixed buffer of the library
+ * instead of a caller workspace.  Same inputs, outputs, layouts and results as that pair (the
+ * same kernels); no workspace argument and no device allocation by the call.
+ * The buffer is a file-scope device array of TREE_NOALLOC_SCRATCH_BYTES (64 MiB); every GPU
+ * the library runs on holds its own copy until the process ends.  All calls on one GPU share
+ * that GPU's copy, so calls that overlap on one GPU (other streams, other host threads) race;
+ * calls in order on one stream are safe.  An invalid segment table makes the forward write
+ * nothing, as with tree_attn_fwd; its status is not reported.
+ * Errors: as tree_attn_fwd, plus TREE_E_UNSUPPORTED when tree_attn_workspace_size exceeds
+ * TREE_NOALLOC_SCRATCH_BYTES (e.g. a 131,072-token row with 64/8 heads needs 49 MiB and fits;
+ * the 507,904-token row does not), and TREE_E_HIP if the buffer's device address cannot be
+ * resolved on the current device.
+ */
+#define TREE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int tree_attn_fwd_noalloc(const tree_attn_desc *d, const void *q, const void *k, const void *v,
+                          void *o, float *lse, void *stream);
 
 /*
  * Backward of tree_attn_fwd ([PTP]: the packing serves training, so every attention layer is

@@ -11,6 +11,7 @@ carry the C names of ``include/treeattn.h``:
   tree_attn_plan_status(desc, ws)
   tree_attn_tiles(desc, ws)      -> dict of device pointers / sizes
   tree_attn_fwd(desc, ws, q, k, v, o, lse)  (async on the current stream)
+  tree_attn_fwd_noalloc(desc, q, k, v, o, lse)  (plan + forward in the library's fixed buffer)
   tree_attn_bwd_workspace_size(desc) -> bytes
   tree_attn_bwd_plan(desc, ws, bws)  (async on the current stream)
   tree_attn_bwd_tiles(desc, bws)     -> (kp_ptr, kp_list) device pointers
@@ -41,7 +42,8 @@ TREE_SCOPE_GLOBAL, TREE_SCOPE_PER_GROUP = 0, 1
 
 EXPORTS = ("tree_pack_plan", "tree_plan_get", "tree_plan_free", "tree_attn_blocks",
            "tree_attn_workspace_size", "tree_attn_plan", "tree_attn_plan_status", "tree_attn_tiles",
-           "tree_attn_fwd", "tree_attn_bwd_workspace_size", "tree_attn_bwd_plan", "tree_attn_bwd_tiles",
+           "tree_attn_fwd", "tree_attn_fwd_noalloc", "tree_attn_bwd_workspace_size", "tree_attn_bwd_plan",
+           "tree_attn_bwd_tiles",
            "tree_attn_bwd", "tree_rope", "tree_gdn_workspace_size", "tree_gdn_plan", "tree_gdn_fwd",
            "tree_status_str")
 
@@ -123,6 +125,7 @@ def lib() -> ctypes.CDLL:
         L.tree_attn_plan_status.argtypes = [D, vp, vp]
         L.tree_attn_tiles.argtypes = [D, vp, ctypes.POINTER(TileView)]
         L.tree_attn_fwd.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
+        L.tree_attn_fwd_noalloc.argtypes = [D, vp, vp, vp, vp, vp, vp]
         L.tree_attn_bwd_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
         L.tree_attn_bwd_plan.argtypes = [D, vp, vp, vp]
         L.tree_attn_bwd_tiles.argtypes = [D, vp, ctypes.POINTER(vp), ctypes.POINTER(vp)]
@@ -307,6 +310,12 @@ def tree_attn_fwd(desc: AttnDesc, ws, q, k, v, o, lse, stream=None) -> None:
     _check_attn_tensors(desc, q, k, v, o, lse)
     _check(lib().tree_attn_fwd(ctypes.byref(desc), _ptr(ws), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                _stream(stream)), "tree_attn_fwd")
+
+
+def tree_attn_fwd_noalloc(desc: AttnDesc, q, k, v, o, lse, stream=None) -> None:
+    _check_attn_tensors(desc, q, k, v, o, lse)
+    _check(lib().tree_attn_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       _stream(stream)), "tree_attn_fwd_noalloc")
 
 
 def tree_attn_bwd_workspace_size(desc: AttnDesc) -> int:

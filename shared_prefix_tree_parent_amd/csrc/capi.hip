@@ -1,6 +1,8 @@
 // C-ABI entry points of the device half of libtreeattn (see include/treeattn.h): argument
-// checks, workspace layout, launches.  No device memory is allocated here.
+// checks, workspace layout, launches.  No device memory is allocated here; the one fixed
+// device buffer (tree_attn_fwd_noalloc's scratch) is a file-scope __device__ array.
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
@@ -126,6 +128,61 @@ extern "C" int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void
     const hipError_t e = launch_fwd(sh, w, static_cast<const char *>(ws), q, k, v, o, lse,
                                     static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TREE_OK : TREE_E_HIP;
+}
+
+// ----------------------------------------------------------------------------- no allocation
+//
+// tree_attn_fwd_noalloc keeps the tile plan in this fixed device buffer instead of a caller
+// workspace.  In host code `scratch` names a host-side stand-in, not the device array: its
+// device address is taken once per device with hipGetSymbolAddress (with that device
+// current) and only that address is passed to kernels.  Every call on a device shares the
+// device's copy; the plan kernels rewrite every part of it the forward reads, so nothing
+// needs clearing between calls, and calls that overlap on one device race.
+namespace {
+__device__ __align__(256) char scratch[TREE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr on failure).
+char *scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        g_scratch_ptr[dev] = static_cast<char *>(p);
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int tree_attn_fwd_noalloc(const tree_attn_desc *d, const void *q, const void *k, const void *v,
+                                     void *o, float *lse, void *stream) {
+    WsLayout w;
+    if (!layout_of(d, &w)) return TREE_E_INVAL;
+    if (d->n_rows > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr))
+        return TREE_E_INVAL;
+    int32_t bq, bk;
+    fwd_blocks(d, &bq, &bk);
+    if (w.BQ != bq || w.BK != bk) return TREE_E_UNSUPPORTED;
+    if (d->dtype == TREE_DT_F32 && d->head_dim != 64) return TREE_E_UNSUPPORTED;
+    if (w.nK > kFwdMaxKTiles) return TREE_E_UNSUPPORTED;
+    if (w.total > TREE_NOALLOC_SCRATCH_BYTES) return TREE_E_UNSUPPORTED;
+    char *ws = scratch_on_current_device();
+    if (ws == nullptr) return TREE_E_HIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_plan(*d, w, ws, s) != hipSuccess) return TREE_E_HIP;
+    FwdShape sh;
+    sh.R = d->n_rows; sh.T = d->row_len; sh.Hq = d->h_q; sh.Hkv = d->h_kv; sh.D = d->head_dim;
+    sh.dtype = d->dtype;
+    sh.G = d->h_q / d->h_kv;
+    sh.HCH = heads_per_wg(sh.G);
+    sh.BQ = bq;
+    sh.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->head_dim));
+    return launch_fwd(sh, w, ws, q, k, v, o, lse, s) == hipSuccess ? TREE_OK : TREE_E_HIP;
 }
 
 // ----------------------------------------------------------------------------- backward
