@@ -384,8 +384,16 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     frag pA[kNBlk][Tr::NKS], pB[kNBlk][Tr::NKS];
     bool pending = false;                       // the last step grew the reference max of a lane
     float alpha_p[kNBlk];                       // ... by these factors (1 where not grown)
+    // mc: the reference in exp2 units (0 while it is -inf); thr: the raw score that would
+    // grow it (m_run + 8 / c, -inf at first so the first visible score sets it)
+    float mc[kNBlk], thr[kNBlk];
+    const float grow_raw = kGrow / a.c;
 #pragma unroll
-    for (int j = 0; j < kNBlk; ++j) alpha_p[j] = 1.f;
+    for (int j = 0; j < kNBlk; ++j) {
+        alpha_p[j] = 1.f;
+        mc[j] = 0.f;
+        thr[j] = -INFINITY;
+    }
 
     // Step u-1 of step 0 (the first 32 keys) multiplies zero weights by V block 1 of slot
     // NB-1; clear that block so it holds finite values.
@@ -473,14 +481,7 @@ void tree_attn_fwd_kernel(FwdArgs a) {
         const int ko_n = koff(tn, 1 - KB), vo_n = voff_of(tn, 1 - KB);
         if (pending) rescale();   // rare: the reference max grew in the previous step
         if ((ent & 3) == kTilePartial) mask(kbc, t, ent >> 2, sc);
-        float mx[kNBlk][2], alpha[kNBlk], mc[kNBlk];
-        bool grow[kNBlk];
-#pragma unroll
-        for (int j = 0; j < kNBlk; ++j) {
-            alpha[j] = 1.f;
-            mc[j] = 0.f;
-            grow[j] = false;
-        }
+        float mx[kNBlk][2];
         static_for<NLOAD>([&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value, n = i / 2;
             const frag op = ring[i % kAhead];
@@ -504,17 +505,33 @@ void tree_attn_fwd_kernel(FwdArgs a) {
             if constexpr (i == 2) {
                 // Grow the reference max only when a block's max exceeds it by more than 2^8 in
                 // the exponent domain; otherwise keep the stale reference (weights stay <= 256),
-                // which spares the accumulator rescale.
+                // which spares the accumulator rescale.  The common case costs one compare per
+                // lane against thr = m_run + 8 / c; only when some lane's partial maximum passes
+                // it does the wave take the update (row max across the lane halves, alphas).
+                float mxl[kNBlk];
+                bool need = false;
 #pragma unroll
                 for (int j = 0; j < kNBlk; ++j) {
-                    const float m = xchg_max(vmax(mx[j][0], mx[j][1]));
-                    grow[j] = m * a.c > m_run[j] * a.c + kGrow;
-                    const float m_new = grow[j] ? m : m_run[j];
-                    alpha[j] = grow[j] ? __builtin_amdgcn_exp2f((m_run[j] - m_new) * a.c) : 1.f;
-                    l_run[j] *= alpha[j];
-                    w_run[j] *= alpha[j];
-                    m_run[j] = m_new;
-                    mc[j] = (m_new == -INFINITY ? 0.f : m_new) * a.c;
+                    mxl[j] = vmax(mx[j][0], mx[j][1]);
+                    need |= mxl[j] > thr[j];
+                }
+                pending = false;
+                if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                    bool any_grow = false;
+#pragma unroll
+                    for (int j = 0; j < kNBlk; ++j) {
+                        const float m = xchg_max(mxl[j]);
+                        const bool grow = m * a.c > m_run[j] * a.c + kGrow;
+                        const float m_new = grow ? m : m_run[j];
+                        alpha_p[j] = grow ? __builtin_amdgcn_exp2f((m_run[j] - m_new) * a.c) : 1.f;
+                        l_run[j] *= alpha_p[j];
+                        w_run[j] *= alpha_p[j];
+                        m_run[j] = m_new;
+                        mc[j] = (m_new == -INFINITY ? 0.f : m_new) * a.c;
+                        thr[j] = m_new + grow_raw;
+                        any_grow |= grow;
+                    }
+                    pending = __builtin_amdgcn_ballot_w64(any_grow) != 0;
                 }
             }
             static_for<16 * kNBlk>([&](auto ec) __attribute__((always_inline)) {
@@ -534,16 +551,12 @@ void tree_attn_fwd_kernel(FwdArgs a) {
         // Keep this step's P^T operands and sums computed here: without a use at this point
         // the compiler sinks the exponentials past the next step's rescale branch, out of the
         // MFMA slots they are meant to fill.
-        bool any_grow = false;
 #pragma unroll
         for (int j = 0; j < kNBlk; ++j) {
 #pragma unroll
             for (int ks = 0; ks < Tr::NKS; ++ks) asm volatile("" ::"v"(pc[j][ks]));
             asm volatile("" ::"v"(l_run[j]), "v"(w_run[j]));
-            any_grow |= grow[j];
-            alpha_p[j] = alpha[j];
         }
-        pending = __builtin_amdgcn_ballot_w64(any_grow) != 0;
     };
 
     // Prologue: tiles 0 and 1 in flight, wait for tile 0, S(0) of both blocks.
