@@ -160,8 +160,9 @@ int tree_attn_workspace_size(const tree_attn_desc *d, size_t *bytes);
  * tree_attn_plan — tile classification on the device ([PTP] mask passage: a token sees whole
  * ancestor segments and the lower triangle of its own segment, so a (q-tile, k-tile) block
  * is fully visible, partly visible or empty, and empty blocks are skipped).  Validates the
- * table into a device status word, computes for every token the end of its segment's subtree, classifies every (q-tile, k-tile) by its exact
- * visible-pair count, builds the per-q-tile CSR lists and a longest-first work list.
+ * table into a device status word, computes for every token the end of its segment's subtree,
+ * classifies every (q-tile, k-tile) by its exact visible-pair count, builds the per-q-tile CSR
+ * lists and the work list (rows in order, a row's q-tiles longest list first).
  * `ws` must hold tree_attn_workspace_size bytes (256-byte aligned).  Asynchronous.
  * Errors: TREE_E_INVAL (sizes, tiles not dividing row_len), TREE_E_HIP.
  */
@@ -182,7 +183,8 @@ typedef struct {
     const uint8_t *kt_kind;     /* [nnz] their classes */
     const int32_t *kend;        /* [n_rows * row_len] token j is visible to exactly the queries
                                    i with j <= i < kend[j]; pads: kend[j] = j */
-    const int32_t *work;        /* [n_rows * n_qtiles] q-tiles, most non-skip tiles first */
+    const int32_t *work;        /* [n_rows * n_qtiles] (row, q-tile) items: rows in order, inside
+                                   a row most non-skip tiles first */
     const int32_t *status;      /* [1] 0 = table valid */
 } tree_tile_view;
 

@@ -229,17 +229,21 @@ __device__ void block_scan(int32_t n, int32_t *x, int32_t *part, int32_t *carry)
 }
 
 // One workgroup: CSR offsets (scan of the per-tile counts), the table status word and the
-// work list: q-tiles ordered by their number of non-skip k-tiles, largest
-// first (a counting sort; the order among equal counts does not affect any result).
-__global__ void finish_plan(int32_t R, int32_t nK, int32_t n_tiles, const int32_t *__restrict__ n_real,
+// work list: rows in order, and inside a row its q-tiles by their number of non-skip k-tiles,
+// largest first (a counting sort over (row, count) buckets; the order among equal counts does
+// not affect any result).  Keeping a row's q-tiles together keeps that row's K/V tiles in the
+// L2 of the XCDs that stream them, while the longest-first order inside the row keeps the
+// tail short.
+__global__ void finish_plan(int32_t R, int32_t nQ, int32_t nK, int32_t n_tiles, const int32_t *__restrict__ n_real,
                             int32_t *__restrict__ qt_ptr, int32_t *__restrict__ hist,
                             int32_t *__restrict__ work, int32_t *__restrict__ status) {
     __shared__ int32_t part[1024 / 64];
     __shared__ int32_t carry, bad;
     if (threadIdx.x == 0) { bad = 0; qt_ptr[0] = 0; }
-    // counts of cost c go to hist[1 + (nK - c)] so that an inclusive scan yields, at
-    // hist[nK - c], the first slot of cost c in descending order.
-    for (int32_t i = threadIdx.x; i < nK + 2; i += blockDim.x) hist[i] = 0;
+    // tiles of row r and cost c go to bucket b = r (nK + 1) + (nK - c), counted at hist[1 + b],
+    // so that an inclusive scan yields at hist[b] the first slot of that bucket.
+    const int32_t n_buckets = R * (nK + 1);
+    for (int32_t i = threadIdx.x; i < n_buckets + 2; i += blockDim.x) hist[i] = 0;
     __syncthreads();
     for (int32_t r = threadIdx.x; r < R; r += blockDim.x)
         if (n_real[r] < 0) atomicOr(&bad, 1);
@@ -247,15 +251,15 @@ __global__ void finish_plan(int32_t R, int32_t nK, int32_t n_tiles, const int32_
     __threadfence_block();
     __syncthreads();
     for (int32_t t = threadIdx.x; t < n_tiles; t += blockDim.x)
-        atomicAdd(&hist[1 + nK - (qt_ptr[t + 1] - qt_ptr[t])], 1);
+        atomicAdd(&hist[1 + (t / nQ) * (nK + 1) + nK - (qt_ptr[t + 1] - qt_ptr[t])], 1);
     __threadfence_block();
     __syncthreads();
-    block_scan(nK + 1, hist, part, &carry);
+    block_scan(n_buckets, hist, part, &carry);
     __threadfence_block();
     __syncthreads();
     for (int32_t t = threadIdx.x; t < n_tiles; t += blockDim.x) {
         const int32_t c = qt_ptr[t + 1] - qt_ptr[t];
-        work[atomicAdd(&hist[nK - c], 1)] = t;
+        work[atomicAdd(&hist[(t / nQ) * (nK + 1) + nK - c], 1)] = t;
     }
     if (threadIdx.x == 0) status[0] = bad ? kStatusLayout : 0;
 }
@@ -499,7 +503,7 @@ hipError_t launch_plan(const tree_attn_desc &d, const WsLayout &w, char *ws, hip
         classify_tiles<<<(n_tiles + 3) / 4, 256, 0, s>>>(w.R, w.BQ, w.BK, w.nQ, w.nK, n_real, kt_stats, cmap,
                                                          qt_ptr);
     }
-    finish_plan<<<1, 1024, 0, s>>>(w.R, w.nK, n_tiles, n_real, qt_ptr, hist, work, status);
+    finish_plan<<<1, 1024, 0, s>>>(w.R, w.nQ, w.nK, n_tiles, n_real, qt_ptr, hist, work, status);
     if (n_tiles > 0)
         fill_lists<<<(n_tiles + 3) / 4, 256, 0, s>>>(w.nK, n_tiles, cmap, qt_ptr, kt_idx, kt_kind);
     return hipGetLastError();

@@ -27,8 +27,8 @@ struct WsLayout {
     size_t qt_ptr = 0;    // int32[R*nQ + 1]
     size_t kt_idx = 0;    // int32[R*nQ*nK]
     size_t kt_kind = 0;   // uint8[R*nQ*nK]
-    size_t work = 0;      // int32[R*nQ]
-    size_t hist = 0;      // int32[nK + 2]
+    size_t work = 0;      // int32[R*nQ]: (row, q-tile) items, rows in order, longest first in a row
+    size_t hist = 0;      // int32[R*(nK + 1) + 2]: work-list buckets (row, k-tile count)
     size_t kt_stats = 0;  // int2[R*nK] per k-tile (min kend, max kend over real keys)
     size_t total = 0;
 };
@@ -52,7 +52,7 @@ inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_
     w.kt_idx = take(tiles * sizeof(int32_t));
     w.kt_kind = take(tiles);
     w.work = take(size_t(R) * w.nQ * sizeof(int32_t));
-    w.hist = take((size_t(w.nK) + 2) * sizeof(int32_t));
+    w.hist = take((size_t(R) * (w.nK + 1) + 2) * sizeof(int32_t));
     w.kt_stats = take(size_t(R) * w.nK * 2 * sizeof(int32_t));
     w.total = off;
     return w;
