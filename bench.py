@@ -35,15 +35,15 @@ METRIC = "tree-attn fwd useful TFLOP/s (% bf16 MFMA peak) + trajectories/s per G
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (2.5 PFLOP/s class, 2.4 GHz)
 PEAK_F32_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 HBM_GBS = 8000.0
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "tree_attn_fwd_config3_traffic.txt")
-CLOCK_RECORD = os.path.join(ROOT, "profiles", "tree_attn_fwd_config3_clock.txt")
+# Counter summaries per workload: profiles/tree_attn_fwd_config<N>_{traffic,clock}.txt
+RECORD_DIR = os.path.join(ROOT, "profiles")
 NOMINAL_CLOCK_GHZ = 2.4      # engine clock the published peak assumes
 
 
 def recorded(path: str, cfg: int, uniform: bool, key: str):
     """A value from a committed rocprofv3 counter summary, or None when the summary is for
-    another workload or the forward kernel's source has changed since the counters were taken
-    (the summary records the SHA-256 of the source it measured)."""
+    another workload or the forward kernel's sources have changed since the counters were
+    taken (the summary records the SHA-256 of the listed source files, concatenated in order)."""
     import hashlib
     try:
         rec = {}
@@ -51,8 +51,10 @@ def recorded(path: str, cfg: int, uniform: bool, key: str):
             k, sep, v = line.strip().partition(": ")
             if sep:
                 rec[k] = v.strip()
-        src = os.path.join(ROOT, rec["source"])
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for src in rec["source"].split():
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        digest = h.hexdigest()
         if digest != rec["source_sha256"] or rec["workload"] != f"config {cfg}" or uniform:
             return None
         return rec[key]
@@ -63,14 +65,15 @@ def recorded(path: str, cfg: int, uniform: bool, key: str):
 def recorded_traffic(cfg: int, uniform: bool):
     """HBM bytes per forward launch (FETCH_SIZE x 2 + WRITE_SIZE x 1, calibrated against a
     copy of known size)."""
-    v = recorded(TRAFFIC_RECORD, cfg, uniform, "traffic_bytes_per_launch")
+    v = recorded(os.path.join(RECORD_DIR, f"tree_attn_fwd_config{cfg}_traffic.txt"), cfg, uniform,
+                 "traffic_bytes_per_launch")
     return int(v) if v is not None else None
 
 
 def recorded_clock_ghz(cfg: int, uniform: bool):
     """Mean engine clock during the forward launches (GRBM_GUI_ACTIVE cycles per XCD over
     the dispatch time)."""
-    v = recorded(CLOCK_RECORD, cfg, uniform, "clock_ghz")
+    v = recorded(os.path.join(RECORD_DIR, f"tree_attn_fwd_config{cfg}_clock.txt"), cfg, uniform, "clock_ghz")
     return float(v) if v is not None else None
 
 
@@ -506,7 +509,7 @@ def main() -> int:
         adj_peak = PEAK_BF16_TFLOPS * clk / NOMINAL_CLOCK_GHZ
         out["clock_adjusted"] = {"clock_ghz": clk, "peak": round(adj_peak, 1), "unit": "TFLOP/s",
                                  "achieved": round(fwd_tflops, 2), "frac": round(fwd_tflops / adj_peak, 4),
-                                 "source": os.path.relpath(CLOCK_RECORD, ROOT)}
+                                 "source": f"profiles/tree_attn_fwd_config{args.config}_clock.txt"}
     try:
         out["host_plan_ms"] = round(host_plan_ms(args.config), 3)
     except Exception as e:  # host planning is reported, not required for the device step
