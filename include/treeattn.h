@@ -197,12 +197,16 @@ int tree_attn_tiles(const tree_attn_desc *d, const void *ws, tree_tile_view *out
  * (itself, earlier tokens of its segment, every token of its ancestor segments), and
  * LSE[h,i] = log-sum-exp of those scores.  Pads get O = 0 and LSE = -inf; pad Q/K/V
  * contents never reach a result.  `ws` must come from tree_attn_plan with the same `d`.
+ * The call hands the plan's (row, q-tile) items out to its workgroups from counters in `ws`
+ * (two int32 per KV lane, zeroed by tree_attn_plan) and leaves them at zero when it ends, so
+ * the plan is reusable by any number of forwards in stream order; two forwards on one
+ * workspace must not overlap (other streams without ordering, other host threads).
  * bf16: bf16 MFMA with fp32 accumulation, head_dim 64 or 128; f32: fp32 MFMA, head_dim 64.
  * Asynchronous.  Errors: TREE_E_INVAL, TREE_E_UNSUPPORTED (plan tiles differ from
- * tree_attn_blocks, f32 with head_dim 128, or row_len > 507904: a workgroup keeps its q-tile's
+ * tree_attn_blocks, f32 with head_dim 128, or row_len > 507648: a workgroup keeps its q-tile's
  * list of row_len/64 k-tiles in LDS), TREE_E_HIP.
  */
-int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const void *k,
+int tree_attn_fwd(const tree_attn_desc *d, void *ws, const void *q, const void *k,
                   const void *v, void *o, float *lse, void *stream);
 
 /*
@@ -218,7 +222,7 @@ int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const 
  * nothing, as with tree_attn_fwd; its status is not reported.
  * Errors: as tree_attn_fwd, plus TREE_E_UNSUPPORTED when tree_attn_workspace_size exceeds
  * TREE_NOALLOC_SCRATCH_BYTES (e.g. a 131,072-token row with 64/8 heads needs 49 MiB and fits;
- * the 507,904-token row does not), and TREE_E_HIP if the buffer's device address cannot be
+ * the 507,648-token row does not), and TREE_E_HIP if the buffer's device address cannot be
  * resolved on the current device.
  */
 #define TREE_NOALLOC_SCRATCH_BYTES (64u << 20)

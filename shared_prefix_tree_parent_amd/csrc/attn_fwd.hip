@@ -26,9 +26,12 @@
 // the exponent domain (a wave-uniform branch), so the accumulator rescale is rare; O is
 // normalized by the sum of the bf16-rounded weights actually fed to the MFMA, the LSE by the
 // fp32 sum.
-// Scheduling: items are dispatched longest first (work list from the classifier); the item's
-// KV head is blockIdx % n_kv_lanes, so with 8 KV heads every XCD (blockIdx round-robin over
-// 8 XCDs) works on one KV head and keeps that head's K/V in its own L2.
+// Scheduling: persistent workgroups, about one per CU.  Workgroup b serves KV lane
+// b % n_kv_lanes and takes that lane's items one after another, in work-list order (rows in
+// order, a row's q-tiles longest list first), from a counter in the workspace; with 8 KV
+// heads every XCD (blockIdx round-robin over 8 XCDs) works on one KV head and keeps that
+// head's K/V in its own L2.  O leaves through LDS as whole rows.
+#include <algorithm>
 #include <type_traits>
 
 #include "internal.h"
@@ -47,6 +50,8 @@ struct FwdArgs {
     const int32_t *qt_ptr, *kt_idx;
     const uint8_t *kt_kind;
     const int32_t *kend, *work, *n_real, *status;
+    int32_t *ctr;         // [2 L]: items handed out per lane, then workgroups finished per lane
+    int32_t n_items;      // rows * q-tiles
     int32_t T, Hq, Hkv, G, HCH, nQ, L, BQ;
     float c;       // scale * log2(e): exponent scale for exp2
     float scale;   // softmax scale (for the natural-log LSE)
@@ -61,6 +66,13 @@ using tile::static_for;
 using tile::wait_loads;
 using tile::wait_loads_but;
 using tile::zero16;
+
+// Next item of a lane's queue (device-scope counter; values come in work-list order).
+__device__ __forceinline__ int fetch_add(int32_t *p) {
+    return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's LDS reads and writes have completed (vmcnt, expcnt not waited for).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // ----------------------------------------------------------------------------- element traits
 //
@@ -199,8 +211,8 @@ struct F32Traits {
     static constexpr bool kRoundedP = false;
 };
 
-// LDS layout: four K tiles, then four V tiles, then the four tiles' kend (64 ints each), then
-// the q-tile's k-tile list.  Tile t lives in buffer slot t % 4.  With K and V in regions of
+// LDS layout: four K tiles, then four V tiles, then the four tiles' kend (64 ints each), four
+// control words, then the q-tile's k-tile list.  Tile t lives in buffer slot t % 4.  With K and V in regions of
 // their own, every fragment read inside a 64 KB region is one per-lane base register plus an
 // instruction immediate (slot and block offsets are compile-time), so reads cost no address
 // arithmetic.
@@ -211,7 +223,8 @@ struct Lds {
     static constexpr int K_OFF = 0;
     static constexpr int V_OFF = NBUF * TILE;
     static constexpr int KE_OFF = 2 * NBUF * TILE;
-    static constexpr int LIST_OFF = KE_OFF + NBUF * 256;
+    static constexpr int CTRL_OFF = KE_OFF + NBUF * 256;
+    static constexpr int LIST_OFF = CTRL_OFF + 16;
     static_assert(NBUF * TILE <= 65536, "a region must be reachable by 16-bit LDS offsets");
 };
 
@@ -241,10 +254,10 @@ __device__ __forceinline__ float max8(const floatx16 &x, int i) {
 
 // ------------------------------------------------------------------------------------ kernel
 //
-// One workgroup = one item = 256 (query head, position) rows = 8 blocks of 32.  By default 8
-// waves own one block each, two waves per SIMD; built with TREEATTN_FWD_BLOCKS_PER_WAVE=2 it
-// is 4 waves of two blocks (one per SIMD), where every K / V fragment read from LDS feeds two
-// MFMAs.
+// A workgroup takes items one at a time; an item = 256 (query head, position) rows = 8 blocks
+// of 32.  By default 8 waves own one block each, two waves per SIMD; built with
+// TREEATTN_FWD_BLOCKS_PER_WAVE=2 it is 4 waves of two blocks (one per SIMD), where every K / V
+// fragment read from LDS feeds two MFMAs.
 //
 // Software pipeline over 32-key steps.  Step u covers block u % 2 (32 keys) of the u / 2-th
 // k-tile of the q-tile's list.  In step u a wave issues the MFMAs of S(u+1) = K Q^T and of
@@ -273,9 +286,17 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
-    const int bid = blockIdx.x;
-    const int u = bid % a.L, item = bid / a.L;
+    const int u = blockIdx.x % a.L;
     const int g = u % a.Hkv, chunk = u / a.Hkv;
+    int32_t *const take = a.ctr + u;          // items of this lane handed out after the first round
+    int32_t *const done = a.ctr + a.L + u;    // workgroups of this lane finished
+    int32_t *const ctrl = reinterpret_cast<int32_t *>(smem + LD::CTRL_OFF);
+    // Workgroups on this lane; the k-th of them starts with the lane's k-th item, and the rest
+    // are handed out by the counter (so the launch does not start with every workgroup
+    // contending for it).
+    const int n_wg = int(gridDim.x) / a.L + (u < int(gridDim.x) % a.L ? 1 : 0);
+    int item = blockIdx.x / a.L;
+    while (item < a.n_items) {
     const int tile = a.work[item];
     const int r = tile / a.nQ, qt = tile % a.nQ;
     const int T = a.T;
@@ -321,7 +342,8 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     // LDS reads, never a vector-memory wait that would also wait for the K/V copies in flight.
     int32_t *const lst = reinterpret_cast<int32_t *>(smem + LD::LIST_OFF);
     for (int i = tid; i < N; i += kWaves * 64) lst[i] = a.kt_idx[t_begin + i] * 4 + a.kt_kind[t_begin + i];
-    __syncthreads();
+    wait_lds();
+    block_barrier();
 
     const int row_stride = a.Hkv * D * Tr::kEsz;   // bytes between keys
     const char *kbase0 = reinterpret_cast<const char *>(a.k) + ((int64_t(r) * T) * a.Hkv + g) * D * Tr::kEsz;
@@ -568,6 +590,7 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     } else {
         wait_loads();
     }
+    wait_lds();   // the cleared V block
     block_barrier();
     if (N > 0) {
         static_for<Tr::NDS>([&](auto nc) __attribute__((always_inline)) {
@@ -605,36 +628,82 @@ void tree_attn_fwd_kernel(FwdArgs a) {
         });
     }
 
-    // Epilogue: combine the two lane halves' partial sums, normalize, write O and LSE.
+    // Epilogue: combine the two lane halves' partial sums, normalize.
+    float lse_v[kNBlk];
 #pragma unroll
     for (int j = 0; j < kNBlk; ++j) {
         const float l_tot = xchg_sum(l_run[j]);
         const float w_tot = Tr::kRoundedP ? xchg_sum(w_run[j]) : l_tot;
         const float inv = w_tot > 0.f ? 1.f / w_tot : 0.f;
-        elem *op = reinterpret_cast<elem *>(a.o) + ((int64_t(r) * T + qpos[j]) * a.Hq + head[j]) * D;
 #pragma unroll
-        for (int db = 0; db < Tr::NDB; ++db) {
+        for (int db = 0; db < Tr::NDB; ++db)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int d0 = 32 * db + 8 * i4 + 4 * h;
-                float vals[4];
+            for (int i = 0; i < 16; ++i) acc[j][db][i] *= inv;
+        lse_v[j] = l_tot > 0.f ? m_run[j] * a.scale + __logf(l_tot) : -INFINITY;
+    }
+    // The next item, claimed before this item's stores (so that waiting for the claim does not
+    // wait for them).
+    int next = 0;
+    if (tid == 0) next = n_wg + fetch_add(take);
+    wait_lds();
+    block_barrier();   // every wave is done reading this item's tiles
+    {
+        // O goes out through LDS as whole rows: each wave writes its 32 x D block into the K / V
+        // regions of slots 0 and 1, reads it back row by row and stores 16 bytes per lane, CH
+        // lanes per row.  16-byte chunks are XOR-swizzled by row.
+        constexpr int ROWB = D * Tr::kEsz, CH = ROWB / 16, RPI = 64 / CH;
+        // Lane index hidden from loop-invariant code motion: the staging addresses are computed
+        // here, per item, instead of living (spilled) across the tile loop.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int p32 = ln & 31;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vals[e] = acc[j][db][4 * i4 + e] * inv;
-                if constexpr (Tr::kEsz == 2) {
-                    uint2 w;
-                    w.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[0]))) |
-                          (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[1]))) << 16);
-                    w.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[2]))) |
-                          (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(vals[3]))) << 16);
-                    *reinterpret_cast<uint2 *>(op + d0) = w;
-                } else {
-                    *reinterpret_cast<float4 *>(op + d0) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+        for (int j = 0; j < kNBlk; ++j) {
+            const int b = kNBlk * wave + j, area = b >> 1;
+            char *base = smem + ((area & 1) ? LD::V_OFF : LD::K_OFF) + (area >> 1) * LD::TILE + (b & 1) * 32 * ROWB;
+#pragma unroll
+            for (int db = 0; db < Tr::NDB; ++db) {
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int byte = (32 * db + 8 * i4 + 4 * h) * Tr::kEsz;
+                    char *dst = base + p32 * ROWB + ((((byte >> 4) ^ p32) & (CH - 1)) << 4) + (byte & 15);
+                    if constexpr (Tr::kEsz == 2) {
+                        uint2 w;
+                        w.x = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j][db][4 * i4 + 0]))) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j][db][4 * i4 + 1]))) << 16);
+                        w.y = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j][db][4 * i4 + 2]))) |
+                              (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j][db][4 * i4 + 3]))) << 16);
+                        *reinterpret_cast<uint2 *>(dst) = w;
+                    } else {
+                        *reinterpret_cast<float4 *>(dst) = make_float4(acc[j][db][4 * i4 + 0], acc[j][db][4 * i4 + 1],
+                                                                       acc[j][db][4 * i4 + 2], acc[j][db][4 * i4 + 3]);
+                    }
                 }
             }
+            asm volatile("" ::: "memory");   // the wave's LDS accesses stay in program order
+            const int pos0 = qpos[j] - l32;   // first position of the block
+            char *orow = reinterpret_cast<char *>(a.o) + ((int64_t(r) * T + pos0) * a.Hq + head[j]) * ROWB;
+            const int64_t pstride = int64_t(a.Hq) * ROWB;
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int p = k * RPI + ln / CH, c = ln % CH;
+                const uint4 v = *reinterpret_cast<const uint4 *>(base + p * ROWB + (((c ^ p) & (CH - 1)) << 4));
+                *reinterpret_cast<uint4 *>(orow + p * pstride + c * 16) = v;
+            }
+            if (h == 0) a.lse[(int64_t(r) * a.Hq + head[j]) * T + qpos[j]] = lse_v[j];
         }
-        if (h == 0) {
-            const float lse = l_tot > 0.f ? m_run[j] * a.scale + __logf(l_tot) : -INFINITY;
-            a.lse[(int64_t(r) * a.Hq + head[j]) * T + qpos[j]] = lse;
+    }
+    if (tid == 0) ctrl[0] = next;
+    wait_lds();
+    block_barrier();   // staged O read back by every wave; the claim visible
+    item = __builtin_amdgcn_readfirstlane(ctrl[0]);
+    }
+
+    // The lane's last workgroup to finish leaves its counters at zero for the next launch.
+    if (tid == 0) {
+        if (__hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == n_wg - 1) {
+            __hip_atomic_store(take, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -655,7 +724,7 @@ hipError_t launch_tr(const FwdArgs &args, int n_blocks, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdShape &sh, const WsLayout &w, const char *ws, const void *q,
+hipError_t launch_fwd(const FwdShape &sh, const WsLayout &w, char *ws, const void *q,
                       const void *k, const void *v, void *o, float *lse, hipStream_t s) {
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -671,8 +740,18 @@ hipError_t launch_fwd(const FwdShape &sh, const WsLayout &w, const char *ws, con
     a.L = sh.Hkv * (sh.G / sh.HCH);
     a.scale = sh.scale;
     a.c = sh.scale * 1.4426950408889634f;
-    const int64_t n_blocks = int64_t(sh.R) * w.nQ * a.L;
-    if (n_blocks == 0) return hipSuccess;
+    a.ctr = reinterpret_cast<int32_t *>(ws + w.ctr);
+    if (a.L != w.n_lanes) return hipErrorInvalidValue;
+    const int64_t n_items = int64_t(sh.R) * w.nQ;
+    if (n_items == 0) return hipSuccess;
+    if (n_items > INT32_MAX) return hipErrorInvalidValue;
+    a.n_items = int32_t(n_items);
+    // One workgroup per CU (an item's K/V buffers fill the CU's LDS), rounded down to whole lanes.
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+        n_cu = 256;
+    const int64_t n_blocks = std::min<int64_t>(std::max(1, n_cu / a.L), n_items) * a.L;
     if (n_blocks > INT32_MAX) return hipErrorInvalidValue;
     if (sh.dtype == TREE_DT_BF16) {
         if (sh.D == 128) return launch_tr<Bf16Traits<128>>(a, int(n_blocks), s);

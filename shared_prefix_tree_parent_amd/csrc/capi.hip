@@ -50,7 +50,7 @@ bool plan_blocks(const tree_attn_desc *d, int32_t *bq, int32_t *bk) {
 bool layout_of(const tree_attn_desc *d, WsLayout *w) {
     int32_t bq, bk;
     if (!shape_ok(d) || !plan_blocks(d, &bq, &bk)) return false;
-    *w = make_layout(d->n_rows, d->row_len, bq, bk, d->n_segs);
+    *w = make_layout(d->n_rows, d->row_len, bq, bk, d->n_segs, d->h_q / heads_per_wg(d->h_q / d->h_kv));
     return true;
 }
 
@@ -107,7 +107,7 @@ extern "C" int tree_attn_tiles(const tree_attn_desc *d, const void *ws, tree_til
     return TREE_OK;
 }
 
-extern "C" int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void *q, const void *k,
+extern "C" int tree_attn_fwd(const tree_attn_desc *d, void *ws, const void *q, const void *k,
                              const void *v, void *o, float *lse, void *stream) {
     WsLayout w;
     if (!layout_of(d, &w) || ws == nullptr) return TREE_E_INVAL;
@@ -125,7 +125,7 @@ extern "C" int tree_attn_fwd(const tree_attn_desc *d, const void *ws, const void
     sh.HCH = heads_per_wg(sh.G);
     sh.BQ = bq;
     sh.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->head_dim));
-    const hipError_t e = launch_fwd(sh, w, static_cast<const char *>(ws), q, k, v, o, lse,
+    const hipError_t e = launch_fwd(sh, w, static_cast<char *>(ws), q, k, v, o, lse,
                                     static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TREE_OK : TREE_E_HIP;
 }

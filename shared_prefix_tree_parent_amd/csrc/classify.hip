@@ -236,10 +236,12 @@ __device__ void block_scan(int32_t n, int32_t *x, int32_t *part, int32_t *carry)
 // tail short.
 __global__ void finish_plan(int32_t R, int32_t nQ, int32_t nK, int32_t n_tiles, const int32_t *__restrict__ n_real,
                             int32_t *__restrict__ qt_ptr, int32_t *__restrict__ hist,
-                            int32_t *__restrict__ work, int32_t *__restrict__ status) {
+                            int32_t *__restrict__ work, int32_t n_ctr, int32_t *__restrict__ ctr,
+                            int32_t *__restrict__ status) {
     __shared__ int32_t part[1024 / 64];
     __shared__ int32_t carry, bad;
     if (threadIdx.x == 0) { bad = 0; qt_ptr[0] = 0; }
+    for (int32_t i = threadIdx.x; i < n_ctr; i += blockDim.x) ctr[i] = 0;   // forward item counters
     // tiles of row r and cost c go to bucket b = r (nK + 1) + (nK - c), counted at hist[1 + b],
     // so that an inclusive scan yields at hist[b] the first slot of that bucket.
     const int32_t n_buckets = R * (nK + 1);
@@ -492,6 +494,7 @@ hipError_t launch_plan(const tree_attn_desc &d, const WsLayout &w, char *ws, hip
     int32_t *work = reinterpret_cast<int32_t *>(ws + w.work);
     int32_t *hist = reinterpret_cast<int32_t *>(ws + w.hist);
     int2 *kt_stats = reinterpret_cast<int2 *>(ws + w.kt_stats);
+    int32_t *ctr = reinterpret_cast<int32_t *>(ws + w.ctr);
     const int32_t n_tiles = w.R * w.nQ;
 
     // No memset nodes: everything the plan needs cleared is cleared by its own kernels.
@@ -503,7 +506,7 @@ hipError_t launch_plan(const tree_attn_desc &d, const WsLayout &w, char *ws, hip
         classify_tiles<<<(n_tiles + 3) / 4, 256, 0, s>>>(w.R, w.BQ, w.BK, w.nQ, w.nK, n_real, kt_stats, cmap,
                                                          qt_ptr);
     }
-    finish_plan<<<1, 1024, 0, s>>>(w.R, w.nQ, w.nK, n_tiles, n_real, qt_ptr, hist, work, status);
+    finish_plan<<<1, 1024, 0, s>>>(w.R, w.nQ, w.nK, n_tiles, n_real, qt_ptr, hist, work, 2 * w.n_lanes, ctr, status);
     if (n_tiles > 0)
         fill_lists<<<(n_tiles + 3) / 4, 256, 0, s>>>(w.nK, n_tiles, cmap, qt_ptr, kt_idx, kt_kind);
     return hipGetLastError();

@@ -12,9 +12,9 @@ namespace treeattn {
 constexpr int kTileSkip = 0, kTileFull = 1, kTilePartial = 2;
 constexpr int kFwdBlockK = 64;        // keys per k-tile in the forward kernel
 constexpr int kFwdRowsPerWG = 256;    // (query head, position) rows one forward workgroup owns
-// Longest k-tile list the forward keeps in LDS beside its four 33 KB K/V buffers (160 KB per
-// workgroup): row_len <= 64 * 7936 = 507904.
-constexpr int kFwdMaxKTiles = 7936;
+// Longest k-tile list the forward keeps in LDS beside its four 32 KB K/V buffers, their kend
+// and 16 bytes of control words (160 KB per workgroup): row_len <= 64 * 7932 = 507648.
+constexpr int kFwdMaxKTiles = 7932;
 
 // Device workspace layout: every section 256-byte aligned, offsets from the base pointer.
 struct WsLayout {
@@ -30,14 +30,18 @@ struct WsLayout {
     size_t work = 0;      // int32[R*nQ]: (row, q-tile) items, rows in order, longest first in a row
     size_t hist = 0;      // int32[R*(nK + 1) + 2]: work-list buckets (row, k-tile count)
     size_t kt_stats = 0;  // int2[R*nK] per k-tile (min kend, max kend over real keys)
+    size_t ctr = 0;       // int32[2*n_lanes]: forward item counters, then finished-workgroup
+                          // counters, one per KV lane (zeroed by the plan; each forward leaves
+                          // them at zero)
+    int32_t n_lanes = 0;  // forward KV lanes: h_q / (query heads per workgroup)
     size_t total = 0;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_t n_segs) {
+inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_t n_segs, int32_t n_lanes) {
     WsLayout w;
-    w.R = R; w.T = T; w.BQ = BQ; w.BK = BK; w.n_segs = n_segs;
+    w.R = R; w.T = T; w.BQ = BQ; w.BK = BK; w.n_segs = n_segs; w.n_lanes = n_lanes;
     w.nQ = T / BQ;
     w.nK = T / BK;
     const size_t tiles = size_t(R) * w.nQ * w.nK;
@@ -54,6 +58,7 @@ inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_
     w.work = take(size_t(R) * w.nQ * sizeof(int32_t));
     w.hist = take((size_t(R) * (w.nK + 1) + 2) * sizeof(int32_t));
     w.kt_stats = take(size_t(R) * w.nK * 2 * sizeof(int32_t));
+    w.ctr = take(size_t(2) * n_lanes * sizeof(int32_t));
     w.total = off;
     return w;
 }
@@ -178,7 +183,7 @@ struct FwdShape {
     int32_t BQ;     // positions per q-tile = kFwdRowsPerWG / HCH
     float scale;
 };
-hipError_t launch_fwd(const FwdShape &sh, const WsLayout &w, const char *ws, const void *q,
+hipError_t launch_fwd(const FwdShape &sh, const WsLayout &w, char *ws, const void *q,
                       const void *k, const void *v, void *o, float *lse, hipStream_t s);
 hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b, const char *ws, char *bws,
                       const void *q, const void *k, const void *v, const void *o, const float *lse,

@@ -218,14 +218,14 @@ def test_deterministic():
 
 
 def test_longest_supported_row():
-    # 507,904 tokens: the last real q-tile lists all 7936 k-tiles, the most the forward keeps
+    # 507,648 tokens: the last real q-tile lists all 7932 k-tiles, the most the forward keeps
     # in LDS.  Positions are checked one by one by the oracle's parent walk (a bit matrix of
     # this row would take 32 GB).
     inp = longest_row_inputs(seed=41)
     log(f"longest row: {inp.row_len} tokens")
     O, L, plan = run_fwd(inp)
     t = fetch_tiles(plan, 1)
-    assert int(np.diff(t["qt_ptr"]).max()) == inp.row_len // t["block_k"] == 7936
+    assert int(np.diff(t["qt_ptr"]).max()) == inp.row_len // t["block_k"] == 7932
     smp = _samples(inp, np.random.default_rng(41), 12)
     Oref, Lref = A.attention_walk_at(inp, smp)
     idx_t = np.array([s[1] for s in smp])

@@ -409,8 +409,8 @@ def test_bwd_fp32_is_unsupported():
 
 
 def test_bwd_longest_supported_row():
-    # 507,904 tokens (7936 k-tiles; the dK/dV kernel keeps each pair's q-tile list of up to
-    # 3968 entries in LDS).  dQ at sampled queries and dK / dV at keys of the 32-token child
+    # 507,648 tokens (7932 k-tiles; the dK/dV kernel keeps each pair's q-tile list of up to
+    # 3966 entries in LDS).  dQ at sampled queries and dK / dV at keys of the 32-token child
     # and of the second child's tail, by the oracle's parent walk and descendant sweep (a bit
     # matrix of this row would take 32 GB); the identities cover every key.
     inp = longest_row_inputs(seed=43)

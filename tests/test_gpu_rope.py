@@ -126,7 +126,7 @@ def test_rope_random_forests(dtype, D, theta):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_rope_large_positions(dtype):
-    # Positions up to 2^24 (rows hold up to 507,904 tokens, and a sequence's positions keep
+    # Positions up to 2^24 (rows hold up to 507,648 tokens, and a sequence's positions keep
     # counting across rows): the angles pos * theta^(-2i/D) are taken in fp64, so the rotation
     # stays within the same rounding bound as at small positions.
     rng = np.random.default_rng(91)
