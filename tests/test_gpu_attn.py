@@ -14,7 +14,7 @@ import pytest
 import shared_prefix_tree_parent_amd as ta
 from oracle import attention as A
 from oracle import packer as P
-from tests.gpu_util import LONGEST_ROW, check_close, fetch_tiles, log, longest_row_inputs, rows_view, run_fwd
+from tests.gpu_util import LONGEST_ROW, check_close, fetch_tiles, log, longest_row_inputs, rows_view, run_fwd, to_dev
 from workloads import RowInputs, bf16_bits_from_f32, fill_pads, make_config, random_forest_row
 
 pytestmark = pytest.mark.gpu
@@ -215,6 +215,35 @@ def test_deterministic():
     O1, L1, plan = run_fwd(inp)
     O2, L2, _ = run_fwd(inp, plan=plan, repeats=2)
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_plans_interleaved_and_reused():
+    """The forward hands items out from counters in the plan's workspace and leaves them at
+    zero: forwards alternating over three plans of different shapes (head groupings, one and
+    several rows), each plan used several times, give each plan's first result every time,
+    and a forward whose table the device rejected (it takes no item) leaves the others intact."""
+    rng = np.random.default_rng(7)
+    cases = [make_config(2),
+             _random_inputs(rng, R=3, T=512, Hq=8, Hkv=2, D=128, dtype="bf16"),
+             _random_inputs(rng, R=1, T=256, Hq=4, Hkv=4, D=64, dtype="bf16")]
+    plans = [ta.attn_plan(c) for c in cases]
+    first = [run_fwd(c, plan=pl) for c, pl in zip(cases, plans)]
+    bad = make_config(2)
+    bad.seg_len = bad.seg_len.copy()
+    bad.seg_len[0] += 1                      # overlaps the next segment: status != 0
+    bad_plan = ta.AttnPlan(bad.seg_row_ptr, bad.seg_start, bad.seg_len, bad.seg_parent, bad.n_rows,
+                           bad.row_len, bad.h_q, bad.h_kv, bad.head_dim, bad.dtype, check_status=False)
+    for rnd in range(3):
+        for i, (c, pl) in enumerate(zip(cases, plans)):
+            O, L, _ = run_fwd(c, plan=pl, repeats=1 + (rnd + i) % 2)
+            assert np.array_equal(O, first[i][0]) and np.array_equal(L, first[i][1]), f"plan {i} round {rnd}"
+        import torch
+        q, k, v = (to_dev(bad, n) for n in ("q", "k", "v"))
+        o = torch.full_like(q, 7.0)
+        lse = torch.full((bad.n_rows, bad.h_q, bad.row_len), 7.0, device=q.device)
+        ta.tree_attn_fwd(bad_plan.desc, bad_plan.ws, q, k, v, o, lse)
+        torch.cuda.synchronize()
+        assert bool(torch.all(o == 7.0)) and bool(torch.all(lse == 7.0))
 
 
 def test_longest_supported_row():
