@@ -24,8 +24,9 @@
 // LDS transpose reads (ds_read_b64_tr_b16).
 // Softmax: the reference max only moves when a tile's max exceeds it by more than 2^8 in
 // the exponent domain (a wave-uniform branch), so the accumulator rescale is rare; O is
-// normalized by the sum of the bf16-rounded weights actually fed to the MFMA, the LSE by the
-// fp32 sum.
+// normalized by the sum of the bf16-rounded weights actually fed to the MFMA, and the LSE is
+// the log of that same sum (the normalizer of the weights O was made from; an fp32 sum beside
+// it would cost one add per score).  The fp32 instantiation sums the weights in fp32.
 // Scheduling: persistent workgroups, about one per CU.  Workgroup b serves KV lane
 // b % n_kv_lanes and takes that lane's items one after another, in work-list order (rows in
 // order, a row's q-tiles longest list first), from a counter in the workspace; with 8 KV
@@ -325,9 +326,9 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     for (int j = 0; j < kNBlk; ++j)
 #pragma unroll
         for (int db = 0; db < Tr::NDB; ++db) acc[j][db] = zero16();
-    // m_run: reference max (raw score units); l_run: fp32 sum of the exponentials (for LSE);
-    // w_run: sum of the weights as rounded for the PV product (normalizes O, so the weights
-    // applied to V sum to one exactly as used).
+    // m_run: reference max (raw score units); w_run: sum of the weights as rounded for the PV
+    // product (normalizes O, so the weights applied to V sum to one exactly as used, and gives
+    // the LSE); l_run: fp32 sum of the exponentials, kept only where P is not rounded.
     float m_run[kNBlk], l_run[kNBlk], w_run[kNBlk];
 #pragma unroll
     for (int j = 0; j < kNBlk; ++j) {
@@ -561,7 +562,7 @@ void tree_attn_fwd_kernel(FwdArgs a) {
                 if constexpr (3 + (e * (NLOAD - 4)) / (16 * kNBlk) == i) {
                     const float x = __builtin_amdgcn_exp2f(fmaf(sc[j][k], a.c, -mc[j]));
                     sc[j][k] = x;
-                    l_run[j] += x;
+                    if constexpr (!Tr::kRoundedP) l_run[j] += x;
                     if constexpr (k % EPF == EPF - 1) {
                         pc[j][k / EPF] = Tr::p_frag(sc[j], k / EPF);
                         if constexpr (Tr::kRoundedP) w_run[j] = Tr::wsum(pc[j][k / EPF], w_run[j]);
@@ -577,7 +578,7 @@ void tree_attn_fwd_kernel(FwdArgs a) {
         for (int j = 0; j < kNBlk; ++j) {
 #pragma unroll
             for (int ks = 0; ks < Tr::NKS; ++ks) asm volatile("" ::"v"(pc[j][ks]));
-            asm volatile("" ::"v"(l_run[j]), "v"(w_run[j]));
+            asm volatile("" ::"v"(Tr::kRoundedP ? w_run[j] : l_run[j]));
         }
     };
 
@@ -632,14 +633,13 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     float lse_v[kNBlk];
 #pragma unroll
     for (int j = 0; j < kNBlk; ++j) {
-        const float l_tot = xchg_sum(l_run[j]);
-        const float w_tot = Tr::kRoundedP ? xchg_sum(w_run[j]) : l_tot;
+        const float w_tot = xchg_sum(Tr::kRoundedP ? w_run[j] : l_run[j]);
         const float inv = w_tot > 0.f ? 1.f / w_tot : 0.f;
 #pragma unroll
         for (int db = 0; db < Tr::NDB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[j][db][i] *= inv;
-        lse_v[j] = l_tot > 0.f ? m_run[j] * a.scale + __logf(l_tot) : -INFINITY;
+        lse_v[j] = w_tot > 0.f ? m_run[j] * a.scale + __logf(w_tot) : -INFINITY;
     }
     // The next item, claimed before this item's stores (so that waiting for the claim does not
     // wait for them).

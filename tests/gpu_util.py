@@ -79,9 +79,12 @@ def check_close(o_gpu, l_gpu, o_ref, l_ref, dtype, real_mask, what=""):
     """Compare [N, Hq, D] outputs and [N, Hq] LSE at N positions (real_mask [N]: real tokens).
 
     Tolerances: bf16 O max-abs 2e-2, mean-abs 2e-3 (over real tokens x heads x head_dim), LSE
-    max-abs 1e-3; f32 O max-abs 1e-4, mean-abs 1e-5, LSE max-abs 1e-4.  Pads exact: O = 0,
-    LSE = -inf."""
-    tol = dict(bf16=(2e-2, 2e-3, 1e-3), f32=(1e-4, 1e-5, 1e-4))[dtype]
+    max-abs 5e-3 and mean-abs 1e-3; f32 O max-abs 1e-4, mean-abs 1e-5, LSE max-abs 1e-4.  The
+    bf16 LSE is the log of the sum of the weights as rounded to bf16 for the P V product: each
+    carries a relative error of at most 2^-8 (bf16's unit roundoff), so the log moves by at most
+    ln(1 + 2^-8) < 3.9e-3 from the exact sum, plus 1e-3 for the fp32 scores and exponentials.
+    Pads exact: O = 0, LSE = -inf."""
+    tol = dict(bf16=(2e-2, 2e-3, 5e-3, 1e-3), f32=(1e-4, 1e-5, 1e-4, 1e-4))[dtype]
     real_mask = np.asarray(real_mask, bool)
     assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite O"
     err = np.abs(o_gpu - o_ref)
@@ -90,10 +93,12 @@ def check_close(o_gpu, l_gpu, o_ref, l_ref, dtype, real_mask, what=""):
     mean_abs = float(real_o.mean()) if real_o.size else 0.0
     lerr = np.abs(l_gpu[real_mask] - l_ref[real_mask])
     lmax = float(lerr.max()) if lerr.size else 0.0
-    log(f"  {what}: O max-abs {max_abs:.3e} mean-abs {mean_abs:.3e}  LSE max-abs {lmax:.3e}")
+    lmean = float(lerr.mean()) if lerr.size else 0.0
+    log(f"  {what}: O max-abs {max_abs:.3e} mean-abs {mean_abs:.3e}  LSE max-abs {lmax:.3e} mean-abs {lmean:.3e}")
     assert max_abs <= tol[0], f"{what}: O max-abs {max_abs}"
     assert mean_abs <= tol[1], f"{what}: O mean-abs {mean_abs}"
     assert lmax <= tol[2], f"{what}: LSE max-abs {lmax}"
+    assert lmean <= tol[3], f"{what}: LSE mean-abs {lmean}"
     pad = ~real_mask
     if pad.any():
         assert np.all(o_gpu[pad] == 0), f"{what}: pad O not zero"

@@ -5,8 +5,8 @@ ragged tails against the float64 oracle, the full-size configs 3-5 against the s
 oracle in float32 (whole rows, all heads; the launch configuration the benchmark times), plus
 the float64 per-query oracle at sampled positions of configs 3-5 (segment starts/ends, the
 last real token, pads) and of the longest supported row.
-Tolerances (bf16): O max-abs 2e-2 and mean-abs 2e-3, LSE max-abs 1e-3; (f32): O 1e-4 /
-1e-5, LSE 1e-4; pads exact.
+Tolerances (bf16): O max-abs 2e-2 and mean-abs 2e-3, LSE max-abs 5e-3 (the log of the
+bf16-rounded weight sum) and mean-abs 1e-3; (f32): O 1e-4 / 1e-5, LSE 1e-4; pads exact.
 """
 import numpy as np
 import pytest
