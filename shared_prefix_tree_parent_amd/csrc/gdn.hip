@@ -30,7 +30,9 @@
 //     parent's final state (zero at roots); per chunk
 //       W = U - Y H,   O = diag(gamma) Q H + P W,   H <- gamma_C H + K^T diag(gamma_C/gamma) W
 //     with bf16 operands (H rounded for the products only) and fp32 accumulation; the
-//     segment's final H is stored for its children.
+//     segment's final H is stored for its children.  A chunk's O goes to LDS at its end and
+//     leaves as whole 256-byte rows right after the next chunk's barrier, so no chunk waits
+//     for its own stores to be acknowledged.
 #include <type_traits>
 #include <utility>
 
@@ -415,7 +417,11 @@ struct ScanLds {
     static constexpr int Q_OFF = 0, K_OFF = TILE, Y_OFF = 2 * TILE, P_OFF = 3 * TILE;
     static constexpr int F_OFF = P_OFF + kGC * kGC * 2;
     static constexpr int STAGE = F_OFF + 2 * kGC * 4;
-    static constexpr int SIZE = 2 * STAGE;
+    // The chunk's O (64 tokens x 128 bf16, 256-byte rows, 16-byte chunks XOR-swizzled by the
+    // token's low 4 bits), two buffers: chunk ci writes its O here at its end, and every wave
+    // stores 16 of its rows to HBM right after chunk ci+1's barrier.
+    static constexpr int O_OFF = 2 * STAGE, OBUF = kGC * kGD * 2;
+    static constexpr int SIZE = O_OFF + 2 * OBUF;
 };
 
 __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
@@ -492,16 +498,37 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) un[u / 4][u % 4] = us[u * 64];
     }
+    // Chunk c's O from its LDS buffer to HBM: this wave's 16 token rows, 16 bytes a lane, 16
+    // lanes a row (rows of real tokens only).
+    auto store_o = [&](int c) __attribute__((always_inline)) {
+        const int n = c + 1 < n_ch ? kGC : last_n;
+        const char *ob = smem + ScanLds::O_OFF + (c & 1) * ScanLds::OBUF;
+        char *og = reinterpret_cast<char *>(a.o) + ((int64_t(r) * a.T + seg_t0 + kGC * c) * a.H + h) * kGD * 2;
+        const int cc = lane & 15;
+        uint4 v[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const int t = 16 * wave + 4 * k4 + (lane >> 4);
+            v[k4] = *reinterpret_cast<const uint4 *>(ob + t * (kGD * 2) + ((cc ^ (t & 15)) << 4));
+        }
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const int t = 16 * wave + 4 * k4 + (lane >> 4);
+            if (t < n) *reinterpret_cast<uint4 *>(og + int64_t(t) * a.H * kGD * 2 + cc * 16) = v[k4];
+        }
+    };
     for (int ci = 0; ci < n_ch; ++ci) {
         // Chunk ci's stage and U have landed for every wave; every wave is done with chunk
-        // ci-1, whose stage buffer chunk ci+1 takes.
+        // ci-1, whose stage buffer chunk ci+1 takes, and chunk ci-1's O is in LDS.
         wait_loads();
         __syncthreads();
+        // Chunk ci-1's O leaves now, while no copy is queued ahead of it, and has the whole
+        // chunk to be acknowledged before the next wait for loads (which counts stores too).
+        if (ci > 0) store_o(ci - 1);
         const bool more = ci + 1 < n_ch;
         const StageSrc nx = stage_src(ci + 1);
         const float4 *nu = u_src(ci + 1);
         const int n = more ? kGC : last_n;
-        const int64_t tok0 = int64_t(r) * a.T + seg_t0 + kGC * ci;
         const char *st = smem + (ci & 1) * ScanLds::STAGE;
         const char *Qt = st + ScanLds::Q_OFF, *Kt = st + ScanLds::K_OFF;
         const char *Yt = st + ScanLds::Y_OFF, *Pt = st + ScanLds::P_OFF;
@@ -644,24 +671,25 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
             }
         }
         {
-            // O of the chunk, stored after the state update's MFMAs are issued (a store issued
-            // right behind the next chunk's copies would hold the wave until they drain): four
-            // consecutive value columns of one token per 8-byte store
-            __bf16 *og = a.o + (tok0 * a.H + h) * kGD + 32 * wave + 4 * hh;
+            // O of the chunk into its LDS buffer: four consecutive value columns of one token
+            // per 8-byte write.
+            char *ob = smem + ScanLds::O_OFF + (ci & 1) * ScanLds::OBUF;
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
                 const int t = 32 * tb + l32;
-                if (t < n) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        bf16x4_t v4;
+                for (int q = 0; q < 4; ++q) {
+                    bf16x4_t v4;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(O[tb][4 * q + e]);
-                        *reinterpret_cast<bf16x4_t *>(og + int64_t(t) * a.H * kGD + 8 * q) = v4;
-                    }
+                    for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(O[tb][4 * q + e]);
+                    *reinterpret_cast<bf16x4_t *>(ob + t * (kGD * 2) + (((4 * wave + q) ^ (t & 15)) << 4) + 8 * hh) = v4;
                 }
             }
         }
+    }
+    if (n_ch > 0) {
+        __syncthreads();   // the last chunk's O is in LDS
+        store_o(n_ch - 1);
     }
     float *dst = a.states + (int64_t(seg) * a.H + h) * kGD * kGD;
 #pragma unroll
