@@ -371,15 +371,17 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
     __syncthreads();
     product(smem + PrepLds::V_OFF, acc);
     {
-        // accumulator order of the scan: wave w's columns, float4 (4 tb + q) * 64 + lane holds
-        // rows 32 tb + 8 q + 4 (lane / 32) + 0..3
-        float4 *Uo = reinterpret_cast<float4 *>(a.U + chh * kGC * kGD) + wave * (kGC * 32 / 4) + lane;
+        // The scan's accumulator order: float4 (4 cb + tb) * 64 + 16 g + j holds rows 16 tb + 4 g
+        // + 0..3 of column 16 cb + j.  This lane holds rows 32 tb + 8 q + 4 (lane / 32) + 0..3 of
+        // column 32 wave + lane % 32.
+        float4 *Uo = reinterpret_cast<float4 *>(a.U + chh * kGC * kGD);
+        const int cl = lane & 31, hh = lane >> 5, cb = 2 * wave + (cl >> 4);
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                Uo[(4 * tb + q) * 64] = make_float4(acc[tb][4 * q], acc[tb][4 * q + 1], acc[tb][4 * q + 2],
-                                                    acc[tb][4 * q + 3]);
+                Uo[(4 * cb + 2 * tb + (q >> 1)) * 64 + 16 * (2 * (q & 1) + hh) + (cl & 15)] =
+                    make_float4(acc[tb][4 * q], acc[tb][4 * q + 1], acc[tb][4 * q + 2], acc[tb][4 * q + 3]);
     }
     __syncthreads();
     build_factor(true);
@@ -407,31 +409,103 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
 
 // ------------------------------------------------------------------------------ gdn_scan
 //
+// 16x16x32 bf16 MFMA: lane l supplies A[m = l%16][k slot (l/16, e)] and B[k slot (l/16, e)]
+// [n = l%16], e = 0..7, and accumulator element i of lane l is C[4(l/16) + i][l%16].  A k-step
+// of 32 gives slot (g, e) the reduced index 32 s + 4 g + e (e < 4) or 32 s + 16 + 4 g + e - 4
+// (e >= 4): exactly the rows that accumulator blocks 2 s and 2 s + 1 hold in lane l, so a
+// product's accumulators become the next product's operand by conversion alone (pair_frag),
+// and the operand read from a tile supplies the same k order (row16_frag, tr16_frag).
+//
+// A wave owns 16 value columns of the state: H (128 x 16) in 8 accumulator blocks, W and O^T
+// of the chunk in 4 each.  Per chunk, 56 MFMAs: W = U - Y H and O^T = H^T Q^T (32), O^T +=
+// W^T P^T (8), H <- gamma_C H + K^T diag(gamma_C / gamma) W (16).  A workgroup of NW waves
+// covers 16 NW columns, so a head takes 128 / (16 NW) workgroups: 2 workgroups of 4 waves when
+// a depth level has few segments (the chains then run on twice the CUs, each wave on its own
+// SIMD), 1 of 8 waves otherwise (the chunk tiles are copied once per head).
+//
 // LDS: two stages of chunk tiles (Q, K, -Y: 64 x 128 bf16; P: 64 x 64 bf16; the decay
-// factors: 128 fp32), the next chunk's stage copied while the current one is used.  U goes
-// straight from HBM into registers (prep wrote it in accumulator order), one chunk ahead.
-// Nothing in the chunk loop waits on a scalar load: chunk ci of a segment starts at the
-// segment's first token + 64 ci.
+// factors: 128 fp32), the next chunk's stage copied while the current one is used; two
+// buffers of the chunk's O (64 tokens x 16 NW columns bf16, 16-byte chunks XOR-swizzled by the
+// token).  U goes straight from HBM into registers (prep wrote it in accumulator order), one
+// chunk ahead.  Nothing in the chunk loop waits on a scalar load: chunk ci of a segment starts
+// at the segment's first token + 64 ci.
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16(bf16x8_t a, bf16x8_t b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+// Operand of one k-step from accumulator blocks 2 s (slots e < 4) and 2 s + 1 (e >= 4).
+__device__ __forceinline__ bf16x8_t pair_frag(const floatx4 &lo, const floatx4 &hi) {
+    bf16x8_t f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[e] = static_cast<__bf16>(lo[e]);
+        f[4 + e] = static_cast<__bf16>(hi[e]);
+    }
+    return f;
+}
+// Operand from a swizzled row-major tile: tile row `row` (the lane's m or n), k-step s of the
+// columns: 32 s + 4 g + 0..3 and 32 s + 16 + 4 g + 0..3 (two 8-byte reads).
+template <int D>
+__device__ __forceinline__ bf16x8_t row16_frag(const char *tile, int row, int g, int s) {
+    using TL = Tile<D>;
+    const int c0 = 32 * s + 4 * g, c1 = c0 + 16;
+    const bf16x4_t y0 = *reinterpret_cast<const bf16x4_t *>(tile + TL::chunk_at(row, c0 >> 3) + (c0 & 7) * 2);
+    const bf16x4_t y1 = *reinterpret_cast<const bf16x4_t *>(tile + TL::chunk_at(row, c1 >> 3) + (c1 & 7) * 2);
+    return __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// Transposed operand from a swizzled row-major tile: lane (g = l/16, j = l%16) receives column
+// col0 + j of rows 32 s + 4 g + 0..3 and 32 s + 16 + 4 g + 0..3.  Two LDS transpose reads; in
+// each 16-lane group lane j points at row base + j/4, columns col0 + 4(j%4) .. +3.
+template <int D>
+__device__ __forceinline__ bf16x8_t tr16_frag(const char *tile, int col0, int lane, int s) {
+    using TL = Tile<D>;
+    typedef shortx4 __attribute__((address_space(3))) *lds_p;
+    const int g = lane >> 4, j = lane & 15;
+    const int col = col0 + 4 * (j & 3);
+    bf16x4_t y[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int row = 32 * s + 16 * r + 4 * g + (j >> 2);
+        const char *p = tile + TL::chunk_at(row, col >> 3) + (col & 7) * 2;
+        y[r] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_p)(p)));
+    }
+    return __builtin_shufflevector(y[0], y[1], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int NW>
 struct ScanLds {
     static constexpr int TILE = kGC * kGD * 2;                  // 64 x 128 bf16
     static constexpr int Q_OFF = 0, K_OFF = TILE, Y_OFF = 2 * TILE, P_OFF = 3 * TILE;
     static constexpr int F_OFF = P_OFF + kGC * kGC * 2;
     static constexpr int STAGE = F_OFF + 2 * kGC * 4;
-    // The chunk's O (64 tokens x 128 bf16, 256-byte rows, 16-byte chunks XOR-swizzled by the
-    // token's low 4 bits), two buffers: chunk ci writes its O here at its end, and every wave
-    // stores 16 of its rows to HBM right after chunk ci+1's barrier.
-    static constexpr int O_OFF = 2 * STAGE, OBUF = kGC * kGD * 2;
+    static constexpr int OROW = 32 * NW, OCPR = OROW / 16;      // O staging: bytes, 16-byte chunks per token
+    static constexpr int O_OFF = 2 * STAGE, OBUF = kGC * OROW;
     static constexpr int SIZE = O_OFF + 2 * OBUF;
 };
 
-__global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
-    using T128 = Tile<kGD>;
-    using T64 = Tile<kGC>;
+// Copy jobs of a stage (1 KB instructions, except the two 256-byte decay-factor rows):
+// Q 0-15, K 16-31, -Y 32-47, P 48-55, gamma 56, gamma_C / gamma 57.
+constexpr int kStageJobs = 58;
+
+// With 4 compute waves a fifth, memory wave issues every copy of the stages and every store
+// of O: a wave that issues a direct-to-LDS copy waits while the CU's memory pipeline is full,
+// and that wait no longer holds a compute wave's MFMAs.  (With 8 compute waves the registers
+// leave no room for a ninth; the compute waves copy and store themselves.)
+template <int NW>
+constexpr bool kMemWave = NW == 4;
+
+template <int NW>
+__global__ __launch_bounds__((NW + (kMemWave<NW> ? 1 : 0)) * 64) void gdn_scan(GdnArgs a, int32_t level) {
+    using LD = ScanLds<NW>;
+    constexpr bool MW = kMemWave<NW>;
+    constexpr int NS = kGD / (16 * NW);                          // workgroups per head
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hh = lane >> 5, l32 = lane & 31;
-    const int h = blockIdx.x % a.H, k = blockIdx.x / a.H;
+    const int g4 = lane >> 4, j16 = lane & 15;
+    const int cs = blockIdx.x % NS, h = (blockIdx.x / NS) % a.H, k = blockIdx.x / (NS * a.H);
     const int lb = a.level_ptr[level], le = a.level_ptr[level + 1];
     if (lb + k >= le) return;
     const int seg = a.level_segs[lb + k];
@@ -439,25 +513,25 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
     const int r = sm.x, c_first = sm.y, n_ch = sm.z, parent = sm.w;
     const int seg_t0 = n_ch > 0 ? a.chunk_meta[c_first].y : 0;
     const int last_n = n_ch > 0 ? a.chunk_meta[c_first + n_ch - 1].z : 0;
-    const int col = 32 * wave + l32;                   // this lane's state / value column
+    const int cw0 = 16 * NW * cs;                                // the workgroup's first value column
+    const bool memw = MW && wave == NW;                          // the memory wave
+    const int v0 = cw0 + 16 * (memw ? 0 : wave);                 // the wave's first value column
 
-    // State columns 32 wave .. +31, rows in 4 blocks of 32 (accumulator layout).
-    floatx16 Hs[4];
-    if (parent < 0) {
+    // H rows 16 kb + 4 g + i, column v0 + j (accumulator layout).
+    floatx4 Hs[8];
+    if (parent < 0 || memw) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Hs[j] = zero16();
+        for (int kb = 0; kb < 8; ++kb) Hs[kb] = zero4();
     } else {
-        const float *src = a.states + (int64_t(parent) * a.H + h) * kGD * kGD;
+        const float *src = a.states + (int64_t(parent) * a.H + h) * kGD * kGD + v0 + j16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) Hs[j][i] = src[(32 * j + 8 * (i / 4) + 4 * hh + (i % 4)) * kGD + col];
+            for (int i = 0; i < 4; ++i) Hs[kb][i] = src[(16 * kb + 4 * g4 + i) * kGD];
     }
 
     const int stride = a.H * kGD * 2;
     const uint32_t lds0 = lds_base(smem);
-    // Chunk ci's stage is copied in 1 KB jobs that the chunk before spreads over its MFMA steps.
-    // Per wave: jobs 0-3 Q, 4-7 K, 8-11 -Y, 12-13 P, 14 the decay factors (waves 0 and 1).
     struct StageSrc {
         int32x4_t q, k, y, p, f;
         uint32_t base;
@@ -471,231 +545,236 @@ __global__ __launch_bounds__(256) void gdn_scan(GdnArgs a, int32_t level) {
         ss.k = tile_rsrc(reinterpret_cast<const char *>(a.kh) + hoff, n, stride);
         ss.y = tile_rsrc(reinterpret_cast<const char *>(a.Yn) + chh * kGC * kGD * 2, kGC, kGD * 2);
         ss.p = tile_rsrc(reinterpret_cast<const char *>(a.P) + chh * kGC * kGC * 2, kGC, kGC * 2);
-        ss.f = buf_rsrc(a.F + chh * 2 * kGC + (wave & 1) * kGC, kGC * 4);
-        ss.base = lds0 + (ci & 1) * ScanLds::STAGE;
+        ss.f = buf_rsrc(a.F + chh * 2 * kGC, 2 * kGC * 4);
+        ss.base = lds0 + (ci & 1) * LD::STAGE;
         return ss;
     };
-    auto stage_job = [&](const StageSrc &ss, int jb) __attribute__((always_inline)) {
-        if (jb < 4) copy_block<kGD>(ss.q, stride, ss.base + ScanLds::Q_OFF, wave + 4 * jb, lane);
-        else if (jb < 8) copy_block<kGD>(ss.k, stride, ss.base + ScanLds::K_OFF, wave + 4 * (jb - 4), lane);
-        else if (jb < 12) copy_block<kGD>(ss.y, kGD * 2, ss.base + ScanLds::Y_OFF, wave + 4 * (jb - 8), lane);
-        else if (jb < 14) copy_block<kGC>(ss.p, kGC * 2, ss.base + ScanLds::P_OFF, wave + 4 * (jb - 12), lane);
-        else if (jb == 14 && wave < 2) buf_to_lds4(ss.f, ss.base + ScanLds::F_OFF + wave * kGC * 4, lane * 4);
+    // The wave's copy job jj of a stage: job wave + NW jj of the list (wave-uniform branches).
+    constexpr int kJobs = (kStageJobs + NW - 1) / NW;
+    auto stage_job = [&](const StageSrc &ss, int jj) __attribute__((always_inline)) {
+        const int jb = wave + NW * jj;
+        if (jb < 16) copy_block<kGD>(ss.q, stride, ss.base + LD::Q_OFF, jb, lane);
+        else if (jb < 32) copy_block<kGD>(ss.k, stride, ss.base + LD::K_OFF, jb - 16, lane);
+        else if (jb < 48) copy_block<kGD>(ss.y, kGD * 2, ss.base + LD::Y_OFF, jb - 32, lane);
+        else if (jb < 56) copy_block<kGC>(ss.p, kGC * 2, ss.base + LD::P_OFF, jb - 48, lane);
+        else if (jb < kStageJobs) buf_to_lds4(ss.f, ss.base + LD::F_OFF + (jb - 56) * kGC * 4, (jb - 56) * kGC * 4 + lane * 4);
     };
-    constexpr int kStageJobs = 15;
-    // U of chunk ci, this wave's 32 columns: un[tb][q] holds (t = 32 tb + 8 q + 4 hh + e, col).
-    float4 un[2][4];
+    // U of chunk ci, this wave's 16 columns: un[tb] holds (t = 16 tb + 4 g + 0..3, v0 + j).
+    floatx4 un[4];
     auto u_src = [&](int ci) __attribute__((always_inline)) {
         return reinterpret_cast<const float4 *>(a.U + (int64_t(c_first + ci) * a.H + h) * kGC * kGD) +
-               wave * (kGC * 32 / 4) + lane;
+               (v0 / 16) * 4 * 64 + lane;
+    };
+    auto load_u = [&](const float4 *us, int tb) __attribute__((always_inline)) {
+        const float4 x = us[tb * 64];
+        un[tb] = floatx4{x.x, x.y, x.z, x.w};
+    };
+    // Every copy of a stage (the memory wave).
+    auto stage_all = [&](const StageSrc &ss) __attribute__((always_inline)) {
+        static_for<16>([&](auto bc) __attribute__((always_inline)) {
+            constexpr int b = decltype(bc)::value;
+            copy_block<kGD>(ss.q, stride, ss.base + LD::Q_OFF, b, lane);
+            copy_block<kGD>(ss.k, stride, ss.base + LD::K_OFF, b, lane);
+            copy_block<kGD>(ss.y, kGD * 2, ss.base + LD::Y_OFF, b, lane);
+            if constexpr (b < 8) copy_block<kGC>(ss.p, kGC * 2, ss.base + LD::P_OFF, b, lane);
+            if constexpr (b < 2) buf_to_lds4(ss.f, ss.base + LD::F_OFF + b * kGC * 4, b * kGC * 4 + lane * 4);
+        });
+    };
+    // Chunk c's O from its LDS buffer to HBM: NI instructions from instruction i0 on, 16 bytes
+    // a lane, OCPR lanes a token row (rows of real tokens only).
+    auto store_rows = [&](int c, auto i0c, auto nic) __attribute__((always_inline)) {
+        constexpr int RPI = 64 / LD::OCPR;                       // rows per instruction
+        constexpr int NI = decltype(nic)::value;
+        const int i0 = i0c;
+        const int n = c + 1 < n_ch ? kGC : last_n;
+        const char *ob = smem + LD::O_OFF + (c & 1) * LD::OBUF;
+        char *og = reinterpret_cast<char *>(a.o) + ((int64_t(r) * a.T + seg_t0 + kGC * c) * a.H + h) * kGD * 2 + cw0 * 2;
+        const int cc = lane % LD::OCPR;
+        uint4 v[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int t = (i0 + i) * RPI + lane / LD::OCPR;
+            v[i] = *reinterpret_cast<const uint4 *>(ob + t * LD::OROW + ((cc ^ (t & (LD::OCPR - 1))) << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int t = (i0 + i) * RPI + lane / LD::OCPR;
+            if (t < n) *reinterpret_cast<uint4 *>(og + int64_t(t) * a.H * kGD * 2 + cc * 16) = v[i];
+        }
+    };
+    constexpr int kOInstr = kGC * LD::OCPR / 64;                 // store instructions per chunk
+    // The chunk's O stores: all of them by the memory wave, else a share per compute wave.
+    auto store_o = [&](int c) __attribute__((always_inline)) {
+        if constexpr (MW) store_rows(c, std::integral_constant<int, 0>{}, std::integral_constant<int, kOInstr>{});
+        else store_rows(c, wave * (kOInstr / NW), std::integral_constant<int, kOInstr / NW>{});
     };
 
     if (n_ch > 0) {
-        const StageSrc s0 = stage_src(0);
+        if (memw) {
+            stage_all(stage_src(0));
+        } else {
+            if constexpr (!MW) {
+                const StageSrc s0 = stage_src(0);
 #pragma unroll
-        for (int jb = 0; jb < kStageJobs; ++jb) stage_job(s0, jb);
-        const float4 *us = u_src(0);
+                for (int jj = 0; jj < kJobs; ++jj) stage_job(s0, jj);
+            }
+            const float4 *us = u_src(0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) un[u / 4][u % 4] = us[u * 64];
+            for (int tb = 0; tb < 4; ++tb) load_u(us, tb);
+        }
     }
-    // Chunk c's O from its LDS buffer to HBM: this wave's 16 token rows, 16 bytes a lane, 16
-    // lanes a row (rows of real tokens only).
-    auto store_o = [&](int c) __attribute__((always_inline)) {
-        const int n = c + 1 < n_ch ? kGC : last_n;
-        const char *ob = smem + ScanLds::O_OFF + (c & 1) * ScanLds::OBUF;
-        char *og = reinterpret_cast<char *>(a.o) + ((int64_t(r) * a.T + seg_t0 + kGC * c) * a.H + h) * kGD * 2;
-        const int cc = lane & 15;
-        uint4 v[4];
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-            const int t = 16 * wave + 4 * k4 + (lane >> 4);
-            v[k4] = *reinterpret_cast<const uint4 *>(ob + t * (kGD * 2) + ((cc ^ (t & 15)) << 4));
-        }
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-            const int t = 16 * wave + 4 * k4 + (lane >> 4);
-            if (t < n) *reinterpret_cast<uint4 *>(og + int64_t(t) * a.H * kGD * 2 + cc * 16) = v[k4];
-        }
-    };
     for (int ci = 0; ci < n_ch; ++ci) {
         // Chunk ci's stage and U have landed for every wave; every wave is done with chunk
         // ci-1, whose stage buffer chunk ci+1 takes, and chunk ci-1's O is in LDS.
         wait_loads();
         __syncthreads();
-        // Chunk ci-1's O leaves now, while no copy is queued ahead of it, and has the whole
-        // chunk to be acknowledged before the next wait for loads (which counts stores too).
-        if (ci > 0) store_o(ci - 1);
+        if (memw) {
+            // The next chunk's stage first (the compute waves wait for it), then chunk ci-1's
+            // O, which has the whole chunk to be acknowledged.
+            if (ci + 1 < n_ch) stage_all(stage_src(ci + 1));
+            if (ci > 0) store_o(ci - 1);
+            continue;
+        }
+        // Without a memory wave chunk ci-1's O leaves now, while no copy is queued ahead of it,
+        // and has the whole chunk to be acknowledged before the next wait for loads (which
+        // counts stores too).
+        if (!MW && ci > 0) store_o(ci - 1);
         const bool more = ci + 1 < n_ch;
         const StageSrc nx = stage_src(ci + 1);
         const float4 *nu = u_src(ci + 1);
-        const int n = more ? kGC : last_n;
-        const char *st = smem + (ci & 1) * ScanLds::STAGE;
-        const char *Qt = st + ScanLds::Q_OFF, *Kt = st + ScanLds::K_OFF;
-        const char *Yt = st + ScanLds::Y_OFF, *Pt = st + ScanLds::P_OFF;
-        const float *Fs = reinterpret_cast<const float *>(st + ScanLds::F_OFF);
-        floatx16 W[2], O[2];
+        const char *st = smem + (ci & 1) * LD::STAGE;
+        const char *Qt = st + LD::Q_OFF, *Kt = st + LD::K_OFF;
+        const char *Yt = st + LD::Y_OFF, *Pt = st + LD::P_OFF;
+        const float *Fs = reinterpret_cast<const float *>(st + LD::F_OFF);
+        floatx4 W[4], Ot[4];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            O[tb] = zero16();
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                W[tb][4 * q + 0] = un[tb][q].x;
-                W[tb][4 * q + 1] = un[tb][q].y;
-                W[tb][4 * q + 2] = un[tb][q].z;
-                W[tb][4 * q + 3] = un[tb][q].w;
-            }
+        for (int tb = 0; tb < 4; ++tb) {
+            W[tb] = un[tb];
+            Ot[tb] = zero4();
         }
 
-        // W = U - Y H and Q H, H as bf16 B operands; step s covers k rows 16 s .. 16 s + 15 for
-        // both row blocks, its A fragments read one step ahead; the next chunk's stage copies
-        // ride along two jobs a step.
+        // W = U - Y H and O^T = H^T Q^T, H as bf16 operands of both; step s covers reduced rows
+        // 32 s .. 32 s + 31, the tiles' fragments read one step ahead; the next chunk's stage
+        // copies ride along.
         {
-            bf16x8_t hb[8];
+            bf16x8_t hb[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int s = 0; s < 4; ++s) hb[s] = pair_frag(Hs[2 * s], Hs[2 * s + 1]);
+            bf16x8_t fy[4], fq[4];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) hb[2 * j + ks] = acc_frag(Hs[j], ks);
-            bf16x8_t fy[2], fq[2];
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                fy[tb] = T128::perm_frag(Yt, 32 * tb, lane, 0);
-                fq[tb] = T128::perm_frag(Qt, 32 * tb, lane, 0);
+            for (int tb = 0; tb < 4; ++tb) {
+                fy[tb] = row16_frag<kGD>(Yt, 16 * tb + j16, g4, 0);
+                fq[tb] = row16_frag<kGD>(Qt, 16 * tb + j16, g4, 0);
             }
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                bf16x8_t ny[2], nq[2];
-                if (s + 1 < 8) {
+            for (int s = 0; s < 4; ++s) {
+                bf16x8_t ny[4], nq[4];
+                if (s + 1 < 4) {
 #pragma unroll
-                    for (int tb = 0; tb < 2; ++tb) {
-                        ny[tb] = T128::perm_frag(Yt, 32 * tb, lane, s + 1);
-                        nq[tb] = T128::perm_frag(Qt, 32 * tb, lane, s + 1);
+                    for (int tb = 0; tb < 4; ++tb) {
+                        ny[tb] = row16_frag<kGD>(Yt, 16 * tb + j16, g4, s + 1);
+                        nq[tb] = row16_frag<kGD>(Qt, 16 * tb + j16, g4, s + 1);
                     }
                 }
-                if (more) {
-                    if (2 * s < kStageJobs) stage_job(nx, 2 * s);
-                    if (2 * s + 1 < kStageJobs) stage_job(nx, 2 * s + 1);
+                if (!MW && more) {
+#pragma unroll
+                    for (int jj = s * kJobs / 4; jj < (s + 1) * kJobs / 4; ++jj) stage_job(nx, jj);
                 }
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    W[tb] = mfma(fy[tb], hb[s], W[tb]);
-                    O[tb] = mfma(hb[s], fq[tb], O[tb]);       // (Q H)^T = H^T Q^T
+                for (int tb = 0; tb < 4; ++tb) {
+                    W[tb] = mfma16(fy[tb], hb[s], W[tb]);
+                    Ot[tb] = mfma16(hb[s], fq[tb], Ot[tb]);       // (Q H)^T = H^T Q^T
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if (s + 1 < 8) {
+                if (s + 1 < 4) {
 #pragma unroll
-                    for (int tb = 0; tb < 2; ++tb) {
+                    for (int tb = 0; tb < 4; ++tb) {
                         fy[tb] = ny[tb];
                         fq[tb] = nq[tb];
                     }
                 }
             }
         }
-        // O^T = (Q H)^T diag(gamma) + W^T P^T, O^T[tb] holding value columns 32 wave + 8 (i/4) +
-        // 4 hh + i%4 (rows) of token 32 tb + lane % 32 (column).  The next chunk's U rides along
-        // two loads a step.
+        // O^T = (Q H)^T diag(gamma) + W^T P^T: Ot[tb] holds value columns v0 + 4 g + i (rows)
+        // of token 16 tb + j (column).  The next chunk's U rides along.
         {
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                const float gm = Fs[32 * tb + l32];
+            for (int tb = 0; tb < 4; ++tb) {
+                const float gm = Fs[16 * tb + j16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) O[tb][i] *= gm;
+                for (int i = 0; i < 4; ++i) Ot[tb][i] *= gm;
             }
-            bf16x8_t wb[4];
+            bf16x8_t wb[2];
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
+            for (int ks = 0; ks < 2; ++ks) wb[ks] = pair_frag(W[2 * ks], W[2 * ks + 1]);
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) wb[2 * sb + ks] = acc_frag(W[sb], ks);
-            bf16x8_t fp[2];
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8_t fp[4];
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) fp[tb] = T64::perm_frag(Pt, 32 * tb, lane, 0);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                bf16x8_t np[2];
-                if (s + 1 < 4) {
-#pragma unroll
-                    for (int tb = 0; tb < 2; ++tb) np[tb] = T64::perm_frag(Pt, 32 * tb, lane, s + 1);
-                }
+                for (int tb = 0; tb < 4; ++tb) fp[tb] = row16_frag<kGC>(Pt, 16 * tb + j16, g4, ks);
                 if (more) {
-                    un[(2 * s) / 4][(2 * s) % 4] = nu[(2 * s) * 64];
-                    un[(2 * s + 1) / 4][(2 * s + 1) % 4] = nu[(2 * s + 1) * 64];
+                    load_u(nu, 2 * ks);
+                    load_u(nu, 2 * ks + 1);
                 }
 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) O[tb] = mfma(wb[s], fp[tb], O[tb]);   // (P W)^T = W^T P^T
+                for (int tb = 0; tb < 4; ++tb) Ot[tb] = mfma16(wb[ks], fp[tb], Ot[tb]);   // (P W)^T = W^T P^T
                 __builtin_amdgcn_sched_barrier(0);
-                if (s + 1 < 4) {
-#pragma unroll
-                    for (int tb = 0; tb < 2; ++tb) fp[tb] = np[tb];
-                }
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // H <- gamma_C H + K^T diag(gamma_C / gamma) W; step s = (row block tb, k half ks), the
-        // four state blocks j interleaved, K^T fragments read one step ahead.
+        // H <- gamma_C H + K^T diag(gamma_C / gamma) W; k-step ks over tokens 32 ks .. +31, the
+        // eight state blocks kb interleaved, K^T fragments read one step ahead.
         {
-            bf16x8_t wg[4];
+            bf16x8_t wg[2];
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 dg = *reinterpret_cast<const float4 *>(Fs + kGC + 32 * tb + 8 * q + 4 * hh);
-                    W[tb][4 * q + 0] *= dg.x;
-                    W[tb][4 * q + 1] *= dg.y;
-                    W[tb][4 * q + 2] *= dg.z;
-                    W[tb][4 * q + 3] *= dg.w;
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) wg[2 * tb + ks] = acc_frag(W[tb], ks);
+            for (int sb = 0; sb < 4; ++sb) {
+                const float4 dg = *reinterpret_cast<const float4 *>(Fs + kGC + 16 * sb + 4 * g4);
+                W[sb][0] *= dg.x;
+                W[sb][1] *= dg.y;
+                W[sb][2] *= dg.z;
+                W[sb][3] *= dg.w;
             }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) wg[ks] = pair_frag(W[2 * ks], W[2 * ks + 1]);
             const float dC = Fs[kGC - 1];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) Hs[j][i] *= dC;
-            bf16x8_t fk[4];
+                for (int i = 0; i < 4; ++i) Hs[kb][i] *= dC;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fk[j] = T128::tr_frag(Kt, 0, lane, 0, j);
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8_t fk[8];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                bf16x8_t nk[4];
-                if (s + 1 < 4) {
+                for (int kb = 0; kb < 8; ++kb) fk[kb] = tr16_frag<kGD>(Kt, 16 * kb, lane, ks);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) nk[j] = T128::tr_frag(Kt, 32 * ((s + 1) / 2), lane, (s + 1) % 2, j);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) Hs[j] = mfma(fk[j], wg[s], Hs[j]);
+                for (int kb = 0; kb < 8; ++kb) Hs[kb] = mfma16(fk[kb], wg[ks], Hs[kb]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (s + 1 < 4) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) fk[j] = nk[j];
-                }
             }
         }
         {
             // O of the chunk into its LDS buffer: four consecutive value columns of one token
-            // per 8-byte write.
-            char *ob = smem + ScanLds::O_OFF + (ci & 1) * ScanLds::OBUF;
+            // per 8-byte write (local columns 16 wave + 4 g .. +3).
+            char *ob = smem + LD::O_OFF + (ci & 1) * LD::OBUF;
+            const int c16 = 2 * wave + (g4 >> 1);
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                const int t = 32 * tb + l32;
+            for (int tb = 0; tb < 4; ++tb) {
+                const int t = 16 * tb + j16;
+                bf16x4_t v4;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    bf16x4_t v4;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(O[tb][4 * q + e]);
-                    *reinterpret_cast<bf16x4_t *>(ob + t * (kGD * 2) + (((4 * wave + q) ^ (t & 15)) << 4) + 8 * hh) = v4;
-                }
+                for (int i = 0; i < 4; ++i) v4[i] = static_cast<__bf16>(Ot[tb][i]);
+                *reinterpret_cast<bf16x4_t *>(ob + t * LD::OROW + ((c16 ^ (t & (LD::OCPR - 1))) << 4) + 8 * (g4 & 1)) = v4;
             }
         }
     }
     if (n_ch > 0) {
         __syncthreads();   // the last chunk's O is in LDS
-        store_o(n_ch - 1);
+        if (memw || !MW) store_o(n_ch - 1);
     }
-    float *dst = a.states + (int64_t(seg) * a.H + h) * kGD * kGD;
+    if (memw) return;
+    float *dst = a.states + (int64_t(seg) * a.H + h) * kGD * kGD + v0 + j16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dst[(32 * j + 8 * (i / 4) + 4 * hh + (i % 4)) * kGD + col] = Hs[j][i];
+        for (int i = 0; i < 4; ++i) dst[(16 * kb + 4 * g4 + i) * kGD] = Hs[kb][i];
 }
 
 }  // namespace
@@ -732,11 +811,26 @@ hipError_t launch_gdn(const GdnShape &sh, const GdnLayout &L, char *gws, const v
                                            hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
         if (e != hipSuccess) return e;
         gdn_prep<<<L.n_chunks * sh.H, 256, PrepLds::SIZE, s>>>(a);
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                ScanLds::SIZE);
-        if (e != hipSuccess) return e;
-        for (int32_t lev = 0; lev < L.n_levels; ++lev)
-            gdn_scan<<<L.max_level_segs * sh.H, 256, ScanLds::SIZE, s>>>(a, lev);
+        // Two workgroups of 4 waves per (segment, head) while that is at most two workgroups per
+        // CU for the widest level, else one of 8 waves (the chunk tiles copied once per head).
+        int dev = 0, n_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+            n_cu = 256;
+        const int64_t split_wgs = int64_t(L.max_level_segs) * sh.H * 2;
+        if (split_wgs <= 2 * int64_t(n_cu)) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan<4>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, ScanLds<4>::SIZE);
+            if (e != hipSuccess) return e;
+            for (int32_t lev = 0; lev < L.n_levels; ++lev)
+                gdn_scan<4><<<unsigned(split_wgs), 5 * 64, ScanLds<4>::SIZE, s>>>(a, lev);
+        } else {
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan<8>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, ScanLds<8>::SIZE);
+            if (e != hipSuccess) return e;
+            for (int32_t lev = 0; lev < L.n_levels; ++lev)
+                gdn_scan<8><<<L.max_level_segs * sh.H, 8 * 64, ScanLds<8>::SIZE, s>>>(a, lev);
+        }
     }
     return hipGetLastError();
 }
