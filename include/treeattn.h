@@ -295,6 +295,12 @@ int tree_attn_bwd(const tree_attn_desc *d, const void *ws, void *bws, const void
  */
 typedef struct {
     int32_t n_chunks, n_segs, n_levels, max_level_segs;
+    /* Depth levels 0..31 with few segments (at most the device's CU count / heads): bit l of
+     * narrow_levels; narrow_segs = the most segments of such a level.  tree_gdn_fwd splits a
+     * head's state over two workgroups on these levels (launch shape only; results do not
+     * depend on it). */
+    int32_t narrow_segs;
+    uint32_t narrow_levels;
 } tree_gdn_info;
 int tree_gdn_workspace_size(const tree_attn_desc *d, const int32_t *h_seg_row_ptr, const int32_t *h_seg_len,
                             size_t *bytes);

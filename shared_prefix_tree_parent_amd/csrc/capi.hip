@@ -333,9 +333,22 @@ extern "C" int tree_gdn_plan(const tree_attn_desc *d, const int32_t *h_seg_row_p
     for (int32_t g = 0; g < n_segs; ++g) n_levels = std::max(n_levels, depth[g] + 1);
     std::vector<int32_t> level_ptr(size_t(n_levels) + 1, 0), level_segs(n_segs);
     for (int32_t g = 0; g < n_segs; ++g) ++level_ptr[depth[g] + 1];
-    int32_t max_level = 0;
+    // Narrow levels: at most (CUs / heads) segments, so that two workgroups per (segment,
+    // head) stay within two per CU.
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+        n_cu = 256;
+    const int32_t narrow_max = std::max(1, n_cu / std::max(1, d->h_q));
+    int32_t max_level = 0, narrow_segs = 0;
+    uint32_t narrow_levels = 0;
     for (int32_t l = 0; l < n_levels; ++l) {
-        max_level = std::max(max_level, level_ptr[l + 1]);
+        const int32_t cnt = level_ptr[l + 1];
+        max_level = std::max(max_level, cnt);
+        if (l < 32 && cnt <= narrow_max) {
+            narrow_levels |= 1u << l;
+            narrow_segs = std::max(narrow_segs, cnt);
+        }
         level_ptr[l + 1] += level_ptr[l];
     }
     {
@@ -359,6 +372,8 @@ extern "C" int tree_gdn_plan(const tree_attn_desc *d, const int32_t *h_seg_row_p
     info->n_segs = n_segs;
     info->n_levels = n_levels;
     info->max_level_segs = max_level;
+    info->narrow_segs = narrow_segs;
+    info->narrow_levels = narrow_levels;
     return TREE_OK;
 }
 
@@ -367,7 +382,8 @@ extern "C" int tree_gdn_fwd(const tree_attn_desc *d, const tree_gdn_info *info, 
                             void *o, void *stream) {
     if (!gdn_shape_ok(d) || info == nullptr || gws == nullptr) return TREE_E_INVAL;
     if (info->n_chunks < 0 || info->n_segs < 0 || info->n_levels < 0 || info->n_levels > info->n_segs ||
-        info->max_level_segs < 0 || info->max_level_segs > info->n_segs)
+        info->max_level_segs < 0 || info->max_level_segs > info->n_segs || info->narrow_segs < 0 ||
+        info->narrow_segs > info->max_level_segs)
         return TREE_E_INVAL;
     if (d->n_rows > 0 && (x_q == nullptr || x_k == nullptr || x_v == nullptr || conv_w == nullptr || g == nullptr ||
                           beta == nullptr || o == nullptr))
@@ -375,6 +391,8 @@ extern "C" int tree_gdn_fwd(const tree_attn_desc *d, const tree_gdn_info *info, 
     GdnLayout L = make_gdn_layout(d->n_rows, d->row_len, d->h_q, info->n_chunks, info->n_segs);
     L.n_levels = info->n_levels;
     L.max_level_segs = info->max_level_segs;
+    L.narrow_segs = info->narrow_segs;
+    L.narrow_levels = info->narrow_levels;
     GdnShape sh{d->n_rows, d->row_len, d->h_q, 1e-6f};
     const hipError_t e = launch_gdn(sh, L, static_cast<char *>(gws), x_q, x_k, x_v, conv_w, g, beta, o,
                                     static_cast<hipStream_t>(stream));

@@ -811,25 +811,21 @@ hipError_t launch_gdn(const GdnShape &sh, const GdnLayout &L, char *gws, const v
                                            hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
         if (e != hipSuccess) return e;
         gdn_prep<<<L.n_chunks * sh.H, 256, PrepLds::SIZE, s>>>(a);
-        // Two workgroups of 4 waves per (segment, head) while that is at most two workgroups per
-        // CU for the widest level, else one of 8 waves (the chunk tiles copied once per head).
-        int dev = 0, n_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
-            n_cu = 256;
-        const int64_t split_wgs = int64_t(L.max_level_segs) * sh.H * 2;
-        if (split_wgs <= 2 * int64_t(n_cu)) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan<4>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, ScanLds<4>::SIZE);
-            if (e != hipSuccess) return e;
-            for (int32_t lev = 0; lev < L.n_levels; ++lev)
-                gdn_scan<4><<<unsigned(split_wgs), 5 * 64, ScanLds<4>::SIZE, s>>>(a, lev);
-        } else {
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan<8>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, ScanLds<8>::SIZE);
-            if (e != hipSuccess) return e;
-            for (int32_t lev = 0; lev < L.n_levels; ++lev)
-                gdn_scan<8><<<L.max_level_segs * sh.H, 8 * 64, ScanLds<8>::SIZE, s>>>(a, lev);
+        // Narrow levels (few segments): two workgroups of 4 compute waves and a memory wave per
+        // (segment, head); the others: one workgroup of 8 waves per (segment, head).
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan<4>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                ScanLds<4>::SIZE);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan<8>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                ScanLds<8>::SIZE);
+        if (e != hipSuccess) return e;
+        for (int32_t lev = 0; lev < L.n_levels; ++lev) {
+            if (lev < 32 && ((L.narrow_levels >> lev) & 1u) != 0) {
+                if (L.narrow_segs > 0)
+                    gdn_scan<4><<<unsigned(L.narrow_segs * sh.H * 2), 5 * 64, ScanLds<4>::SIZE, s>>>(a, lev);
+            } else if (L.max_level_segs > 0) {
+                gdn_scan<8><<<unsigned(L.max_level_segs * sh.H), 8 * 64, ScanLds<8>::SIZE, s>>>(a, lev);
+            }
         }
     }
     return hipGetLastError();

@@ -141,6 +141,8 @@ struct GdnLayout {
     size_t states = 0;       // f32[n_segs*H*128*128]: final state of every segment
     size_t total = 0;
     int32_t n_chunks = 0, n_segs = 0, n_levels = 0, max_level_segs = 0;
+    int32_t narrow_segs = 0;      // levels of bit l in narrow_levels: at most this many segments
+    uint32_t narrow_levels = 0;
 };
 inline GdnLayout make_gdn_layout(int32_t R, int32_t T, int32_t H, int32_t n_chunks, int32_t n_segs) {
     GdnLayout g;

@@ -98,6 +98,30 @@ def test_gdn_chunk_boundaries():
     check(got, Gd.gdn_forward(gin), _real(rows), "chunk boundaries")
 
 
+def test_gdn_narrow_and_wide_levels():
+    """A root of 150 tokens with 24 children at 16 heads: the root's level has one segment
+    (two workgroups per head plus a memory wave), the children's level more segments than CUs
+    per head allow (one 8-wave workgroup per head); the plan marks exactly the narrow level."""
+    import torch
+    H = 16
+    lens = [150] + [20 + 3 * i for i in range(24)]
+    pars = [-1] + [0] * 24
+    T = int(np.sum(lens)) + 37
+    st = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+    rows = RowInputs("gdn", 1, T, 1, 1, 128, "bf16", 0.0, np.array([0, len(lens)], np.int32), st,
+                     np.asarray(lens, np.int32), np.asarray(pars, np.int32), np.zeros(len(lens), np.int32), 0,
+                     real_len=np.array([int(np.sum(lens))]))
+    gin = draw_gdn(rows, heads=H, seed=13)
+    got, plan = run_gdn(gin)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    narrow_max = max(1, n_cu // H)
+    want_mask = (1 if 1 <= narrow_max else 0) | (2 if 24 <= narrow_max else 0)
+    log(f"  {n_cu} CUs: narrow levels {plan.info.narrow_levels:#x}, narrow_segs {plan.info.narrow_segs}")
+    assert plan.info.n_levels == 2 and plan.info.max_level_segs == 24
+    assert plan.info.narrow_levels == want_mask
+    check(got, Gd.gdn_forward(gin), _real(rows), "narrow and wide levels")
+
+
 def test_gdn_one_long_segment():
     T = 1280
     rows = RowInputs("gdn", 1, T, 1, 1, 128, "bf16", 0.0, np.array([0, 1], np.int32), np.array([0], np.int32),
