@@ -323,9 +323,12 @@ struct KvLds {
     static constexpr int Q_OFF = 0, DO_OFF = TILE, LSE_OFF = 2 * TILE, DL_OFF = 2 * TILE + kQBlk * 4;
     static constexpr int NS = 4;                                // stages, one block each
     static constexpr int AHEAD = NS - 1;                        // blocks copied ahead of the one in use
-    // copies per wave per block: Q and dO split over the waves; waves 0 and 1 also copy LSE2 / D
-    static constexpr int PERW = 2 * (TILE / 1024) / kKvWaves;
-    static_assert((2 * (TILE / 1024)) % kKvWaves == 0, "waves must split a block evenly");
+    // load instructions per block, all issued by the memory wave: Q and dO (1 KB each), LSE2, D
+    static constexpr int PERB = 2 * (TILE / 1024) + 2;
+    static_assert((AHEAD - 1) * PERB < 64, "vmcnt field");
+    // V of the pair's 128 keys (B operand of dP = dO V^T, read like the Q / dO rows), then the
+    // slice's q-tile list
+    static constexpr int V_OFF = NS * BLK, VTILE = 2 * kBK * D * 2, LIST_OFF = V_OFF + VTILE;
 };
 
 // Softmax of one block for a wave's 32 keys: P and dS as bf16 operands (accumulator register
@@ -371,22 +374,24 @@ __device__ __forceinline__ void kv_softmax(const floatx16 &s, const floatx16 &dp
 // One block for a wave: S and dP, softmax, then dV^T += dO^T P and dK^T += Q^T dS.
 template <int D>
 __device__ __forceinline__ void kv_block(const char *blk, const LaneOffsets<D> &lo, const bf16x8_t (&kf)[D / 16],
-                                         const bf16x8_t (&vf)[D / 16], float c, int h, int key, int kend_k,
+                                         const char *Vt, float c, int h, int key, int kend_k,
                                          int q0, bool partial, floatx16 (&dk)[D / 32], floatx16 (&dv)[D / 32]) {
     using TL = Tile<D>;
     using LD = KvLds<D>;
     const char *Qt = blk + LD::Q_OFF;
     const char *Ot = blk + LD::DO_OFF;
-    // Operand reads run RING MFMAs ahead of their use, from the S / dP products into the dV /
+    // Operand reads run RING reads ahead of their use, from the S / dP products into the dV /
     // dK ones (whose first operands are read before the softmax).
-    constexpr int NP1 = 2 * TL::NDS, NP2 = 4 * TL::NDB, RING = 4;
+    constexpr int NP1 = 3 * TL::NDS, NP2 = 4 * TL::NDB, RING = 4;
     static_assert(NP1 >= RING && NP2 >= RING, "ring deeper than a phase");
-    // operand i < NP1: row read of Q (even) / dO (odd) for S / dP; NP1 + j: transposed read of
-    // dO (j even, for dV) / Q (j odd, for dK), j = (ks NDB + db) 2 + t
+    // operand i < NP1: row read of Q (i % 3 == 0, for S), dO (1) and V (2, for dP) at k-step
+    // i / 3; NP1 + j: transposed read of dO (j even, for dV) / Q (j odd, for dK),
+    // j = (ks NDB + db) 2 + t
     auto operand = [&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         if constexpr (i < NP1) {
-            return TL::row_at((i % 2 == 0 ? Qt : Ot) + lo.row[i / 2]);
+            constexpr int t = i % 3;
+            return TL::row_at((t == 0 ? Qt : t == 1 ? Ot : Vt) + lo.row[i / 3]);
         } else {
             constexpr int j = i - NP1, t = j % 2, db = (j / 2) % TL::NDB, ks = j / 2 / TL::NDB;
             const char *base = (t == 0 ? Ot : Qt) + 16 * ks * TL::ROWB;
@@ -396,13 +401,20 @@ __device__ __forceinline__ void kv_block(const char *blk, const LaneOffsets<D> &
     bf16x8_t ring[RING];
     static_for<RING>([&](auto ic) __attribute__((always_inline)) { ring[decltype(ic)::value] = operand(ic); });
     floatx16 s = zero16(), dp = zero16();
+    bf16x8_t dof;                            // the k-step's dO operand, until its V operand
     static_for<NP1>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         const bf16x8_t op = ring[i % RING];
         ring[i % RING] = operand(std::integral_constant<int, i + RING>{});
-        if constexpr (i % 2 == 0) s = mfma(op, kf[i / 2], s);
-        else dp = mfma(op, vf[i / 2], dp);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (i % 3 == 0) {
+            s = mfma(op, kf[i / 3], s);
+            __builtin_amdgcn_sched_barrier(0);
+        } else if constexpr (i % 3 == 1) {
+            dof = op;
+        } else {
+            dp = mfma(dof, op, dp);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     });
     bf16x8_t pf[2], sf[2];
     kv_softmax<D>(s, dp, blk, h, c, partial, key, kend_k, q0 + 4 * h, pf, sf);
@@ -431,8 +443,11 @@ struct BlockCursor {
     }
 };
 
+// Waves 0-3 compute (32 keys each); wave 4, the memory wave, issues every copy of the Q / dO
+// blocks into LDS: a wave that issues a direct-to-LDS copy waits while the CU's memory
+// pipeline is full, and that wait no longer holds a compute wave's MFMAs.
 template <int D>
-__global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__((kKvWaves + 1) * 64) void dkdv_kernel(BwdArgs a) {
     using TL = Tile<D>;
     using LD = KvLds<D>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -452,31 +467,28 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     const int r = pitem / a.nP, pr = pitem % a.nP;
     const int T = a.T;
     const int n_real = a.n_real[r];
-    const int half = wave >> 1;                          // k-tile 2 pr + half
+    const bool memw = wave == kKvWaves;                  // the memory wave
+    const int half = (wave >> 1) & 1;                    // k-tile 2 pr + half
     const int key = (2 * pr + half) * kBK + 32 * (wave & 1) + l32;   // this lane's key
     const bool kin = key < T;                            // false only past an odd k-tile count
     const bool kreal = key < n_real;
     const int kend_k = kin ? a.kend[int64_t(r) * T + key] : key;      // == key at pads: never visible
     const int cls_shift = half ? 0 : 2;
 
-    // K and V fragments of the wave's 32 keys (B operands of S = Q K^T and dP = dO V^T):
-    // lane holds columns 16 ds + 8h .. +7 of its key; zero at pad keys.
-    bf16x8_t kf[TL::NDS], vf[TL::NDS];
-    {
+    // K fragments of the wave's 32 keys (B operand of S = Q K^T): lane holds columns 16 ds +
+    // 8h .. +7 of its key; zero at pad keys.  (V is read from LDS, rows past the last real key
+    // zero.)
+    bf16x8_t kf[TL::NDS];
+    if (!memw) {
         const int64_t off = ((int64_t(r) * T + (kin ? key : 0)) * a.Hkv + g) * D;
         const bf16x8_t *pk = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.k) + off);
-        const bf16x8_t *pv = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.v) + off);
 #pragma unroll
         for (int ds = 0; ds < TL::NDS; ++ds) {
-            const bf16x8_t x = pk[2 * ds + h], y = pv[2 * ds + h];
-            bf16x8_t zx, zy;
+            const bf16x8_t x = pk[2 * ds + h];
+            bf16x8_t zx;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                zx[e] = kreal ? x[e] : static_cast<__bf16>(0.f);
-                zy[e] = kreal ? y[e] : static_cast<__bf16>(0.f);
-            }
+            for (int e = 0; e < 8; ++e) zx[e] = kreal ? x[e] : static_cast<__bf16>(0.f);
             kf[ds] = zx;
-            vf[ds] = zy;
         }
     }
     const LaneOffsets<D> lo(lane);
@@ -492,8 +504,8 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     const int32_t l_begin = list_begin + NL_pair * slice / n_slices;
     const int NL = list_begin + NL_pair * (slice + 1) / n_slices - l_begin;
     // the slice's q-tile entries, staged in LDS once (no scalar load inside the block loop)
-    int32_t *lst = reinterpret_cast<int32_t *>(smem + LD::NS * LD::BLK);
-    for (int e = tid; e < NL; e += kKvWaves * 64) lst[e] = a.kp_list[l_begin + e];
+    int32_t *lst = reinterpret_cast<int32_t *>(smem + LD::LIST_OFF);
+    for (int e = tid; e < NL; e += (kKvWaves + 1) * 64) lst[e] = a.kp_list[l_begin + e];
     __syncthreads();
     const int CH = a.BQ / kQBlk;
     const int NB = NL * a.G * CH;
@@ -508,40 +520,50 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
         const uint32_t bl = lds0 + (n % LD::NS) * LD::BLK;
         const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - q0, 0), kQBlk));
         const int64_t roff = ((int64_t(r) * T + q0) * a.Hq + head) * D * 2;
-        copy_tile<D>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, bl + LD::Q_OFF, kQBlk, wave, kKvWaves, lane);
-        copy_tile<D>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride, bl + LD::DO_OFF, kQBlk, wave, kKvWaves, lane);
-        if (wave < 2 && lane < kQBlk) {
+        copy_tile<D>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, bl + LD::Q_OFF, kQBlk, 0, 1, lane);
+        copy_tile<D>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride, bl + LD::DO_OFF, kQBlk, 0, 1, lane);
+        if (lane < kQBlk) {
             const int64_t loff = (int64_t(r) * a.Hq + head) * T + q0;
-            const float *src = wave == 0 ? a.lse2 : a.delta;
-            buf_to_lds4(buf_rsrc(src + loff, uint32_t(n_valid) * 4), bl + (wave == 0 ? LD::LSE_OFF : LD::DL_OFF), lane * 4);
+            buf_to_lds4(buf_rsrc(a.lse2 + loff, uint32_t(n_valid) * 4), bl + LD::LSE_OFF, lane * 4);
+            buf_to_lds4(buf_rsrc(a.delta + loff, uint32_t(n_valid) * 4), bl + LD::DL_OFF, lane * 4);
         }
     };
 
-#pragma unroll
-    for (int n = 0; n < LD::AHEAD; ++n)
-        if (n < NB) issue(n);
-    for (int n = 0; n < NB; ++n) {
-        // Block n has landed for this wave once only the newer blocks' copies (at most
-        // AHEAD - 1 of them) may be in flight; the barrier extends that to every wave and
-        // also means every wave is done with block n - 1, whose stage block n + AHEAD takes.
-        const int newer = min(LD::AHEAD - 1, NB - 1 - n);
-        if (wave < 2) {
-            if (newer >= 2) wait_loads_but<2 * (LD::PERW + 1)>();
-            else if (newer == 1) wait_loads_but<LD::PERW + 1>();
-            else wait_loads();
-        } else {
-            if (newer >= 2) wait_loads_but<2 * LD::PERW>();
-            else if (newer == 1) wait_loads_but<LD::PERW>();
-            else wait_loads();
+    if (memw) {
+        // The memory wave: block n has landed once only the newer blocks' copies (at most
+        // AHEAD - 1 of them) may be in flight (it issues loads only, so they land in order);
+        // the barrier extends that to every wave and also means every wave is done with block
+        // n - 1, whose stage block n + AHEAD takes.
+        {
+            // the pair's V rows first: they land before block 0's copies
+            const int key0 = 2 * pr * kBK;
+            const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - key0, 0), 2 * kBK));
+            const int64_t voff = ((int64_t(r) * T + key0) * a.Hkv + g) * D * 2;
+            copy_tile<D>(reinterpret_cast<const char *>(a.v) + voff, n_valid, a.Hkv * D * 2, lds0 + LD::V_OFF, 2 * kBK,
+                         0, 1, lane);
         }
-        block_barrier();
-        if (n + LD::AHEAD < NB) issue(n + LD::AHEAD);
+#pragma unroll
+        for (int n = 0; n < LD::AHEAD; ++n)
+            if (n < NB) issue(n);
+        for (int n = 0; n < NB; ++n) {
+            const int newer = min(LD::AHEAD - 1, NB - 1 - n);
+            if (newer >= 2) wait_loads_but<2 * LD::PERB>();
+            else if (newer == 1) wait_loads_but<LD::PERB>();
+            else wait_loads();
+            block_barrier();
+            if (n + LD::AHEAD < NB) issue(n + LD::AHEAD);
+        }
+        return;
+    }
+    for (int n = 0; n < NB; ++n) {
+        block_barrier();   // block n is in LDS (the memory wave waited for it)
         const int ent = __builtin_amdgcn_readfirstlane(lst[cc.e]);
         const int q0 = (ent >> 4) * a.BQ + cc.ch * kQBlk;
         cc.next(a.G, CH);
         const int cls = (ent >> cls_shift) & 3;
         if (cls != kTileSkip)
-            kv_block<D>(smem + (n % LD::NS) * LD::BLK, lo, kf, vf, a.c, h, key, kend_k, q0, cls == kTilePartial, dk, dv);
+            kv_block<D>(smem + (n % LD::NS) * LD::BLK, lo, kf, smem + LD::V_OFF + 32 * wave * TL::ROWB, a.c, h, key,
+                        kend_k, q0, cls == kTilePartial, dk, dv);
     }
 
     if (n_slices > 1) {
@@ -639,13 +661,13 @@ hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, int n
         dq_kernel<D><<<n_items_q, kDqWaves * 64, smem, s>>>(a);
     }
     if (n_items_k > 0) {
-        // stages, then one pair's list (at most nQ entries)
-        const int smem = KvLds<D>::NS * KvLds<D>::BLK + 4 * ((a.nQ + 3) & ~3);
+        // stages, the pair's V rows, then one pair's list (at most nQ entries)
+        const int smem = KvLds<D>::LIST_OFF + 4 * ((a.nQ + 3) & ~3);
         if (smem > 160 * 1024) return hipErrorInvalidValue;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(dkdv_kernel<D>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return e;
-        dkdv_kernel<D><<<n_units_k, kKvWaves * 64, smem, s>>>(a);
+        dkdv_kernel<D><<<n_units_k, (kKvWaves + 1) * 64, smem, s>>>(a);
         dkdv_reduce<D><<<n_items_k, 256, 0, s>>>(a);
     }
     return hipGetLastError();

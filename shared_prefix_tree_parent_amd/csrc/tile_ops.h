@@ -179,8 +179,8 @@ __device__ __forceinline__ uint32_t lds_base(const char *p) {
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 template <int N>
 __device__ __forceinline__ void wait_loads_but() {
-    static_assert(N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt field (6 bits: immediate bits 3:0 and 15:14)");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
