@@ -16,7 +16,8 @@
 //   * 8 waves, one 32-row block each, two waves per SIMD: while one wave runs its softmax on
 //     the VALU the other's MFMAs issue (the template also allows 4 waves of two blocks);
 //   * K/V tiles (64 keys) are copied HBM -> LDS with direct-to-LDS loads into four buffer
-//     slots, two tiles ahead, so the copies run under the compute with no registers.
+//     slots, two tiles ahead, so the copies run under the compute with no registers; one wave
+//     per SIMD issues them.
 // MFMA orientation: S^T = K Q^T and O^T = V^T P^T, so each lane owns one query (column) of
 // every 32x32 accumulator: row max / row sum are in-lane plus one exchange with lane^32
 // (v_permlane32_swap), and the P^T operand of the second product is the first product's
@@ -356,14 +357,19 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     // there after swizzling.  The per-lane source offsets never change; the tile base lives in
     // the buffer descriptor, whose size stops at the row's last real key, so pad keys read as
     // zeros (NaN pads cannot reach PV).
-    constexpr int ROWS = 1024 / (D * Tr::kEsz), INSTR = LD::TILE / 1024, PER_WAVE = 2 * INSTR / kWaves;
-    static_assert((2 * INSTR) % kWaves == 0, "waves must split the tile evenly");
+    // Copying waves: one per SIMD (waves 0-3 sit on SIMDs 0-3).  A wave that issues a
+    // direct-to-LDS copy waits while the CU's memory pipeline is full; with one copying wave per
+    // SIMD the other wave of the SIMD keeps issuing meanwhile.
+    constexpr int kCW = kWaves >= 8 ? kWaves / 2 : kWaves;
+    const bool cw = wave < kCW;
+    constexpr int ROWS = 1024 / (D * Tr::kEsz), INSTR = LD::TILE / 1024, PER_WAVE = 2 * INSTR / kCW;
+    static_assert((2 * INSTR) % kCW == 0, "waves must split the tile evenly");
     static_assert(PER_WAVE + 1 < 16, "vmcnt field");
     int voff[PER_WAVE];
 #pragma unroll
     for (int jj = 0; jj < PER_WAVE; ++jj) {
-        const bool isv = jj >= INSTR / kWaves;
-        const int blk = isv ? wave + kWaves * (jj - INSTR / kWaves) : wave + kWaves * jj;
+        const bool isv = jj >= INSTR / kCW;
+        const int blk = isv ? wave + kCW * (jj - INSTR / kCW) : wave + kCW * jj;
         const int row = blk * ROWS + lane / Tr::CPR;
         const int c = (lane % Tr::CPR) ^ (isv ? Tr::vsw(row) : Tr::ksw(row));
         voff[jj] = row * row_stride + c * 16;
@@ -379,14 +385,16 @@ void tree_attn_fwd_kernel(FwdArgs a) {
         const int64_t tb = int64_t(kt) * 64 * row_stride;
         const int32x4_t rk = buf_rsrc(kbase0 + tb, n_valid * row_stride);
         const int32x4_t rv = buf_rsrc(vbase0 + tb, n_valid * row_stride);
+        if (cw) {
 #pragma unroll
-        for (int jj = 0; jj < PER_WAVE; ++jj) {
-            const bool isv = jj >= INSTR / kWaves;
-            const int blk = isv ? wave + kWaves * (jj - INSTR / kWaves) : wave + kWaves * jj;
-            const uint32_t dst = lds0 + (isv ? LD::V_OFF : LD::K_OFF) + slot * LD::TILE + blk * 1024;
-            buf_to_lds16(isv ? rv : rk, dst, voff[jj]);
+            for (int jj = 0; jj < PER_WAVE; ++jj) {
+                const bool isv = jj >= INSTR / kCW;
+                const int blk = isv ? wave + kCW * (jj - INSTR / kCW) : wave + kCW * jj;
+                const uint32_t dst = lds0 + (isv ? LD::V_OFF : LD::K_OFF) + slot * LD::TILE + blk * 1024;
+                buf_to_lds16(isv ? rv : rk, dst, voff[jj]);
+            }
         }
-        if (wave == kWaves - 1)
+        if (wave == kCW - 1)
             buf_to_lds4(buf_rsrc(kend_row + kt * 64, 256), lds0 + LD::KE_OFF + slot * 256, lane * 4);
     };
 
@@ -586,8 +594,9 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     if (N > 0) issue(0);
     if (N > 1) {
         issue(1);
-        if (wave == kWaves - 1) wait_loads_but<PER_WAVE + 1>();
-        else wait_loads_but<PER_WAVE>();
+        if (wave == kCW - 1) wait_loads_but<PER_WAVE + 1>();
+        else if (cw) wait_loads_but<PER_WAVE>();
+        else wait_loads();
     } else {
         wait_loads();
     }
