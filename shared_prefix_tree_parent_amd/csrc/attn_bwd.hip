@@ -131,8 +131,13 @@ struct DqLds {
     static constexpr int NB = 3;                       // k-tile buffers (tile t+2 copied under t)
     static constexpr int K_OFF = 0, V_OFF = NB * TILE, KE_OFF = 2 * NB * TILE;
     static constexpr int LIST_OFF = KE_OFF + NB * 256;
-    static constexpr int PERW = 2 * (TILE / 1024) / kDqWaves;   // K and V copies per wave per tile
-    static_assert((2 * (TILE / 1024)) % kDqWaves == 0, "waves must split a tile evenly");
+    // K and V copies per copying wave per tile.  One wave per SIMD copies (waves 0-3): a wave
+    // that issues direct-to-LDS loads stalls while the CU's memory pipeline is full, and the
+    // other wave of its SIMD keeps issuing meanwhile.
+    static constexpr int CW = 4;
+    static constexpr int PERW = 2 * (TILE / 1024) / CW;
+    static_assert((2 * (TILE / 1024)) % CW == 0, "waves must split a tile evenly");
+    static_assert(PERW + 1 < 16, "vmcnt field");
 };
 
 // One k-tile of the dq pass for a wave's 32 queries: P^T, dS^T of both 32-key blocks, then
@@ -266,9 +271,11 @@ void dq_kernel(BwdArgs a) {
         const int slot = t % NB;
         const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - kt * kBK, 0), kBK));
         const int64_t tb = int64_t(kt) * kBK * row_stride;
-        copy_tile<D>(kbase0 + tb, n_valid, row_stride, lds0 + LD::K_OFF + slot * LD::TILE, kBK, wave, kDqWaves, lane);
-        copy_tile<D>(vbase0 + tb, n_valid, row_stride, lds0 + LD::V_OFF + slot * LD::TILE, kBK, wave, kDqWaves, lane);
-        if (wave == kDqWaves - 1) buf_to_lds4(buf_rsrc(kend_row + kt * kBK, 256), lds0 + LD::KE_OFF + slot * 256, lane * 4);
+        if (wave < LD::CW) {
+            copy_tile<D>(kbase0 + tb, n_valid, row_stride, lds0 + LD::K_OFF + slot * LD::TILE, kBK, wave, LD::CW, lane);
+            copy_tile<D>(vbase0 + tb, n_valid, row_stride, lds0 + LD::V_OFF + slot * LD::TILE, kBK, wave, LD::CW, lane);
+        }
+        if (wave == LD::CW - 1) buf_to_lds4(buf_rsrc(kend_row + kt * kBK, 256), lds0 + LD::KE_OFF + slot * 256, lane * 4);
     };
 
     if (N > 0) issue(0);
@@ -279,8 +286,9 @@ void dq_kernel(BwdArgs a) {
         // slot takes tile t+2.
         if (t + 1 < N) {
             // leave tile t+1's copies (the newest) in flight
-            if (wave == kDqWaves - 1) wait_loads_but<DqLds<D>::PERW + 1>();
-            else wait_loads_but<DqLds<D>::PERW>();
+            if (wave == LD::CW - 1) wait_loads_but<DqLds<D>::PERW + 1>();
+            else if (wave < LD::CW) wait_loads_but<DqLds<D>::PERW>();
+            else wait_loads();
         } else {
             wait_loads();
         }
