@@ -301,6 +301,13 @@ typedef struct {
      * depend on it). */
     int32_t narrow_segs;
     uint32_t narrow_levels;
+    /* Chunks of depth-0 segments.  When depth 0 is narrow and deeper levels exist, tree_gdn_fwd
+     * preps only these before the depth-0 scan and preps the others beside it, as many as the
+     * scan's chain (lead_chain) leaves time for, then the rest (launch order only; results do
+     * not depend on it). */
+    int32_t lead_chunks;
+    int32_t lead_chain;   /* the most chunks of one depth-0 segment (its scan's chain length) */
+    int32_t lead_segs;    /* depth-0 segments */
 } tree_gdn_info;
 int tree_gdn_workspace_size(const tree_attn_desc *d, const int32_t *h_seg_row_ptr, const int32_t *h_seg_len,
                             size_t *bytes);

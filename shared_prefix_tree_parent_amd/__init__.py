@@ -100,7 +100,8 @@ class TileView(ctypes.Structure):
 class GdnInfo(ctypes.Structure):
     _fields_ = [("n_chunks", ctypes.c_int32), ("n_segs", ctypes.c_int32), ("n_levels", ctypes.c_int32),
                 ("max_level_segs", ctypes.c_int32), ("narrow_segs", ctypes.c_int32),
-                ("narrow_levels", ctypes.c_uint32)]
+                ("narrow_levels", ctypes.c_uint32), ("lead_chunks", ctypes.c_int32),
+                ("lead_chain", ctypes.c_int32), ("lead_segs", ctypes.c_int32)]
 
 
 _lib = None

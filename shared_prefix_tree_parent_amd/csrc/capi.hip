@@ -355,6 +355,19 @@ extern "C" int tree_gdn_plan(const tree_attn_desc *d, const int32_t *h_seg_row_p
         std::vector<int32_t> fill(level_ptr.begin(), level_ptr.end() - 1);
         for (int32_t g = 0; g < n_segs; ++g) level_segs[fill[depth[g]]++] = g;
     }
+    // Prep order: the chunks of depth-0 segments first (the depth-0 scan needs only these).
+    std::vector<int32_t> prep_order;
+    prep_order.reserve(size_t(n_chunks));
+    for (int pass = 0; pass < 2; ++pass)
+        for (int32_t c = 0; c < n_chunks; ++c)
+            if ((depth[chunk_meta[size_t(c) * 4 + 3]] == 0) == (pass == 0)) prep_order.push_back(c);
+    int32_t lead_chunks = 0, lead_chain = 0, lead_segs = 0;
+    for (int32_t c = 0; c < n_chunks; ++c) lead_chunks += depth[chunk_meta[size_t(c) * 4 + 3]] == 0 ? 1 : 0;
+    for (int32_t g = 0; g < n_segs; ++g)
+        if (depth[g] == 0) {
+            lead_chain = std::max(lead_chain, seg_meta[size_t(g) * 4 + 2]);
+            ++lead_segs;
+        }
     const GdnLayout L = make_gdn_layout(R, T, d->h_q, n_chunks, n_segs);
     char *w = static_cast<char *>(gws);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -363,7 +376,8 @@ extern "C" int tree_gdn_plan(const tree_attn_desc *d, const int32_t *h_seg_row_p
                           {L.chunk_meta, chunk_meta.data(), chunk_meta.size() * 4},
                           {L.seg_meta, seg_meta.data(), seg_meta.size() * 4},
                           {L.level_ptr, level_ptr.data(), level_ptr.size() * 4},
-                          {L.level_segs, level_segs.data(), level_segs.size() * 4}};
+                          {L.level_segs, level_segs.data(), level_segs.size() * 4},
+                          {L.prep_order, prep_order.data(), prep_order.size() * 4}};
     for (const Part &pt : parts)
         if (pt.bytes > 0 && hipMemcpyAsync(w + pt.off, pt.src, pt.bytes, hipMemcpyHostToDevice, s) != hipSuccess)
             return TREE_E_HIP;
@@ -374,6 +388,9 @@ extern "C" int tree_gdn_plan(const tree_attn_desc *d, const int32_t *h_seg_row_p
     info->max_level_segs = max_level;
     info->narrow_segs = narrow_segs;
     info->narrow_levels = narrow_levels;
+    info->lead_chunks = lead_chunks;
+    info->lead_chain = lead_chain;
+    info->lead_segs = lead_segs;
     return TREE_OK;
 }
 
@@ -383,7 +400,9 @@ extern "C" int tree_gdn_fwd(const tree_attn_desc *d, const tree_gdn_info *info, 
     if (!gdn_shape_ok(d) || info == nullptr || gws == nullptr) return TREE_E_INVAL;
     if (info->n_chunks < 0 || info->n_segs < 0 || info->n_levels < 0 || info->n_levels > info->n_segs ||
         info->max_level_segs < 0 || info->max_level_segs > info->n_segs || info->narrow_segs < 0 ||
-        info->narrow_segs > info->max_level_segs)
+        info->narrow_segs > info->max_level_segs || info->lead_chunks < 0 || info->lead_chunks > info->n_chunks ||
+        info->lead_chain < 0 || info->lead_chain > info->lead_chunks || info->lead_segs < 0 ||
+        info->lead_segs > info->n_segs)
         return TREE_E_INVAL;
     if (d->n_rows > 0 && (x_q == nullptr || x_k == nullptr || x_v == nullptr || conv_w == nullptr || g == nullptr ||
                           beta == nullptr || o == nullptr))
@@ -393,6 +412,9 @@ extern "C" int tree_gdn_fwd(const tree_attn_desc *d, const tree_gdn_info *info, 
     L.max_level_segs = info->max_level_segs;
     L.narrow_segs = info->narrow_segs;
     L.narrow_levels = info->narrow_levels;
+    L.lead_chunks = info->lead_chunks;
+    L.lead_chain = info->lead_chain;
+    L.lead_segs = info->lead_segs;
     GdnShape sh{d->n_rows, d->row_len, d->h_q, 1e-6f};
     const hipError_t e = launch_gdn(sh, L, static_cast<char *>(gws), x_q, x_k, x_v, conv_w, g, beta, o,
                                     static_cast<hipStream_t>(stream));

@@ -33,6 +33,7 @@
 //     segment's final H is stored for its children.  A chunk's O goes to LDS at its end and
 //     leaves as whole 256-byte rows right after the next chunk's barrier, so no chunk waits
 //     for its own stores to be acknowledged.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -171,24 +172,30 @@ struct GdnArgs {
     float *F;                    // [n_chunks, H, 128]: gamma_t (t < 64), gamma_C / gamma_t
     float *states;               // [n_segs, H, 128, 128]
     __bf16 *o;                   // [R, T, H, 128]
+    const int32_t *prep_order;   // [n_chunks]: the chunks of depth-0 segments first, then the rest
+    int32_t prep_base, prep_end; // the prep launch takes prep_order[prep_base .. prep_end)
+    int32_t scan_wgs;            // fused launch: workgroups of the depth-0 scan before the prep's
 };
 
-__global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
+// Chunk c, head h of the prep.  Four waves do the work; a workgroup of more waves (the fused
+// scan and prep launch has five) runs the extra ones through the same barriers, idle (act false).
+__device__ __forceinline__ void prep_body(const GdnArgs &a, int c, int h) {
     using T128 = Tile<kGD>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = blockIdx.x % a.H, c = blockIdx.x / a.H;
-    if (c >= a.n_chunks) return;
+    const bool act = wave < 4;
     const int4 cm = a.chunk_meta[c];
     const int r = cm.x, t0 = cm.y, n = cm.z;
     const int64_t tok0 = int64_t(r) * a.T + t0;
     const int stride = a.H * kGD * 2;
     const uint32_t lds0 = lds_base(smem);
     const int64_t hoff = (tok0 * a.H + h) * kGD * 2;
-    copy_tile<kGD>(reinterpret_cast<const char *>(a.qh) + hoff, n, stride, lds0 + PrepLds::Q_OFF, kGC, wave, 4, lane);
-    copy_tile<kGD>(reinterpret_cast<const char *>(a.kh) + hoff, n, stride, lds0 + PrepLds::K_OFF, kGC, wave, 4, lane);
-    copy_tile<kGD>(reinterpret_cast<const char *>(a.vh) + hoff, n, stride, lds0 + PrepLds::V_OFF, kGC, wave, 4, lane);
+    if (act) {
+        copy_tile<kGD>(reinterpret_cast<const char *>(a.qh) + hoff, n, stride, lds0 + PrepLds::Q_OFF, kGC, wave, 4, lane);
+        copy_tile<kGD>(reinterpret_cast<const char *>(a.kh) + hoff, n, stride, lds0 + PrepLds::K_OFF, kGC, wave, 4, lane);
+        copy_tile<kGD>(reinterpret_cast<const char *>(a.vh) + hoff, n, stride, lds0 + PrepLds::V_OFF, kGC, wave, 4, lane);
+    }
     float *Gs = reinterpret_cast<float *>(smem + PrepLds::G_OFF);
     float *Bs = reinterpret_cast<float *>(smem + PrepLds::GB_OFF);
     if (wave == 0) {
@@ -218,7 +225,9 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
     // transposed (rows s, columns t): A^T is then stored along lanes, and each lane holds four
     // consecutive s of one t of P (one 8-byte store).
     const char *Qt = smem + PrepLds::Q_OFF, *Kt = smem + PrepLds::K_OFF;
-    const int bt = wave >> 1, bs = wave & 1;
+    const int bt = (wave >> 1) & 1, bs = wave & 1;
+    float *As = reinterpret_cast<float *>(smem + PrepLds::A_OFF);
+    if (act) {
     floatx16 kkT = zero16(), qkT = zero16();
 #pragma unroll
     for (int ds = 0; ds < kGD / 16; ++ds) {
@@ -226,7 +235,6 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
         kkT = mfma(kb, T128::row_frag(Kt, 32 * bt, lane, ds), kkT);
         qkT = mfma(kb, T128::row_frag(Qt, 32 * bt, lane, ds), qkT);
     }
-    float *As = reinterpret_cast<float *>(smem + PrepLds::A_OFF);
     {
         const int t = 32 * bt + (lane & 31);
         __bf16 *Pout = a.P + ((int64_t(c) * a.H + h) * kGC + t) * kGC + 32 * bs + 4 * (lane >> 5);
@@ -243,6 +251,7 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
             *reinterpret_cast<bf16x4_t *>(Pout + 8 * i4) = p4;
         }
     }
+    }
     __syncthreads();
 
     // T = (I + A)^-1 in 16 x 16 blocks, all four waves.  As holds A^T in its strict upper
@@ -257,7 +266,7 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
     //  3. The blocks above the diagonal, still A^T, are cleared.
     {
         constexpr int NB16 = kGC / 16;
-        if (lane < 16) {
+        if (act && lane < 16) {
             const int b0 = 16 * wave;
             float x[16];
 #pragma unroll
@@ -320,7 +329,7 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
         });
         __syncthreads();
         // clear the blocks above the diagonal (i < j): 6 blocks x 64 float4
-        for (int e = tid; e < 6 * 64; e += 256) {
+        for (int e = tid; act && e < 6 * 64; e += 256) {
             const int blk = e >> 6, w = e & 63, rr = w >> 2, cc = 4 * (w & 3);
             const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
             const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
@@ -367,8 +376,9 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
     };
     const int64_t chh = int64_t(c) * a.H + h;
     floatx16 acc[2];
-    build_factor(false);
+    if (act) build_factor(false);
     __syncthreads();
+    if (act) {
     product(smem + PrepLds::V_OFF, acc);
     {
         // The scan's accumulator order: float4 (4 cb + tb) * 64 + 16 g + j holds rows 16 tb + 4 g
@@ -383,12 +393,13 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
                 Uo[(4 * cb + 2 * tb + (q >> 1)) * 64 + 16 * (2 * (q & 1) + hh) + (cl & 15)] =
                     make_float4(acc[tb][4 * q], acc[tb][4 * q + 1], acc[tb][4 * q + 2], acc[tb][4 * q + 3]);
     }
+    }
     __syncthreads();
-    build_factor(true);
+    if (act) build_factor(true);
     __syncthreads();
-    product(smem + PrepLds::K_OFF, acc);
+    if (act) product(smem + PrepLds::K_OFF, acc);
     __syncthreads();
-    {
+    if (act) {
         // -Y as bf16, row-major [t][128] in the Q tile's space, then out in 16-byte rows
         __bf16 *Ys = reinterpret_cast<__bf16 *>(smem + PrepLds::YS_OFF);
         const int colw = 32 * wave + (lane & 31);
@@ -399,12 +410,18 @@ __global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
                 Ys[(32 * tb + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4)) * kGD + colw] = static_cast<__bf16>(-acc[tb][i]);
     }
     __syncthreads();
-    {
+    if (act) {
         const bf16x8_t *src = reinterpret_cast<const bf16x8_t *>(smem + PrepLds::YS_OFF);
         bf16x8_t *dst = reinterpret_cast<bf16x8_t *>(a.Yn + chh * kGC * kGD);
 #pragma unroll
         for (int k4 = 0; k4 < kGC * kGD / 8 / 256; ++k4) dst[tid + 256 * k4] = src[tid + 256 * k4];
     }
+}
+
+__global__ __launch_bounds__(256) void gdn_prep(GdnArgs a) {
+    const int h = blockIdx.x % a.H, ord = a.prep_base + int(blockIdx.x / a.H);
+    if (ord >= a.prep_end) return;
+    prep_body(a, a.prep_order[ord], h);
 }
 
 // ------------------------------------------------------------------------------ gdn_scan
@@ -497,7 +514,7 @@ template <int NW>
 constexpr bool kMemWave = NW == 4;
 
 template <int NW>
-__global__ __launch_bounds__((NW + (kMemWave<NW> ? 1 : 0)) * 64) void gdn_scan(GdnArgs a, int32_t level) {
+__device__ __forceinline__ void scan_body(const GdnArgs &a, int32_t level, int bid) {
     using LD = ScanLds<NW>;
     constexpr bool MW = kMemWave<NW>;
     constexpr int NS = kGD / (16 * NW);                          // workgroups per head
@@ -505,7 +522,7 @@ __global__ __launch_bounds__((NW + (kMemWave<NW> ? 1 : 0)) * 64) void gdn_scan(G
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, j16 = lane & 15;
-    const int cs = blockIdx.x % NS, h = (blockIdx.x / NS) % a.H, k = blockIdx.x / (NS * a.H);
+    const int cs = bid % NS, h = (bid / NS) % a.H, k = bid / (NS * a.H);
     const int lb = a.level_ptr[level], le = a.level_ptr[level + 1];
     if (lb + k >= le) return;
     const int seg = a.level_segs[lb + k];
@@ -777,6 +794,25 @@ __global__ __launch_bounds__((NW + (kMemWave<NW> ? 1 : 0)) * 64) void gdn_scan(G
         for (int i = 0; i < 4; ++i) dst[(16 * kb + 4 * g4 + i) * kGD] = Hs[kb][i];
 }
 
+template <int NW>
+__global__ __launch_bounds__((NW + (kMemWave<NW> ? 1 : 0)) * 64) void gdn_scan(GdnArgs a, int32_t level) {
+    scan_body<NW>(a, level, int(blockIdx.x));
+}
+
+// The depth-0 scan (split shape: 4 compute waves and a memory wave) and, in the workgroups after
+// it, the prep of every deeper chunk: the root level's chunk chain runs on a few CUs, and the
+// rest of the chip preps the chunks the next levels need meanwhile.
+__global__ __launch_bounds__(5 * 64) void gdn_scan_prep(GdnArgs a) {
+    if (int(blockIdx.x) < a.scan_wgs) {
+        scan_body<4>(a, 0, int(blockIdx.x));
+        return;
+    }
+    const int k = int(blockIdx.x) - a.scan_wgs;
+    const int h = k % a.H, ord = a.prep_base + k / a.H;
+    if (ord >= a.prep_end) return;
+    prep_body(a, a.prep_order[ord], h);
+}
+
 }  // namespace
 
 hipError_t launch_gdn(const GdnShape &sh, const GdnLayout &L, char *gws, const void *xq, const void *xk,
@@ -807,19 +843,55 @@ hipError_t launch_gdn(const GdnShape &sh, const GdnLayout &L, char *gws, const v
                                             reinterpret_cast<__bf16 *>(gws + L.qh), reinterpret_cast<__bf16 *>(gws + L.kh),
                                             reinterpret_cast<__bf16 *>(gws + L.vh));
     if (L.n_chunks > 0) {
+        a.prep_order = reinterpret_cast<const int32_t *>(gws + L.prep_order);
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_prep),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::SIZE);
         if (e != hipSuccess) return e;
-        gdn_prep<<<L.n_chunks * sh.H, 256, PrepLds::SIZE, s>>>(a);
-        // Narrow levels (few segments): two workgroups of 4 compute waves and a memory wave per
-        // (segment, head); the others: one workgroup of 8 waves per (segment, head).
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan<4>), hipFuncAttributeMaxDynamicSharedMemorySize,
                                 ScanLds<4>::SIZE);
         if (e != hipSuccess) return e;
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan<8>), hipFuncAttributeMaxDynamicSharedMemorySize,
                                 ScanLds<8>::SIZE);
         if (e != hipSuccess) return e;
-        for (int32_t lev = 0; lev < L.n_levels; ++lev) {
+        // Narrow levels (few segments): two workgroups of 4 compute waves and a memory wave per
+        // (segment, head); the others: one workgroup of 8 waves per (segment, head).  When depth
+        // 0 is narrow and deeper levels exist, only its chunks are prepped first; its scan then
+        // shares one launch with the prep of as many other chunks as its chain leaves time for
+        // (that launch holds one workgroup per CU: the scan's LDS), and the rest are prepped
+        // after it at full occupancy.  A chunk of the chain takes ~2.3 us, a prep workgroup
+        // alone on a CU ~15 us, so the chain covers 3/20 of its length in prep rounds.
+        int dev = 0, n_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+            n_cu = 256;
+        const bool narrow0 = (L.narrow_levels & 1u) != 0 && L.narrow_segs > 0;
+        const int64_t scan_wgs = int64_t(L.lead_segs) * sh.H * 2;   // the depth-0 scan's workgroups
+        int64_t shadow = 0;     // chunks prepped beside the depth-0 scan
+        if (narrow0 && L.n_levels >= 2 && L.lead_segs > 0 && L.lead_chunks < L.n_chunks && n_cu > scan_wgs) {
+            const int64_t rounds = int64_t(L.lead_chain) * 3 / 20;
+            shadow = std::min<int64_t>(L.n_chunks - L.lead_chunks, (int64_t(n_cu - scan_wgs) * rounds) / sh.H);
+        }
+        a.prep_base = 0;
+        a.prep_end = shadow > 0 ? L.lead_chunks : L.n_chunks;
+        gdn_prep<<<a.prep_end * sh.H, 256, PrepLds::SIZE, s>>>(a);
+        int32_t lev0 = 0;
+        if (shadow > 0) {
+            constexpr int kFusedLds = ScanLds<4>::SIZE > PrepLds::SIZE ? ScanLds<4>::SIZE : PrepLds::SIZE;
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(gdn_scan_prep),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds);
+            if (e != hipSuccess) return e;
+            a.scan_wgs = int32_t(scan_wgs);
+            a.prep_base = L.lead_chunks;
+            a.prep_end = L.lead_chunks + int32_t(shadow);
+            gdn_scan_prep<<<unsigned(scan_wgs + shadow * sh.H), 5 * 64, kFusedLds, s>>>(a);
+            if (a.prep_end < L.n_chunks) {
+                a.prep_base = a.prep_end;
+                a.prep_end = L.n_chunks;
+                gdn_prep<<<(a.prep_end - a.prep_base) * sh.H, 256, PrepLds::SIZE, s>>>(a);
+            }
+            lev0 = 1;
+        }
+        for (int32_t lev = lev0; lev < L.n_levels; ++lev) {
             if (lev < 32 && ((L.narrow_levels >> lev) & 1u) != 0) {
                 if (L.narrow_segs > 0)
                     gdn_scan<4><<<unsigned(L.narrow_segs * sh.H * 2), 5 * 64, ScanLds<4>::SIZE, s>>>(a, lev);

@@ -133,6 +133,7 @@ struct GdnLayout {
     size_t seg_meta = 0;     // int4[n_segs]: (row, first chunk, chunks, parent segment or -1)
     size_t level_ptr = 0;    // int32[n_levels + 1] (room for n_segs + 1): segments per depth, CSR
     size_t level_segs = 0;   // int32[n_segs]: segments by depth
+    size_t prep_order = 0;   // int32[n_chunks]: chunks of depth-0 segments first, then the rest
     size_t qh = 0, kh = 0, vh = 0;   // bf16[R*T*H*128] each: conv + norm outputs
     size_t U = 0;            // f32[n_chunks*H*64*128], in the scan's accumulator order
     size_t Yn = 0;           // bf16[n_chunks*H*64*128]
@@ -143,6 +144,9 @@ struct GdnLayout {
     int32_t n_chunks = 0, n_segs = 0, n_levels = 0, max_level_segs = 0;
     int32_t narrow_segs = 0;      // levels of bit l in narrow_levels: at most this many segments
     uint32_t narrow_levels = 0;
+    int32_t lead_chunks = 0;      // chunks of depth-0 segments (the head of prep_order)
+    int32_t lead_chain = 0;       // the most chunks of one depth-0 segment
+    int32_t lead_segs = 0;        // depth-0 segments
 };
 inline GdnLayout make_gdn_layout(int32_t R, int32_t T, int32_t H, int32_t n_chunks, int32_t n_segs) {
     GdnLayout g;
@@ -154,6 +158,7 @@ inline GdnLayout make_gdn_layout(int32_t R, int32_t T, int32_t H, int32_t n_chun
     g.seg_meta = take(size_t(n_segs) * 16);
     g.level_ptr = take((size_t(n_segs) + 1) * 4);
     g.level_segs = take(size_t(n_segs) * 4);
+    g.prep_order = take(size_t(n_chunks) * 4);
     g.qh = take(tok * H * 128 * 2);
     g.kh = take(tok * H * 128 * 2);
     g.vh = take(tok * H * 128 * 2);
