@@ -13,7 +13,8 @@
 // Launches (all on the caller's stream):
 //   * gdn_conv: one workgroup per (16 tokens, tensor q / k / v); the conv follows the
 //     token-parent chain, so a child's first tokens convolve with its parent's last ones (the
-//     context carried across the join).
+//     context carried across the join), from a window of the three rows before each token
+//     that is reloaded only where the chain leaves the previous row.
 //   * gdn_prep: one workgroup per (chunk, head), chunk-parallel.  Chunks are 64 tokens of one
 //     segment, counted from the segment's start (the last one ragged), so every segment ends
 //     on a chunk boundary and its exact final state is available to its children: no tail is
@@ -54,14 +55,41 @@ constexpr float kGLog2e = 1.4426950408889634f;
 //
 // One workgroup (256 threads) per (block of kConvTok tokens, tensor q / k / v); a thread takes
 // 8 consecutive channels and keeps their conv weights in registers; 16 threads cover a head
-// (the L2 norm is a 16-lane sum).  The block's input rows, with the 3 rows before it, are
-// loaded once into a register window before any output is stored (stores and loads share one
-// counter, so a load issued after a store would also wait for the store); a tap reads the
-// window when the token-parent chain runs through the previous rows, which it does everywhere
-// except at the first tokens after a join, where the tap row is loaded on its own.  The parent
-// chains of the block are loaded once, all tokens in parallel (lane k of every wave walks
-// token k's chain).
+// (the L2 norm is a 16-lane sum, on DPP row moves, so no LDS round trip).  The block's rows are
+// loaded at the start, before any output is stored (stores and loads share one counter, so a
+// load issued after a store would also wait for the store).  The taps come from a window of
+// the three rows before the current token along its parent chain, in fp32 and zero past a
+// root: after a token the window shifts by one (its row enters), which stays right as long as
+// the next token's parent is this token; at a join or a root start (the parent is not the
+// previous row) the window is reloaded from the chain.  Each row is converted once.  The
+// parent chains of the block are loaded once, all tokens in parallel (lane k of every wave
+// walks token k's chain).
 constexpr int kConvTok = 16;
+
+// Sum over each aligned group of 16 lanes, the result in all 16 (the same value in each: every
+// step adds two operands that commute).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+    v += dpp_row<0xB1>(v);    // quad_perm [1, 0, 3, 2]: lane ^ 1
+    v += dpp_row<0x4E>(v);    // quad_perm [2, 3, 0, 1]: lane ^ 2
+    v += dpp_row<0x141>(v);   // row_half_mirror: the other quad of the 8-lane half
+    v += dpp_row<0x140>(v);   // row_mirror: the other half of the 16-lane row
+    return v;
+}
+
+__device__ __forceinline__ void conv_row(const __bf16 *x, int r, int C, int c8, float (&f)[8]) {
+    if (r < 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = 0.f;
+    } else {
+        const bf16x8_t v = *reinterpret_cast<const bf16x8_t *>(x + int64_t(r) * C + c8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = float(v[e]);
+    }
+}
 
 __global__ __launch_bounds__(256) void gdn_conv(int32_t n_tok, int32_t H, const int32_t *__restrict__ pi,
                                                 const __bf16 *__restrict__ xq, const __bf16 *__restrict__ xk,
@@ -91,46 +119,56 @@ __global__ __launch_bounds__(256) void gdn_conv(int32_t n_tok, int32_t H, const 
             const float4 w4 = *reinterpret_cast<const float4 *>(w + ((int64_t(tsr) * C + c8 + e) * kGW));
             wr[e][0] = w4.x; wr[e][1] = w4.y; wr[e][2] = w4.z; wr[e][3] = w4.w;
         }
-        // win[i] = row tok_begin - (kGW - 1) + i (rows outside [0, n_tok) clamped; never used)
-        bf16x8_t win[kConvTok + kGW - 1];
+        // the block's rows (past n_tok clamped: pads, never stored)
+        bf16x8_t xr[kConvTok];
 #pragma unroll
-        for (int i = 0; i < kConvTok + kGW - 1; ++i) {
-            const int rr = min(max(tok_begin - (kGW - 1) + i, 0), n_tok - 1);
-            win[i] = *reinterpret_cast<const bf16x8_t *>(x + int64_t(rr) * C + c8);
-        }
+        for (int k = 0; k < kConvTok; ++k)
+            xr[k] = *reinterpret_cast<const bf16x8_t *>(x + int64_t(min(tok_begin + k, n_tok - 1)) * C + c8);
+        // window: rows pi^1, pi^2, pi^3 of the current token
+        float r1[8], r2[8], r3[8];
+        conv_row(x, __builtin_amdgcn_readfirstlane(c1), C, c8, r1);
+        conv_row(x, __builtin_amdgcn_readfirstlane(c2), C, c8, r2);
+        conv_row(x, __builtin_amdgcn_readfirstlane(c3), C, c8, r3);
 #pragma unroll
         for (int k = 0; k < kConvTok; ++k) {
-            if (__builtin_amdgcn_readlane(c0, k) < -1) continue;     // pad: never read downstream
             const int tok = tok_begin + k;
-            const int ch[kGW] = {tok, __builtin_amdgcn_readlane(c1, k), __builtin_amdgcn_readlane(c2, k),
-                                 __builtin_amdgcn_readlane(c3, k)};
-            float y[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = 0.f;
-#pragma unroll
-            for (int j = 0; j < kGW; ++j) {
-                if (ch[j] < 0) break;
-                bf16x8_t xv8;
-                if (ch[j] == tok - j) xv8 = win[k + kGW - 1 - j];
-                else xv8 = *reinterpret_cast<const bf16x8_t *>(x + int64_t(ch[j]) * C + c8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = fmaf(wr[e][kGW - 1 - j], float(xv8[e]), y[e]);
+            if (k > 0) {
+                const int p = __builtin_amdgcn_readlane(c1, k);
+                if (p != tok - 1) {                        // a join or a root start
+                    conv_row(x, p, C, c8, r1);
+                    conv_row(x, __builtin_amdgcn_readlane(c2, k), C, c8, r2);
+                    conv_row(x, __builtin_amdgcn_readlane(c3, k), C, c8, r3);
+                }
             }
+            float xc[8], y[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = y[e] * __builtin_amdgcn_rcpf(1.f + __expf(-y[e]));
+            for (int e = 0; e < 8; ++e) {
+                xc[e] = float(xr[k][e]);
+                y[e] = fmaf(wr[e][3], xc[e], 0.f);
+                y[e] = fmaf(wr[e][2], r1[e], y[e]);
+                y[e] = fmaf(wr[e][1], r2[e], y[e]);
+                y[e] = fmaf(wr[e][0], r3[e], y[e]);
+                y[e] = y[e] * __builtin_amdgcn_rcpf(1.f + __expf(-y[e]));
+            }
             float scale = 1.f;
             if (tsr < 2) {
                 float ss = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
-#pragma unroll
-                for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 16);
-                scale = rsqrtf(ss + eps) * oscale;
+                scale = __builtin_amdgcn_rsqf(sum16(ss) + eps) * oscale;
             }
-            bf16x8_t o8;
+            if (__builtin_amdgcn_readlane(c0, k) >= -1) {  // pads are never written
+                bf16x8_t o8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o8[e] = static_cast<__bf16>(y[e] * scale);
-            *reinterpret_cast<bf16x8_t *>(out + int64_t(tok) * C + c8) = o8;
+                for (int e = 0; e < 8; ++e) o8[e] = static_cast<__bf16>(y[e] * scale);
+                *reinterpret_cast<bf16x8_t *>(out + int64_t(tok) * C + c8) = o8;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                r3[e] = r2[e];
+                r2[e] = r1[e];
+                r1[e] = xc[e];
+            }
         }
     }
 }
