@@ -240,21 +240,21 @@ int tree_attn_fwd_noalloc(const tree_attn_desc *d, const void *q, const void *k,
  *
  * tree_attn_bwd_workspace_size: bytes of the caller-allocated backward workspace `bws`
  *   (256-byte aligned): per-token row terms D and log2-scaled LSE ([R, Hq, T] fp32 each),
- *   the per-pair q-tile lists and unit list below, and a pool of at most 1024 fp32 partial slots of dK and
- *   dV per KV head (each 2 x 128 x head_dim x 4 bytes; 128 MiB per KV head at head_dim 128,
- *   whatever the batch size and row length): a
- *   pair seen by many q-tiles is split over up to 4 workgroups along its list, so that the
- *   long pairs of a shared prefix do not serialize, as long as slots remain (longest pairs
- *   first); the partials are added in a fixed order (results do not depend on timing).
- * tree_attn_bwd_plan: from the forward plan in `ws`, build into `bws`, for every pair of
- *   k-tiles (2p, 2p+1) of a row, the list of q-tiles that see either of them (ascending, entry =
- *   q_tile * 16 + class(2p) * 4 + class(2p+1), classes as in tree_tile_view, a missing k-tile
- *   2p+1 counting as SKIP), the order of the pair work (longest list first, equal lengths in
- *   pair order, so the same on every run), the partial slots of the split pairs and the list
- *   of (pair, slice) units the dK/dV pass launches one workgroup for.  Once per batch, like
- *   tree_attn_plan; asynchronous.
+ *   the per-group q-tile lists and unit list below, and a pool of at most 512 fp32 partial
+ *   slots of dK and dV per KV head (each 2 x 256 x head_dim x 4 bytes; 128 MiB per KV head at
+ *   head_dim 128, whatever the batch size and row length): a k-tile group seen by many
+ *   q-tiles is split over up to 4 workgroups along its list, so that the long groups of a
+ *   shared prefix do not serialize, as long as slots remain (longest groups first); the
+ *   partials are added in a fixed order (results do not depend on timing).
+ * tree_attn_bwd_plan: from the forward plan in `ws`, build into `bws`, for every group of four
+ *   consecutive k-tiles (4p .. 4p+3) of a row, the list of q-tiles that see any of them
+ *   (ascending, entry = q_tile * 256 + sum_i class(4p+i) << 2(3-i), classes as in
+ *   tree_tile_view, k-tiles past the row's last counting as SKIP), the order of the group work
+ *   (longest list first, equal lengths in group order, so the same on every run), the partial
+ *   slots of the split groups and the list of (group, slice) units the dK/dV pass launches
+ *   one workgroup for.  Once per batch, like tree_attn_plan; asynchronous.
  * tree_attn_bwd_tiles: device pointers (into bws) of those lists, for tests:
- *   kp_ptr[R * ceil(n_ktiles / 2) + 1] CSR over (row, pair), kp_list the entries.
+ *   kp_ptr[R * ceil(n_ktiles / 4) + 1] CSR over (row, group), kp_list the entries.
  * tree_attn_bwd: q, k, v as given to tree_attn_fwd; o and lse as it returned them; dout in
  *   q's layout; writes dq (q's layout), dk and dv (k's layout), bf16.  Overwrites the row
  *   terms in bws (the lists are kept).  Asynchronous.  Errors: TREE_E_INVAL,

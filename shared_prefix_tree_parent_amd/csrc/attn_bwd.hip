@@ -11,17 +11,18 @@
 //   * dq_kernel: one workgroup per forward item (row, q-tile, KV head, chunk of its query
 //     heads), 8 waves of 32 query rows, walking the q-tile's k-tile list with K/V tiles
 //     staged in LDS (direct-to-LDS copies, two tiles ahead);
-//   * dkdv_kernel: one workgroup per (row, pair of k-tiles, KV head, query slice), 4 waves of
-//     32 keys whose K and V fragments stay in registers, walking the slice's run of the pair's
-//     list of q-tiles (the transposed tile lists) and every query head of the group in blocks
-//     of 32 queries; each block's Q, dO, LSE and D are staged in LDS once for all four waves,
-//     three blocks ahead.  A wave whose k-tile does not see a block's q-tile skips it.  A pair
-//     seen by many q-tiles (a shared prefix's keys are seen by every query after them) is split
-//     into up to kBwdSlices slices so that its work spreads over several CUs, as long as the
-//     bounded pool of partial slots lasts (the plan hands the slots to the longest pairs first).
-//     The grid follows the plan's list of (pair, slice) units, so no workgroup is launched for
-//     a slice that does not exist; only a short surplus at the end of the grid exits at once;
-//   * dkdv_reduce (only where a pair was split): adds the slices' fp32 partials in slice order.
+//   * dkdv_kernel: one workgroup per (row, group of kKvGroup = 4 k-tiles, KV head, query
+//     slice), 8 waves of 32 keys (two per SIMD) whose K fragments stay in registers and whose
+//     V rows stay in LDS, walking the slice's run of the group's list of q-tiles (the
+//     transposed tile lists) and every query head of the group in blocks of 32 queries; each
+//     block's Q, dO, LSE and D are staged in LDS once for all eight waves, three blocks ahead.
+//     A wave whose k-tile does not see a block's q-tile skips it.  A group seen by many q-tiles
+//     (a shared prefix's keys are seen by every query after them) is split into up to
+//     kBwdSlices slices so that its work spreads over several CUs, as long as the bounded pool
+//     of partial slots lasts (the plan hands the slots to the longest groups first).  The grid
+//     follows the plan's list of (group, slice) units, so no workgroup is launched for a slice
+//     that does not exist; only a short surplus at the end of the grid exits at once;
+//   * dkdv_reduce (only where a group was split): adds the slices' fp32 partials in slice order.
 // Every result is written exactly once (no atomics); gradients of pads are zero.
 //
 // Orientation (32x32x16 bf16 MFMA, accumulator element i of lane l at row 8(i/4) + 4(l/32) +
@@ -33,6 +34,7 @@
 // The "transposed" operands (K^T, dO^T, Q^T) are LDS transpose reads of row-major tiles.
 // The softmax takes the LSE in log2 units (one FMA and one exp per element); the mask of a
 // PARTIAL tile is applied in its own uniform branch, so FULL tiles do no mask arithmetic.
+#include <algorithm>
 #include <type_traits>
 
 #include "internal.h"
@@ -49,6 +51,7 @@ using tile::shortx4;
 using tile::zero16;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLdsBytes = 160 * 1024;     // LDS of one CU (one workgroup per CU at most)
 
 struct BwdArgs {
     const void *q, *k, *v, *o, *dout;
@@ -64,6 +67,7 @@ struct BwdArgs {
     const int32_t *n_units;        // units in use; workgroups past them exit
     const int32_t *kend, *work, *n_real, *status;
     int32_t T, Hq, Hkv, G, HCH, nQ, nK, nP, L, BQ;
+    int32_t lcap;  // q-tile list entries the dK/dV kernel stages in LDS at a time
     float c;       // scale * log2(e)
     float scale;
 };
@@ -321,7 +325,7 @@ void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------- dkdv_kernel
-constexpr int kKvWaves = 4;               // 32 keys each: a pair of 64-key tiles per workgroup
+constexpr int kKvWaves = 2 * kKvGroup;    // 32 keys each: kKvGroup 64-key tiles per workgroup
 constexpr int kQBlk = 32;                 // queries per block (one LDS stage)
 
 template <int D>
@@ -331,12 +335,17 @@ struct KvLds {
     static constexpr int Q_OFF = 0, DO_OFF = TILE, LSE_OFF = 2 * TILE, DL_OFF = 2 * TILE + kQBlk * 4;
     static constexpr int NS = 4;                                // stages, one block each
     static constexpr int AHEAD = NS - 1;                        // blocks copied ahead of the one in use
-    // load instructions per block, all issued by the memory wave: Q and dO (1 KB each), LSE2, D
-    static constexpr int PERB = 2 * (TILE / 1024) + 2;
-    static_assert((AHEAD - 1) * PERB < 64, "vmcnt field");
-    // V of the pair's 128 keys (B operand of dP = dO V^T, read like the Q / dO rows), then the
-    // slice's q-tile list
-    static constexpr int V_OFF = NS * BLK, VTILE = 2 * kBK * D * 2, LIST_OFF = V_OFF + VTILE;
+    // Copies are issued by one wave per SIMD (waves 0-3): a wave that issues direct-to-LDS
+    // loads stalls while the CU's memory pipeline is full, and the other wave of its SIMD keeps
+    // issuing meanwhile.  Per block each copying wave issues PERW 1 KB loads of Q and dO; the
+    // last one also the LSE2 and D rows.
+    static constexpr int CW = 4;
+    static constexpr int PERW = 2 * (TILE / 1024) / CW;
+    static_assert((2 * (TILE / 1024)) % CW == 0, "copying waves must split a block evenly");
+    static_assert(AHEAD == 3 && 2 * (PERW + 2) < 64, "vmcnt field");
+    // V of the group's 64 kKvGroup keys (B operand of dP = dO V^T, read like the Q / dO rows),
+    // then the slice's q-tile list
+    static constexpr int V_OFF = NS * BLK, VTILE = kKvWaves * 32 * D * 2, LIST_OFF = V_OFF + VTILE;
 };
 
 // Softmax of one block for a wave's 32 keys: P and dS as bf16 operands (accumulator register
@@ -451,11 +460,9 @@ struct BlockCursor {
     }
 };
 
-// Waves 0-3 compute (32 keys each); wave 4, the memory wave, issues every copy of the Q / dO
-// blocks into LDS: a wave that issues a direct-to-LDS copy waits while the CU's memory
-// pipeline is full, and that wait no longer holds a compute wave's MFMAs.
+// kKvWaves waves of 32 keys each (two per SIMD); waves 0-3 also issue the copies.
 template <int D>
-__global__ __launch_bounds__((kKvWaves + 1) * 64) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     using TL = Tile<D>;
     using LD = KvLds<D>;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -475,19 +482,19 @@ __global__ __launch_bounds__((kKvWaves + 1) * 64) void dkdv_kernel(BwdArgs a) {
     const int r = pitem / a.nP, pr = pitem % a.nP;
     const int T = a.T;
     const int n_real = a.n_real[r];
-    const bool memw = wave == kKvWaves;                  // the memory wave
-    const int half = (wave >> 1) & 1;                    // k-tile 2 pr + half
-    const int key = (2 * pr + half) * kBK + 32 * (wave & 1) + l32;   // this lane's key
-    const bool kin = key < T;                            // false only past an odd k-tile count
+    const bool cw = wave < LD::CW;                       // a copying wave
+    const int key0 = kKvGroup * pr * kBK;                // the group's first key
+    const int key = key0 + 32 * wave + l32;              // this lane's key (k-tile wave / 2)
+    const bool kin = key < T;                            // false only past the row's last k-tile
     const bool kreal = key < n_real;
     const int kend_k = kin ? a.kend[int64_t(r) * T + key] : key;      // == key at pads: never visible
-    const int cls_shift = half ? 0 : 2;
+    const int cls_shift = 2 * (kKvGroup - 1 - (wave >> 1));
 
     // K fragments of the wave's 32 keys (B operand of S = Q K^T): lane holds columns 16 ds +
     // 8h .. +7 of its key; zero at pad keys.  (V is read from LDS, rows past the last real key
     // zero.)
     bf16x8_t kf[TL::NDS];
-    if (!memw) {
+    {
         const int64_t off = ((int64_t(r) * T + (kin ? key : 0)) * a.Hkv + g) * D;
         const bf16x8_t *pk = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.k) + off);
 #pragma unroll
@@ -507,71 +514,79 @@ __global__ __launch_bounds__((kKvWaves + 1) * 64) void dkdv_kernel(BwdArgs a) {
         dv[db] = zero16();
     }
 
-    // Blocks: (entry of the pair's q-tile list, query head, 32-query chunk), one LDS stage each,
-    // copied AHEAD blocks ahead of the one in use.
+    // Blocks: (entry of the group's q-tile list, query head, 32-query chunk), one LDS stage
+    // each, copied AHEAD blocks ahead of the one in use.  The slice's entries are staged in LDS
+    // (no scalar load inside the block loop), lcap at a time: a longer slice (only on rows of
+    // more than lcap q-tiles) runs as several passes, the copies drained between them.
     const int32_t l_begin = list_begin + NL_pair * slice / n_slices;
     const int NL = list_begin + NL_pair * (slice + 1) / n_slices - l_begin;
-    // the slice's q-tile entries, staged in LDS once (no scalar load inside the block loop)
     int32_t *lst = reinterpret_cast<int32_t *>(smem + LD::LIST_OFF);
-    for (int e = tid; e < NL; e += (kKvWaves + 1) * 64) lst[e] = a.kp_list[l_begin + e];
-    __syncthreads();
     const int CH = a.BQ / kQBlk;
-    const int NB = NL * a.G * CH;
     const int q_stride = a.Hq * D * 2;
     const uint32_t lds0 = lds_base(smem);
-    BlockCursor ci, cc;            // next block to copy / to compute
-    auto issue = [&](int n) __attribute__((always_inline)) {
-        const int ent = __builtin_amdgcn_readfirstlane(lst[ci.e]);
-        const int q0 = (ent >> 4) * a.BQ + ci.ch * kQBlk;
-        const int head = g * a.G + ci.hd;
-        ci.next(a.G, CH);
-        const uint32_t bl = lds0 + (n % LD::NS) * LD::BLK;
-        const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - q0, 0), kQBlk));
-        const int64_t roff = ((int64_t(r) * T + q0) * a.Hq + head) * D * 2;
-        copy_tile<D>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, bl + LD::Q_OFF, kQBlk, 0, 1, lane);
-        copy_tile<D>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride, bl + LD::DO_OFF, kQBlk, 0, 1, lane);
-        if (lane < kQBlk) {
-            const int64_t loff = (int64_t(r) * a.Hq + head) * T + q0;
-            buf_to_lds4(buf_rsrc(a.lse2 + loff, uint32_t(n_valid) * 4), bl + LD::LSE_OFF, lane * 4);
-            buf_to_lds4(buf_rsrc(a.delta + loff, uint32_t(n_valid) * 4), bl + LD::DL_OFF, lane * 4);
-        }
-    };
-
-    if (memw) {
-        // The memory wave: block n has landed once only the newer blocks' copies (at most
-        // AHEAD - 1 of them) may be in flight (it issues loads only, so they land in order);
-        // the barrier extends that to every wave and also means every wave is done with block
-        // n - 1, whose stage block n + AHEAD takes.
-        {
-            // the pair's V rows first: they land before block 0's copies
-            const int key0 = 2 * pr * kBK;
-            const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - key0, 0), 2 * kBK));
-            const int64_t voff = ((int64_t(r) * T + key0) * a.Hkv + g) * D * 2;
-            copy_tile<D>(reinterpret_cast<const char *>(a.v) + voff, n_valid, a.Hkv * D * 2, lds0 + LD::V_OFF, 2 * kBK,
-                         0, 1, lane);
-        }
+    // The group's V rows, before block 0's copies (so they land first).
+    if (cw && NL > 0) {
+        const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - key0, 0), kKvWaves * 32));
+        const int64_t voff = ((int64_t(r) * T + key0) * a.Hkv + g) * D * 2;
+        copy_tile<D>(reinterpret_cast<const char *>(a.v) + voff, n_valid, a.Hkv * D * 2, lds0 + LD::V_OFF,
+                     kKvWaves * 32, wave, LD::CW, lane);
+    }
+    for (int c0 = 0; c0 < NL; c0 += a.lcap) {
+        const int nl = min(a.lcap, NL - c0);
+        if (c0 > 0) __syncthreads();   // every wave is done with the previous pass's list and stages
+        for (int e = tid; e < nl; e += kKvWaves * 64) lst[e] = a.kp_list[l_begin + c0 + e];
+        __syncthreads();
+        const int NB = nl * a.G * CH;
+        BlockCursor ci, cc;            // next block to copy / to compute
+        auto issue = [&](int n) __attribute__((always_inline)) {
+            if (!cw) return;
+            const int ent = __builtin_amdgcn_readfirstlane(lst[ci.e]);
+            const int q0 = (ent >> 8) * a.BQ + ci.ch * kQBlk;
+            const int head = g * a.G + ci.hd;
+            ci.next(a.G, CH);
+            const uint32_t bl = lds0 + (n % LD::NS) * LD::BLK;
+            const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - q0, 0), kQBlk));
+            const int64_t roff = ((int64_t(r) * T + q0) * a.Hq + head) * D * 2;
+            copy_tile<D>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, bl + LD::Q_OFF, kQBlk, wave,
+                         LD::CW, lane);
+            copy_tile<D>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride, bl + LD::DO_OFF, kQBlk,
+                         wave, LD::CW, lane);
+            if (wave == LD::CW - 1 && lane < kQBlk) {
+                const int64_t loff = (int64_t(r) * a.Hq + head) * T + q0;
+                buf_to_lds4(buf_rsrc(a.lse2 + loff, uint32_t(n_valid) * 4), bl + LD::LSE_OFF, lane * 4);
+                buf_to_lds4(buf_rsrc(a.delta + loff, uint32_t(n_valid) * 4), bl + LD::DL_OFF, lane * 4);
+            }
+        };
 #pragma unroll
         for (int n = 0; n < LD::AHEAD; ++n)
             if (n < NB) issue(n);
         for (int n = 0; n < NB; ++n) {
-            const int newer = min(LD::AHEAD - 1, NB - 1 - n);
-            if (newer >= 2) wait_loads_but<2 * LD::PERB>();
-            else if (newer == 1) wait_loads_but<LD::PERB>();
-            else wait_loads();
+            // Block n has landed once each copying wave has only the newer blocks' copies (at
+            // most AHEAD - 1 of them) in flight (loads only: they land in order); the barrier
+            // extends that to every wave and also means every wave is done with block n - 1,
+            // whose stage block n + AHEAD takes.
+            if (cw) {
+                const int newer = min(LD::AHEAD - 1, NB - 1 - n);
+                if (wave == LD::CW - 1) {
+                    if (newer >= 2) wait_loads_but<2 * (LD::PERW + 2)>();
+                    else if (newer == 1) wait_loads_but<LD::PERW + 2>();
+                    else wait_loads();
+                } else {
+                    if (newer >= 2) wait_loads_but<2 * LD::PERW>();
+                    else if (newer == 1) wait_loads_but<LD::PERW>();
+                    else wait_loads();
+                }
+            }
             block_barrier();
             if (n + LD::AHEAD < NB) issue(n + LD::AHEAD);
+            const int ent = __builtin_amdgcn_readfirstlane(lst[cc.e]);
+            const int q0 = (ent >> 8) * a.BQ + cc.ch * kQBlk;
+            cc.next(a.G, CH);
+            const int cls = (ent >> cls_shift) & 3;
+            if (cls != kTileSkip)
+                kv_block<D>(smem + (n % LD::NS) * LD::BLK, lo, kf, smem + LD::V_OFF + 32 * wave * TL::ROWB, a.c, h,
+                            key, kend_k, q0, cls == kTilePartial, dk, dv);
         }
-        return;
-    }
-    for (int n = 0; n < NB; ++n) {
-        block_barrier();   // block n is in LDS (the memory wave waited for it)
-        const int ent = __builtin_amdgcn_readfirstlane(lst[cc.e]);
-        const int q0 = (ent >> 4) * a.BQ + cc.ch * kQBlk;
-        cc.next(a.G, CH);
-        const int cls = (ent >> cls_shift) & 3;
-        if (cls != kTileSkip)
-            kv_block<D>(smem + (n % LD::NS) * LD::BLK, lo, kf, smem + LD::V_OFF + 32 * wave * TL::ROWB, a.c, h, key,
-                        kend_k, q0, cls == kTilePartial, dk, dv);
     }
 
     if (n_slices > 1) {
@@ -638,7 +653,7 @@ __global__ __launch_bounds__(256) void dkdv_reduce(BwdArgs a) {
             sk.x += k4.x; sk.y += k4.y; sk.z += k4.z; sk.w += k4.w;
             sv.x += v4.x; sv.y += v4.y; sv.z += v4.z; sv.w += v4.w;
         }
-        const int key = (2 * pr + (wave >> 1)) * kBK + 32 * (wave & 1) + (lane & 31);
+        const int key = kKvGroup * pr * kBK + 32 * wave + (lane & 31);
         if (key >= T) continue;
         const int d0 = 32 * db + 8 * i4 + 4 * (lane >> 5);
         const int64_t off = ((int64_t(r) * T + key) * a.Hkv + g) * D + d0;
@@ -662,20 +677,20 @@ hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, int n
     }
     if (n_items_q > 0) {
         const int smem = DqLds<D>::LIST_OFF + 4 * ((a.nK + 3) & ~3);
-        if (smem > 160 * 1024) return hipErrorInvalidValue;
+        if (smem > kLdsBytes) return hipErrorInvalidValue;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(dq_kernel<D>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return e;
         dq_kernel<D><<<n_items_q, kDqWaves * 64, smem, s>>>(a);
     }
     if (n_items_k > 0) {
-        // stages, the pair's V rows, then one pair's list (at most nQ entries)
-        const int smem = KvLds<D>::LIST_OFF + 4 * ((a.nQ + 3) & ~3);
-        if (smem > 160 * 1024) return hipErrorInvalidValue;
+        // stages, the group's V rows, then the list entries of one pass
+        const int smem = KvLds<D>::LIST_OFF + 4 * a.lcap;
+        if (a.lcap < 1 || smem > kLdsBytes) return hipErrorInvalidValue;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(dkdv_kernel<D>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return e;
-        dkdv_kernel<D><<<n_units_k, (kKvWaves + 1) * 64, smem, s>>>(a);
+        dkdv_kernel<D><<<n_units_k, kKvWaves * 64, smem, s>>>(a);
         dkdv_reduce<D><<<n_items_k, 256, 0, s>>>(a);
     }
     return hipGetLastError();
@@ -709,6 +724,11 @@ hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b,
     a.T = sh.T; a.Hq = sh.Hq; a.Hkv = sh.Hkv; a.G = sh.G; a.HCH = sh.HCH;
     a.nQ = w.nQ; a.nK = w.nK; a.nP = b.nP; a.BQ = sh.BQ;
     a.L = sh.Hkv * (sh.G / sh.HCH);
+    {
+        // as many list entries as fit beside the stages and V rows (a multiple of 4), at most nQ
+        const int room = (kLdsBytes - (sh.D == 128 ? KvLds<128>::LIST_OFF : KvLds<64>::LIST_OFF)) / 4 & ~3;
+        a.lcap = std::min(room, (w.nQ + 3) & ~3);
+    }
     a.scale = sh.scale;
     a.c = sh.scale * kLog2e;
     const int64_t n_q = int64_t(sh.R) * w.nQ * a.L;

@@ -217,7 +217,12 @@ extern "C" int tree_attn_bwd_plan(const tree_attn_desc *d, const void *ws, void 
     const int rc = bwd_check(d, &w, &b);
     if (rc != TREE_OK) return rc;
     if (ws == nullptr || bws == nullptr || (reinterpret_cast<uintptr_t>(bws) & 255) != 0) return TREE_E_INVAL;
-    const hipError_t e = launch_bwd_plan(w, b, static_cast<const char *>(ws), static_cast<char *>(bws),
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+        n_cu = 256;
+    const int per = bwd_slice_entries(int64_t(w.R) * b.nP, d->h_kv, n_cu);
+    const hipError_t e = launch_bwd_plan(w, b, per, static_cast<const char *>(ws), static_cast<char *>(bws),
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TREE_OK : TREE_E_HIP;
 }

@@ -289,16 +289,26 @@ __global__ void fill_lists(int32_t nK, int32_t n_tiles, const uint8_t *__restric
     }
 }
 
-// ------------------------------------------------------------------ backward (k-tile pair) lists
+// ------------------------------------------------------------ backward (k-tile group) lists
 //
-// The backward's dK/dV pass walks, for every (row, pair of k-tiles 2p and 2p+1), the q-tiles
-// that see either of them, with both classes: the transpose of the per-q-tile lists, read from
-// the same class map.  A missing k-tile 2p+1 (odd tile count) counts as SKIP.
+// The backward's dK/dV pass walks, for every (row, group of kKvGroup k-tiles kKvGroup p ..),
+// called a pair here for short, the q-tiles that see any of them, with every class: the
+// transpose of the per-q-tile lists, read from the same class map.  K-tiles past the row's
+// last (a tile count that is not a multiple of kKvGroup) count as SKIP.
 
-__device__ __forceinline__ void pair_classes(const uint8_t *cm, int32_t nK, int32_t qt, int32_t kt0, uint8_t &ca,
-                                             uint8_t &cb) {
-    ca = cm[int64_t(qt) * nK + kt0];
-    cb = kt0 + 1 < nK ? cm[int64_t(qt) * nK + kt0 + 1] : uint8_t(kTileSkip);
+// Entry of q-tile qt for the group starting at k-tile kt0: qt * 256 + the classes packed two
+// bits each, the group's first k-tile in the highest bits; 0 in the class bits means no entry.
+__device__ __forceinline__ int32_t group_entry(const uint8_t *cm, int32_t nK, int32_t qt, int32_t kt0, bool &on) {
+    static_assert(kKvGroup == 4, "two class bits per k-tile in the low byte");
+    int32_t e = 0;
+    on = false;
+#pragma unroll
+    for (int i = 0; i < kKvGroup; ++i) {
+        const uint8_t c = kt0 + i < nK ? cm[int64_t(qt) * nK + kt0 + i] : uint8_t(kTileSkip);
+        on |= c != kTileSkip;
+        e |= int32_t(c) << (2 * (kKvGroup - 1 - i));
+    }
+    return qt * 256 + e;
 }
 
 // One wave per (row, pair): number of q-tiles that see the pair, to kp_ptr[item + 1].
@@ -312,9 +322,9 @@ __global__ void count_pairs(int32_t nQ, int32_t nK, int32_t nP, int32_t n_items,
     int32_t cnt = 0;
     for (int32_t q0 = 0; q0 < nQ; q0 += 64) {
         const int32_t qt = q0 + lane;
-        uint8_t ca = kTileSkip, cb = kTileSkip;
-        if (qt < nQ) pair_classes(cm, nK, qt, 2 * p, ca, cb);
-        cnt += __popcll(__ballot(ca != kTileSkip || cb != kTileSkip));
+        bool on = false;
+        if (qt < nQ) group_entry(cm, nK, qt, kKvGroup * p, on);
+        cnt += __popcll(__ballot(on));
     }
     if (lane == 0) kp_ptr[item + 1] = cnt;
 }
@@ -371,7 +381,7 @@ __global__ void finish_pairs(int32_t nQ, int32_t n_items, int32_t *__restrict__ 
     }
 }
 
-// One wave per (row, pair): the q-tiles in ascending order, as q-tile*16 + class_a*4 + class_b.
+// One wave per (row, pair): the q-tiles in ascending order, as group_entry values.
 __global__ void fill_pairs(int32_t nQ, int32_t nK, int32_t nP, int32_t n_items, const uint8_t *__restrict__ cmap,
                            const int32_t *__restrict__ kp_ptr, int32_t *__restrict__ kp_list) {
     const int32_t item = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -383,11 +393,11 @@ __global__ void fill_pairs(int32_t nQ, int32_t nK, int32_t nP, int32_t n_items, 
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int32_t q0 = 0; q0 < nQ; q0 += 64) {
         const int32_t qt = q0 + lane;
-        uint8_t ca = kTileSkip, cb = kTileSkip;
-        if (qt < nQ) pair_classes(cm, nK, qt, 2 * p, ca, cb);
-        const bool on = ca != kTileSkip || cb != kTileSkip;
+        bool on = false;
+        int32_t ent = 0;
+        if (qt < nQ) ent = group_entry(cm, nK, qt, kKvGroup * p, on);
         const uint64_t m = __ballot(on);
-        if (on) kp_list[pos + __popcll(m & below)] = qt * 16 + ca * 4 + cb;
+        if (on) kp_list[pos + __popcll(m & below)] = ent;
         pos += __popcll(m);
     }
 }
@@ -414,6 +424,7 @@ __device__ int32_t scan1024(int32_t v, int32_t *buf) {
 // dK/dV workgroup each; n_units[0] = their number (at most max_units: the slices beyond the
 // first belong to granted pairs and so fit in the n_slots pool).
 __global__ __launch_bounds__(1024) void assign_slices(int32_t n_items, int32_t n_slots, int64_t max_units,
+                                                      int32_t slice_entries,
                                                       const int32_t *__restrict__ kp_ptr,
                                                       const int32_t *__restrict__ kwork, int2 *__restrict__ pslot,
                                                       int2 *__restrict__ units, int32_t *__restrict__ n_units) {
@@ -430,7 +441,7 @@ __global__ __launch_bounds__(1024) void assign_slices(int32_t n_items, int32_t n
         int32_t item = -1, sl = 1;
         if (t < n_items) {
             item = kwork[t];
-            sl = bwd_slices(kp_ptr[item + 1] - kp_ptr[item]);
+            sl = bwd_slices(kp_ptr[item + 1] - kp_ptr[item], slice_entries);
         }
         const int32_t want = sl > 1 ? sl : 0;
         const int32_t req = scan1024(want, scan);            // inclusive scan of the requests
@@ -462,7 +473,8 @@ __global__ __launch_bounds__(1024) void assign_slices(int32_t n_items, int32_t n
 
 }  // namespace
 
-hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, const char *ws, char *bws, hipStream_t s) {
+hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, int slice_entries, const char *ws, char *bws,
+                           hipStream_t s) {
     const uint8_t *cmap = reinterpret_cast<const uint8_t *>(ws + w.cmap);
     int32_t *kp_ptr = reinterpret_cast<int32_t *>(bws + b.kp_ptr);
     int32_t *kp_list = reinterpret_cast<int32_t *>(bws + b.kp_list);
@@ -476,7 +488,7 @@ hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, const char *ws
         fill_pairs<<<(n_items + 3) / 4, 256, 0, s>>>(w.nQ, w.nK, b.nP, n_items, cmap, kp_ptr, kp_list);
     }
     // Always: an empty batch still needs n_units = 0 for the dK/dV launch.
-    assign_slices<<<1, 1024, 0, s>>>(n_items, b.n_slots, b.max_units, kp_ptr, kwork,
+    assign_slices<<<1, 1024, 0, s>>>(n_items, b.n_slots, b.max_units, slice_entries, kp_ptr, kwork,
                                      reinterpret_cast<int2 *>(bws + b.pslot), reinterpret_cast<int2 *>(bws + b.units),
                                      reinterpret_cast<int32_t *>(bws + b.n_units));
     return hipGetLastError();

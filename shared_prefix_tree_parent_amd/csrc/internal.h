@@ -64,46 +64,54 @@ inline WsLayout make_layout(int32_t R, int32_t T, int32_t BQ, int32_t BK, int32_
 }
 
 // Backward workspace layout (caller-allocated, filled by tree_attn_bwd_plan / tree_attn_bwd).
-// The dK/dV pass works on pairs of k-tiles (k-tiles 2p and 2p+1, 128 keys).
-// dK/dV query slices: a k-tile pair whose q-tile list has n entries is processed as
-// min(kBwdSlices, max(1, n / kBwdSliceEntries)) workgroups per KV head, each over an equal
+// The dK/dV pass works on groups of kKvGroup consecutive k-tiles (k-tiles 4p .. 4p+3, 256
+// keys), called pairs below for short.
+// dK/dV query slices: a k-tile group whose q-tile list has n entries is processed as
+// min(kBwdSlices, max(1, n / e)) workgroups per KV head (e = kBwdSliceEntries, or
+// kBwdSliceEntriesSmall on a batch too small to fill the device), each over an equal
 // run of the list; when there is more than one, each writes an fp32 partial and a reduce pass
 // adds them in slice order (deterministic).  Partials take slots from a pool of at most
 // kBwdMaxSlots (per KV head), handed out to the longest pairs first; a pair that does not fit
 // runs unsplit.  The plan lists the (pair, slice) units in work order, so the dK/dV launch
 // has one workgroup per unit and KV head (plus a surplus at the end of the grid that exits at
-// once): at most R*nP + min(3*R*nP, kBwdMaxSlots) units, since only granted pairs have more
-// than one slice and their slices fit in the pool.
+// once): at most R*nP + min((kBwdSlices-1)*R*nP, kBwdMaxSlots) units, since only granted
+// pairs have more than one slice and their slices fit in the pool.
+constexpr int kKvGroup = 4;        // k-tiles per dK/dV unit
 constexpr int kBwdSlices = 4;
-constexpr int kBwdSliceEntries = 16;
-constexpr int kBwdMaxSlots = 1024;
-__host__ __device__ inline int bwd_slices(int n) {
-    const int k = n / kBwdSliceEntries;
+constexpr int kBwdSliceEntries = 16;        // list entries per slice ...
+constexpr int kBwdSliceEntriesSmall = 8;    // ... where the batch has fewer (group, KV head)
+                                            // items than twice the device's CUs
+constexpr int kBwdMaxSlots = 512;
+__host__ __device__ inline int bwd_slices(int n, int per) {
+    const int k = n / per;
     return k < 1 ? 1 : (k > kBwdSlices ? kBwdSlices : k);
+}
+inline int bwd_slice_entries(int64_t n_items, int32_t Hkv, int n_cu) {
+    return n_items * Hkv < 2 * int64_t(n_cu) ? kBwdSliceEntriesSmall : kBwdSliceEntries;
 }
 
 struct BwdLayout {
     size_t delta = 0;     // float[R*Hq*T]: rowsum(dO * O) per (row, head, token); 0 at pads
     size_t lse2 = 0;      // float[R*Hq*T]: the forward's LSE times log2(e)
-    size_t kp_ptr = 0;    // int32[R*nP + 1]: CSR over (row, k-tile pair) of the q-tiles that see it
-    size_t kp_list = 0;   // int32[R*nQ*nP]: q-tile*16 + class(2p)*4 + class(2p+1), ascending q-tile
+    size_t kp_ptr = 0;    // int32[R*nP + 1]: CSR over (row, k-tile group) of the q-tiles that see it
+    size_t kp_list = 0;   // int32[R*nQ*nP]: q-tile*256 + sum_i class(4p+i) << 2(3-i), ascending q-tile
     size_t kwork = 0;     // int32[R*nP]: (row, pair) items, longest list first
     size_t khist = 0;     // int32[nQ + 2]
     size_t pslot = 0;     // int2[R*nP]: per pair (query slices, first partial slot)
     size_t units = 0;     // int2[max_units]: (pair item, slice) in work order
     size_t n_units = 0;   // int32[1]: units in use
-    size_t part = 0;      // float[n_slots*Hkv*2*128*D]: per-slice dK^T, dV^T partials
+    size_t part = 0;      // float[n_slots*Hkv*2*(64 kKvGroup)*D]: per-slice dK^T, dV^T partials
     size_t total = 0;
-    int32_t nP = 0;       // k-tile pairs per row: ceil(nK / 2)
+    int32_t nP = 0;       // k-tile groups per row: ceil(nK / kKvGroup)
     int32_t n_slots = 0;  // partial slots: min(R*nP*kBwdSlices, kBwdMaxSlots)
-    int64_t max_units = 0;   // R*nP + min(3*R*nP, kBwdMaxSlots)
+    int64_t max_units = 0;   // R*nP + min((kBwdSlices-1)*R*nP, kBwdMaxSlots)
 };
 
 inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq, int32_t Hkv, int32_t D) {
     BwdLayout b;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    b.nP = (w.nK + 1) / 2;
+    b.nP = (w.nK + kKvGroup - 1) / kKvGroup;
     b.delta = take(size_t(w.R) * Hq * w.T * sizeof(float));
     b.lse2 = take(size_t(w.R) * Hq * w.T * sizeof(float));
     b.kp_ptr = take((size_t(w.R) * b.nP + 1) * sizeof(int32_t));
@@ -114,10 +122,11 @@ inline BwdLayout make_bwd_layout(const WsLayout &w, int32_t Hq, int32_t Hkv, int
     b.n_slots = static_cast<int32_t>(want < kBwdMaxSlots ? want : kBwdMaxSlots);
     b.pslot = take(size_t(w.R) * b.nP * 2 * sizeof(int32_t));
     const int64_t n_items = int64_t(w.R) * b.nP;
-    b.max_units = n_items + (3 * n_items < kBwdMaxSlots ? 3 * n_items : kBwdMaxSlots);
+    const int64_t extra = int64_t(kBwdSlices - 1) * n_items;
+    b.max_units = n_items + (extra < kBwdMaxSlots ? extra : kBwdMaxSlots);
     b.units = take(size_t(b.max_units) * 2 * sizeof(int32_t));
     b.n_units = take(sizeof(int32_t));
-    b.part = take(size_t(b.n_slots) * Hkv * 2 * 128 * D * sizeof(float));
+    b.part = take(size_t(b.n_slots) * Hkv * 2 * (64 * kKvGroup) * D * sizeof(float));
     b.total = off;
     return b;
 }
@@ -181,7 +190,8 @@ hipError_t launch_gdn(const GdnShape &sh, const GdnLayout &L, char *gws, const v
                       hipStream_t s);
 hipError_t launch_rope(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
                        const int32_t *pos_ids, float theta, int32_t inverse, void *q, void *k, hipStream_t s);
-hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, const char *ws, char *bws, hipStream_t s);
+hipError_t launch_bwd_plan(const WsLayout &w, const BwdLayout &b, int slice_entries, const char *ws, char *bws,
+                           hipStream_t s);
 
 struct FwdShape {
     int32_t R, T, Hq, Hkv, D, dtype;

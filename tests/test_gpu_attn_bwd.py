@@ -6,8 +6,8 @@ the launch configuration the benchmark times, dQ at sampled queries and dK / dV 
 keys the oracle computes one by one, plus two identities that hold at any size and cover
 every key of the row: sum_j dV_j = sum_i dO_i over a row's real queries (each softmax row
 sums to one) and sum_j dK_j = 0 (each row of dS sums to zero), per KV head.  The backward's
-per-pair q-tile lists (the transposed tile lists) are compared bit for bit with lists built
-from the oracle's classes.
+per-group q-tile lists (the transposed tile lists, one per four consecutive k-tiles) are
+compared bit for bit with lists built from the oracle's classes.
 Tolerances: tests/gpu_util.py (check_grad); pads exactly zero.
 """
 import numpy as np
@@ -120,7 +120,7 @@ def test_bwd_one_segment_and_singletons():
 
 
 def test_bwd_split_pairs_d64():
-    """A long shared root at D = 64: its k-tile pairs are seen by >= 32 q-tiles, so the dK/dV
+    """A long shared root at D = 64: its k-tile groups are seen by >= 32 q-tiles, so the dK/dV
     pass splits them into query slices whose fp32 partials a reduce pass adds (the slice path
     at the other head size than config 2's)."""
     rng = np.random.default_rng(64)
@@ -133,14 +133,14 @@ def test_bwd_split_pairs_d64():
     inp.real_len = np.array([4140])
     plan = ta.attn_plan(inp)
     BQ, BK = ta.tree_attn_blocks(plan.desc)
-    ptr, _ = _fetch_pairs(plan, (inp.row_len // BK + 1) // 2)
-    assert int(np.diff(ptr).max()) >= 32, "no pair long enough to be split"
+    ptr, _ = _fetch_pairs(plan, _n_groups(inp, BK))
+    assert int(np.diff(ptr).max()) >= 32, "no k-tile group long enough to be split"
     _full_check(inp, "split pairs D64")
 
 
 @pytest.mark.parametrize("T,Hq,Hkv,D", [(576, 8, 2, 128), (320, 4, 1, 64)])
 def test_bwd_odd_ktile_count(T, Hq, Hkv, D):
-    """Rows of an odd number of 64-key tiles: the last k-tile pair has one tile."""
+    """Rows of 9 and 5 64-key tiles: the last k-tile group has one tile."""
     rng = np.random.default_rng(T + D)
     inp = _random_inputs(rng, R=2, T=T, Hq=Hq, Hkv=Hkv, D=D)
     _full_check(inp, f"odd k-tiles T{T} {Hq}/{Hkv} D{D}")
@@ -160,7 +160,7 @@ def test_bwd_empty_middle_row():
 
 
 def test_bwd_all_pad_batch():
-    # Two rows with no segments at all: every k-tile pair has an empty list (one unit each,
+    # Two rows with no segments at all: every k-tile group has an empty list (one unit each,
     # no blocks), and every gradient must be exactly zero, also with NaN in the pad inputs.
     rng = np.random.default_rng(23)
     R, T = 2, 256
@@ -300,20 +300,26 @@ def test_bwd_full_size_configs_sampled(cfg):
 
 # ------------------------------------------------------------------ lists, pads, determinism
 
+KV_GROUP = 4          # k-tiles per dK/dV unit
+
+
+def _n_groups(inp, BK):
+    return inp.n_rows * ((inp.row_len // BK + KV_GROUP - 1) // KV_GROUP)
+
+
 def _want_pairs(inp, BQ, BK):
-    """Per (row, pair of k-tiles 2p, 2p+1): ascending q-tiles that see either, as
-    q-tile*16 + class(2p)*4 + class(2p+1) (a missing k-tile 2p+1 is SKIP), from the oracle's
-    class map."""
+    """Per (row, group of KV_GROUP k-tiles 4p .. 4p+3): ascending q-tiles that see any of
+    them, as q-tile*256 + sum_i class(4p+i) << 2(3-i) (k-tiles past the row's last are SKIP),
+    from the oracle's class map."""
     cmap = M.tile_plan(inp, BQ, BK)["class_map"]                  # [R, nQ, nK]
     R, nQ, nK = cmap.shape
     ptr, lst = [0], []
     for r in range(R):
-        for p in range(0, nK, 2):
+        for p in range(0, nK, KV_GROUP):
             for qt in range(nQ):
-                ca = int(cmap[r, qt, p])
-                cb = int(cmap[r, qt, p + 1]) if p + 1 < nK else M.SKIP
-                if ca != M.SKIP or cb != M.SKIP:
-                    lst.append(qt * 16 + ca * 4 + cb)
+                cls = [int(cmap[r, qt, p + i]) if p + i < nK else M.SKIP for i in range(KV_GROUP)]
+                if any(c != M.SKIP for c in cls):
+                    lst.append(qt * 256 + sum(c << (2 * (KV_GROUP - 1 - i)) for i, c in enumerate(cls)))
             ptr.append(len(lst))
     return np.asarray(ptr, np.int32), np.asarray(lst, np.int32)
 
@@ -347,7 +353,7 @@ def test_bwd_tile_lists_match_oracle(cfg):
     plan = ta.attn_plan(inp)
     BQ, BK = ta.tree_attn_blocks(plan.desc)
     want_ptr, want_list = _want_pairs(inp, BQ, BK)
-    got_ptr, got_list = _fetch_pairs(plan, inp.n_rows * ((inp.row_len // BK + 1) // 2))
+    got_ptr, got_list = _fetch_pairs(plan, _n_groups(inp, BK))
     assert np.array_equal(got_ptr, want_ptr)
     assert np.array_equal(got_list, want_list)
 
@@ -377,9 +383,9 @@ def test_bwd_deterministic():
 
 def test_bwd_slot_pool_overflow():
     # Fourteen causal rows of 4096 tokens with 8 query heads per KV head (32-position q-tiles):
-    # most k-tile pairs ask for 4 query slices, more than the 1024 partial slots in all, so the
-    # pairs past the pool run unsplit.  Two plans built independently must give bit-identical
-    # gradients (which pairs split may not depend on run-to-run ordering), and sampled
+    # most k-tile groups ask for 4 query slices, more than the 512 partial slots in all, so the
+    # groups past the pool run unsplit.  Two plans built independently must give bit-identical
+    # gradients (which groups split may not depend on run-to-run ordering), and sampled
     # positions must match the oracle.
     rng = np.random.default_rng(61)
     R, T, used = 14, 4096, 4000
@@ -390,7 +396,7 @@ def test_bwd_slot_pool_overflow():
         setattr(inp, name, bf16_bits_from_f32(rng.standard_normal((R, T, H, 64), dtype=np.float32)))
     ptr, _ = _want_pairs(inp, 32, 64)
     wants = sum(min(4, n // 16) for n in np.diff(ptr) if n // 16 > 1)
-    assert wants > 1024, wants
+    assert wants > 512, wants
     dO = draw_grad(inp, 61)
     g1, _ = run_bwd(inp, dO)
     g2, _ = run_bwd(inp, dO)
@@ -408,13 +414,18 @@ def test_bwd_fp32_is_unsupported():
     assert e.value.code == ta.TREE_E_UNSUPPORTED and bws_bytes is None
 
 
-def test_bwd_longest_supported_row():
-    # 507,648 tokens (7932 k-tiles; the dK/dV kernel keeps each pair's q-tile list of up to
-    # 3966 entries in LDS).  dQ at sampled queries and dK / dV at keys of the 32-token child
-    # and of the second child's tail, by the oracle's parent walk and descendant sweep (a bit
-    # matrix of this row would take 32 GB); the identities cover every key.
-    inp = longest_row_inputs(seed=43)
-    log(f"backward longest row: {inp.row_len} tokens")
+@pytest.mark.parametrize("hq", [2, 8])
+def test_bwd_longest_supported_row(hq):
+    # 507,648 tokens (7932 k-tiles).  With 2 query heads (128-position q-tiles) a k-tile
+    # group's q-tile list has at most 3966 entries, which the dK/dV kernel stages in LDS at
+    # once; with 8 (32-position q-tiles) it has up to 15,864, more than fit beside the stages
+    # and V rows at head_dim 128, so the unsplit groups of the root (past the slot pool) walk
+    # their lists in several staged passes.  dQ at sampled queries and dK / dV at keys of the
+    # 32-token child and of the second child's tail, by the oracle's parent walk and
+    # descendant sweep (a bit matrix of this row would take 32 GB); the identities cover every
+    # key.
+    inp = longest_row_inputs(seed=43, Hq=hq)
+    log(f"backward longest row: {inp.row_len} tokens, {hq} query heads")
     dO = draw_grad(inp, 43)
     (dq, dk, dv), _ = run_bwd(inp, dO)
     used = int(inp.real_len[0])
