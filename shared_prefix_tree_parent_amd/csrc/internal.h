@@ -80,14 +80,14 @@ constexpr int kKvGroup = 4;        // k-tiles per dK/dV unit
 constexpr int kBwdSlices = 4;
 constexpr int kBwdSliceEntries = 16;        // list entries per slice ...
 constexpr int kBwdSliceEntriesSmall = 8;    // ... where the batch has fewer (group, KV head)
-                                            // items than twice the device's CUs
+                                            // items than the device has CUs
 constexpr int kBwdMaxSlots = 512;
 __host__ __device__ inline int bwd_slices(int n, int per) {
     const int k = n / per;
     return k < 1 ? 1 : (k > kBwdSlices ? kBwdSlices : k);
 }
 inline int bwd_slice_entries(int64_t n_items, int32_t Hkv, int n_cu) {
-    return n_items * Hkv < 2 * int64_t(n_cu) ? kBwdSliceEntriesSmall : kBwdSliceEntries;
+    return n_items * Hkv < int64_t(n_cu) ? kBwdSliceEntriesSmall : kBwdSliceEntries;
 }
 
 struct BwdLayout {
