@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "lane_sum.h"
 #include "tile_ops.h"
 
 namespace treeattn {
@@ -116,8 +117,7 @@ __global__ void row_terms(int32_t R, int32_t T, int32_t Hq, const __bf16 *__rest
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf(float(x[e]), float(y[e]), acc);
     }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+    acc = lanes::group_sum<LPR>(acc);
     if (part == 0) {
         const int64_t idx = (int64_t(r) * Hq + h) * T + i;
         delta[idx] = acc;
@@ -628,13 +628,16 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
         }
 }
 
-// Sum of a split pair's slice partials, in slice order, to bf16 dK (times scale) and dV.  One
-// workgroup per (pair item, KV head), as dkdv_kernel without the slice; unsplit pairs return.
+// Sum of a split group's slice partials, in slice order, to bf16 dK (times scale) and dV.
+// kRedParts workgroups per (group item, KV head), each over an equal part of the group's
+// accumulator elements (a single workgroup per pair left most CUs idle); unsplit groups return.
+constexpr int kRedParts = 4;
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_reduce(BwdArgs a) {
     using TL = Tile<D>;
     if (a.status[0] != 0) return;
-    const int g = blockIdx.x % a.Hkv, item = blockIdx.x / a.Hkv;
+    const int part = blockIdx.x % kRedParts, gi = blockIdx.x / kRedParts;
+    const int g = gi % a.Hkv, item = gi / a.Hkv;
     const int pitem = a.kwork[item];
     const int2 ps = a.pslot[pitem];
     const int n_slices = ps.x;
@@ -644,7 +647,8 @@ __global__ __launch_bounds__(256) void dkdv_reduce(BwdArgs a) {
     constexpr int PER = kKvWaves * TL::NDB * 4 * 64;            // float4 per tensor per slice
     // slot (first + sl) of head g: float4 ((first + sl) Hkv + g) 2 PER, dK then dV
     const float4 *base = reinterpret_cast<const float4 *>(a.part) + (int64_t(ps.y) * a.Hkv + g) * 2 * PER;
-    for (int idx = threadIdx.x; idx < PER; idx += blockDim.x) {
+    static_assert(PER % (kRedParts * 256) == 0, "parts of whole 256-thread rounds");
+    for (int idx = part * (PER / kRedParts) + threadIdx.x; idx < (part + 1) * (PER / kRedParts); idx += blockDim.x) {
         const int lane = idx % 64, i4 = (idx / 64) % 4, db = (idx / 256) % TL::NDB, wave = idx / (256 * TL::NDB);
         float4 sk = base[idx], sv = base[PER + idx];
         for (int sl = 1; sl < n_slices; ++sl) {
@@ -691,7 +695,7 @@ hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, int n
                                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
         if (e != hipSuccess) return e;
         dkdv_kernel<D><<<n_units_k, kKvWaves * 64, smem, s>>>(a);
-        dkdv_reduce<D><<<n_items_k, 256, 0, s>>>(a);
+        dkdv_reduce<D><<<n_items_k * kRedParts, 256, 0, s>>>(a);
     }
     return hipGetLastError();
 }
@@ -733,6 +737,7 @@ hipError_t launch_bwd(const FwdShape &sh, const WsLayout &w, const BwdLayout &b,
     a.c = sh.scale * kLog2e;
     const int64_t n_q = int64_t(sh.R) * w.nQ * a.L;
     const int64_t n_k = int64_t(sh.R) * b.nP * sh.Hkv;
+    if (n_k * kRedParts > INT32_MAX) return hipErrorInvalidValue;
     const int64_t n_u = b.max_units * sh.Hkv;
     if (n_q > INT32_MAX || n_k > INT32_MAX || n_u > INT32_MAX) return hipErrorInvalidValue;
     if (sh.dtype != TREE_DT_BF16) return hipErrorInvalidValue;

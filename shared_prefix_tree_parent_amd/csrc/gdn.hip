@@ -39,6 +39,7 @@
 #include <utility>
 
 #include "internal.h"
+#include "lane_sum.h"
 #include "tile_ops.h"
 
 namespace treeattn {
@@ -65,20 +66,6 @@ constexpr float kGLog2e = 1.4426950408889634f;
 // parent chains of the block are loaded once, all tokens in parallel (lane k of every wave
 // walks token k's chain).
 constexpr int kConvTok = 16;
-
-// Sum over each aligned group of 16 lanes, the result in all 16 (the same value in each: every
-// step adds two operands that commute).
-template <int CTRL>
-__device__ __forceinline__ float dpp_row(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float sum16(float v) {
-    v += dpp_row<0xB1>(v);    // quad_perm [1, 0, 3, 2]: lane ^ 1
-    v += dpp_row<0x4E>(v);    // quad_perm [2, 3, 0, 1]: lane ^ 2
-    v += dpp_row<0x141>(v);   // row_half_mirror: the other quad of the 8-lane half
-    v += dpp_row<0x140>(v);   // row_mirror: the other half of the 16-lane row
-    return v;
-}
 
 __device__ __forceinline__ void conv_row(const __bf16 *x, int r, int C, int c8, float (&f)[8]) {
     if (r < 0) {
@@ -155,7 +142,7 @@ __global__ __launch_bounds__(256) void gdn_conv(int32_t n_tok, int32_t H, const 
                 float ss = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss = fmaf(y[e], y[e], ss);
-                scale = __builtin_amdgcn_rsqf(sum16(ss) + eps) * oscale;
+                scale = __builtin_amdgcn_rsqf(lanes::group_sum<16>(ss) + eps) * oscale;
             }
             if (__builtin_amdgcn_readlane(c0, k) >= -1) {  // pads are never written
                 bf16x8_t o8;
