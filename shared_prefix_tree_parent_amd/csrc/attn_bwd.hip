@@ -398,8 +398,10 @@ __device__ __forceinline__ void kv_block(const char *blk, const LaneOffsets<D> &
     const char *Qt = blk + LD::Q_OFF;
     const char *Ot = blk + LD::DO_OFF;
     // Operand reads run RING reads ahead of their use, from the S / dP products into the dV /
-    // dK ones (whose first operands are read before the softmax).
-    constexpr int NP1 = 3 * TL::NDS, NP2 = 4 * TL::NDB, RING = 4;
+    // dK ones (whose first operands are read before the softmax).  Three: with the stage
+    // offsets as immediates (the block loop runs one stage per unrolled copy) a fourth would
+    // push the kernel past 256 registers.
+    constexpr int NP1 = 3 * TL::NDS, NP2 = 4 * TL::NDB, RING = 3;
     static_assert(NP1 >= RING && NP2 >= RING, "ring deeper than a phase");
     // operand i < NP1: row read of Q (i % 3 == 0, for S), dO (1) and V (2, for dP) at k-step
     // i / 3; NP1 + j: transposed read of dO (j even, for dV) / Q (j odd, for dK),
@@ -560,32 +562,39 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int n = 0; n < LD::AHEAD; ++n)
             if (n < NB) issue(n);
-        for (int n = 0; n < NB; ++n) {
-            // Block n has landed once each copying wave has only the newer blocks' copies (at
-            // most AHEAD - 1 of them) in flight (loads only: they land in order); the barrier
-            // extends that to every wave and also means every wave is done with block n - 1,
-            // whose stage block n + AHEAD takes.
-            if (cw) {
-                const int newer = min(LD::AHEAD - 1, NB - 1 - n);
-                if (wave == LD::CW - 1) {
-                    if (newer >= 2) wait_loads_but<2 * (LD::PERW + 2)>();
-                    else if (newer == 1) wait_loads_but<LD::PERW + 2>();
-                    else wait_loads();
-                } else {
-                    if (newer >= 2) wait_loads_but<2 * LD::PERW>();
-                    else if (newer == 1) wait_loads_but<LD::PERW>();
-                    else wait_loads();
+        // The loop runs NS blocks per iteration, one per stage, so that every stage offset is
+        // a compile-time constant (an instruction immediate of the operand reads).
+        for (int n0 = 0; n0 < NB; n0 += LD::NS) {
+            static_for<LD::NS>([&](auto sc) __attribute__((always_inline)) {
+                constexpr int st = decltype(sc)::value;
+                const int n = n0 + st;
+                if (n >= NB) return;
+                // Block n has landed once each copying wave has only the newer blocks' copies
+                // (at most AHEAD - 1 of them) in flight (loads only: they land in order); the
+                // barrier extends that to every wave and also means every wave is done with
+                // block n - 1, whose stage block n + AHEAD takes.
+                if (cw) {
+                    const int newer = min(LD::AHEAD - 1, NB - 1 - n);
+                    if (wave == LD::CW - 1) {
+                        if (newer >= 2) wait_loads_but<2 * (LD::PERW + 2)>();
+                        else if (newer == 1) wait_loads_but<LD::PERW + 2>();
+                        else wait_loads();
+                    } else {
+                        if (newer >= 2) wait_loads_but<2 * LD::PERW>();
+                        else if (newer == 1) wait_loads_but<LD::PERW>();
+                        else wait_loads();
+                    }
                 }
-            }
-            block_barrier();
-            if (n + LD::AHEAD < NB) issue(n + LD::AHEAD);
-            const int ent = __builtin_amdgcn_readfirstlane(lst[cc.e]);
-            const int q0 = (ent >> 8) * a.BQ + cc.ch * kQBlk;
-            cc.next(a.G, CH);
-            const int cls = (ent >> cls_shift) & 3;
-            if (cls != kTileSkip)
-                kv_block<D>(smem + (n % LD::NS) * LD::BLK, lo, kf, smem + LD::V_OFF + 32 * wave * TL::ROWB, a.c, h,
-                            key, kend_k, q0, cls == kTilePartial, dk, dv);
+                block_barrier();
+                if (n + LD::AHEAD < NB) issue(n + LD::AHEAD);
+                const int ent = __builtin_amdgcn_readfirstlane(lst[cc.e]);
+                const int q0 = (ent >> 8) * a.BQ + cc.ch * kQBlk;
+                cc.next(a.G, CH);
+                const int cls = (ent >> cls_shift) & 3;
+                if (cls != kTileSkip)
+                    kv_block<D>(smem + st * LD::BLK, lo, kf, smem + LD::V_OFF + 32 * wave * TL::ROWB, a.c, h, key,
+                                kend_k, q0, cls == kTilePartial, dk, dv);
+            });
         }
     }
 
