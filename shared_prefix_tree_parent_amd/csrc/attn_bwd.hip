@@ -155,7 +155,7 @@ __device__ __forceinline__ void dq_tile(const char *Kt, const char *Vt, const in
     // Operand reads run RING MFMAs ahead of use, across the softmax and the two 32-key halves.
     // Operand i of half kb = i / PER: r = i % PER < NA a row read of K (even r) or V (odd) for
     // S^T / dP^T; else the transposed K read of dQ^T's MFMA (ks, db) = ((r - NA) / NDB, % NDB).
-    constexpr int NDB = TL::NDB, NA = 2 * TL::NDS, PER = NA + 2 * NDB, TOT = 2 * PER, RING = 4;
+    constexpr int NDB = TL::NDB, NA = 2 * TL::NDS, PER = NA + 2 * NDB, TOT = 2 * PER, RING = 3;
     auto operand = [&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value, kb = i / PER, r = i % PER;
         if constexpr (r < NA) {
@@ -284,28 +284,34 @@ void dq_kernel(BwdArgs a) {
 
     if (N > 0) issue(0);
     if (N > 1) issue(1);
-    for (int t = 0; t < N; ++t) {
-        // Tile t has landed for every wave once each waited for its own copies of t (only
-        // t+1's may still be in flight), and every wave is past tile t-1 before its buffer
-        // slot takes tile t+2.
-        if (t + 1 < N) {
-            // leave tile t+1's copies (the newest) in flight
-            if (wave == LD::CW - 1) wait_loads_but<DqLds<D>::PERW + 1>();
-            else if (wave < LD::CW) wait_loads_but<DqLds<D>::PERW>();
-            else wait_loads();
-        } else {
-            wait_loads();
-        }
-        block_barrier();
-        if (t + 2 < N) issue(t + 2);
-        const int ent = __builtin_amdgcn_readfirstlane(lst[t]);
-        const int kt = ent >> 2;
-        const int slot = t % NB;
-        const char *Kt = smem + LD::K_OFF + slot * LD::TILE;
-        const char *Vt = smem + LD::V_OFF + slot * LD::TILE;
-        const int32_t *KEs = reinterpret_cast<const int32_t *>(smem + LD::KE_OFF + slot * 256) + 4 * h;
-        const int dq_ = qpos - kt * kBK - 4 * h;
-        dq_tile<D>(Kt, Vt, KEs, lo, qf, dof, a.c, lse2, dlt, (ent & 3) == kTilePartial, dq_, qpos, acc);
+    // NB tiles per iteration, one per buffer slot, so that slot offsets are compile-time
+    // constants (instruction immediates of the operand reads).
+    for (int t0 = 0; t0 < N; t0 += NB) {
+        static_for<NB>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int slot = decltype(sc)::value;
+            const int t = t0 + slot;
+            if (t >= N) return;
+            // Tile t has landed for every wave once each waited for its own copies of t (only
+            // t+1's may still be in flight), and every wave is past tile t-1 before its buffer
+            // slot takes tile t+2.
+            if (t + 1 < N) {
+                // leave tile t+1's copies (the newest) in flight
+                if (wave == LD::CW - 1) wait_loads_but<DqLds<D>::PERW + 1>();
+                else if (wave < LD::CW) wait_loads_but<DqLds<D>::PERW>();
+                else wait_loads();
+            } else {
+                wait_loads();
+            }
+            block_barrier();
+            if (t + 2 < N) issue(t + 2);
+            const int ent = __builtin_amdgcn_readfirstlane(lst[t]);
+            const int kt = ent >> 2;
+            const char *Kt = smem + LD::K_OFF + slot * LD::TILE;
+            const char *Vt = smem + LD::V_OFF + slot * LD::TILE;
+            const int32_t *KEs = reinterpret_cast<const int32_t *>(smem + LD::KE_OFF + slot * 256) + 4 * h;
+            const int dq_ = qpos - kt * kBK - 4 * h;
+            dq_tile<D>(Kt, Vt, KEs, lo, qf, dof, a.c, lse2, dlt, (ent & 3) == kTilePartial, dq_, qpos, acc);
+        });
     }
 
     // dQ = scale * (dQ^T)^T; lane holds query qpos, 4 consecutive d per register group.

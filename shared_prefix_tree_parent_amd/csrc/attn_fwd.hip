@@ -616,15 +616,22 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     static_for<kAhead>([&](auto ic) __attribute__((always_inline)) {
         ring[decltype(ic)::value] = load(ic, std::integral_constant<int, 1>{}, koff(0, 0), voff_of(0, 0));
     });
-    for (int t = 0; t < N; ++t) {
-        // Tile t+1 (read from step 2t+1 on) must have landed, and every wave must be done
-        // with tile t-2 (last read in step 2t-2) before its buffer takes tile t+2.
-        if (t + 1 < N) wait_loads();
-        block_barrier();
-        const int ent = __builtin_amdgcn_readfirstlane(lst[t]);
-        if (t + 2 < N) issue(t + 2);
-        step(std::integral_constant<int, 0>{}, t, ent, sA, sB, pA, pB);
-        step(std::integral_constant<int, 1>{}, t, ent, sB, sA, pB, pA);
+    // NB tiles per iteration (t0 a multiple of NB), so that every buffer slot (t & (NB - 1))
+    // is a compile-time constant and the fragment reads take it as an instruction immediate
+    // instead of an address add per read.
+    for (int t0 = 0; t0 < N; t0 += NB) {
+        static_for<NB>([&](auto sc) __attribute__((always_inline)) {
+            const int t = t0 + decltype(sc)::value;
+            if (t >= N) return;
+            // Tile t+1 (read from step 2t+1 on) must have landed, and every wave must be done
+            // with tile t-2 (last read in step 2t-2) before its buffer takes tile t+2.
+            if (t + 1 < N) wait_loads();
+            block_barrier();
+            const int ent = __builtin_amdgcn_readfirstlane(lst[t]);
+            if (t + 2 < N) issue(t + 2);
+            step(std::integral_constant<int, 0>{}, t, ent, sA, sB, pA, pB);
+            step(std::integral_constant<int, 1>{}, t, ent, sB, sA, pB, pA);
+        });
     }
     // Drain: PV of the last step (block 1 of tile N-1, weights pB).
     if (N > 0) {
