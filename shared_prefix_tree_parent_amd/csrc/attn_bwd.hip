@@ -83,7 +83,6 @@ using tile::block_barrier;
 using tile::buf_rsrc;
 using tile::buf_to_lds16;
 using tile::buf_to_lds4;
-using tile::copy_tile;
 using tile::LaneOffsets;
 using tile::lds_base;
 using tile::mfma;
@@ -91,6 +90,19 @@ using tile::static_for;
 using tile::Tile;
 using tile::wait_loads;
 using tile::wait_loads_but;
+
+// A tile copy split over NW waves with the split fixed at compile time: wave w issues the 1 KB
+// block copies w, w + NW, ... (ROWS rows of D bf16 in all), an unrolled run of immediates
+// instead of a loop with a runtime trip count.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void copy_rows(const char *src, int n_valid, int stride, uint32_t dst, int wave,
+                                          int lane) {
+    constexpr int NBLK = ROWS / (1024 / (D * 2));
+    static_assert(NBLK % NW == 0, "the waves must split the tile evenly");
+    const int32x4_t rs = tile::tile_rsrc(src, n_valid, stride);
+#pragma unroll
+    for (int i = 0; i < NBLK / NW; ++i) tile::copy_block<D>(rs, stride, dst, wave + NW * i, lane);
+}
 
 // ------------------------------------------------------------------------------ row_terms
 //
@@ -276,8 +288,8 @@ void dq_kernel(BwdArgs a) {
         const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - kt * kBK, 0), kBK));
         const int64_t tb = int64_t(kt) * kBK * row_stride;
         if (wave < LD::CW) {
-            copy_tile<D>(kbase0 + tb, n_valid, row_stride, lds0 + LD::K_OFF + slot * LD::TILE, kBK, wave, LD::CW, lane);
-            copy_tile<D>(vbase0 + tb, n_valid, row_stride, lds0 + LD::V_OFF + slot * LD::TILE, kBK, wave, LD::CW, lane);
+            copy_rows<D, kBK, LD::CW>(kbase0 + tb, n_valid, row_stride, lds0 + LD::K_OFF + slot * LD::TILE, wave, lane);
+            copy_rows<D, kBK, LD::CW>(vbase0 + tb, n_valid, row_stride, lds0 + LD::V_OFF + slot * LD::TILE, wave, lane);
         }
         if (wave == LD::CW - 1) buf_to_lds4(buf_rsrc(kend_row + kt * kBK, 256), lds0 + LD::KE_OFF + slot * 256, lane * 4);
     };
@@ -536,8 +548,8 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
     if (cw && NL > 0) {
         const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - key0, 0), kKvWaves * 32));
         const int64_t voff = ((int64_t(r) * T + key0) * a.Hkv + g) * D * 2;
-        copy_tile<D>(reinterpret_cast<const char *>(a.v) + voff, n_valid, a.Hkv * D * 2, lds0 + LD::V_OFF,
-                     kKvWaves * 32, wave, LD::CW, lane);
+        copy_rows<D, kKvWaves * 32, LD::CW>(reinterpret_cast<const char *>(a.v) + voff, n_valid, a.Hkv * D * 2,
+                                            lds0 + LD::V_OFF, wave, lane);
     }
     for (int c0 = 0; c0 < NL; c0 += a.lcap) {
         const int nl = min(a.lcap, NL - c0);
@@ -555,10 +567,10 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
             const uint32_t bl = lds0 + (n % LD::NS) * LD::BLK;
             const int n_valid = __builtin_amdgcn_readfirstlane(min(max(n_real - q0, 0), kQBlk));
             const int64_t roff = ((int64_t(r) * T + q0) * a.Hq + head) * D * 2;
-            copy_tile<D>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, bl + LD::Q_OFF, kQBlk, wave,
-                         LD::CW, lane);
-            copy_tile<D>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride, bl + LD::DO_OFF, kQBlk,
-                         wave, LD::CW, lane);
+            copy_rows<D, kQBlk, LD::CW>(reinterpret_cast<const char *>(a.q) + roff, n_valid, q_stride, bl + LD::Q_OFF,
+                                        wave, lane);
+            copy_rows<D, kQBlk, LD::CW>(reinterpret_cast<const char *>(a.dout) + roff, n_valid, q_stride,
+                                        bl + LD::DO_OFF, wave, lane);
             if (wave == LD::CW - 1 && lane < kQBlk) {
                 const int64_t loff = (int64_t(r) * a.Hq + head) * T + q0;
                 buf_to_lds4(buf_rsrc(a.lse2 + loff, uint32_t(n_valid) * 4), bl + LD::LSE_OFF, lane * 4);
