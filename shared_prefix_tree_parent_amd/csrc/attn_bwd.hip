@@ -7,10 +7,10 @@
 //   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q.
 //
 // Three launches on the caller's stream:
-//   * row_terms: D and the forward's LSE in log2 units per (row, head, token), 0 / -inf at pads;
 //   * dq_kernel: one workgroup per forward item (row, q-tile, KV head, chunk of its query
 //     heads), 8 waves of 32 query rows, walking the q-tile's k-tile list with K/V tiles
-//     staged in LDS (direct-to-LDS copies, two tiles ahead);
+//     staged in LDS (direct-to-LDS copies, two tiles ahead); each wave first forms its rows'
+//     D = rowsum(dO * O) and log2-domain LSE and writes them for the dK/dV kernel;
 //   * dkdv_kernel: one workgroup per (row, group of kKvGroup = 4 k-tiles, KV head, query
 //     slice), 8 waves of 32 keys (two per SIMD) whose K fragments stay in registers and whose
 //     V rows stay in LDS, walking the slice's run of the group's list of q-tiles (the
@@ -38,7 +38,6 @@
 #include <type_traits>
 
 #include "internal.h"
-#include "lane_sum.h"
 #include "tile_ops.h"
 
 namespace treeattn {
@@ -102,39 +101,6 @@ __device__ __forceinline__ void copy_rows(const char *src, int n_valid, int stri
     const int32x4_t rs = tile::tile_rsrc(src, n_valid, stride);
 #pragma unroll
     for (int i = 0; i < NBLK / NW; ++i) tile::copy_block<D>(rs, stride, dst, wave + NW * i, lane);
-}
-
-// ------------------------------------------------------------------------------ row_terms
-//
-// D[r, h, i] = sum_d dO[r, i, h, d] * O[r, i, h, d] in fp32 for real tokens, 0 at pads (their
-// dO / O contents are never read), and LSE2[r, h, i] = LSE[r, h, i] * log2(e).  D / 8 lanes
-// per (token, head) row, 16 bytes each, summed across the lanes.
-template <int D>
-__global__ void row_terms(int32_t R, int32_t T, int32_t Hq, const __bf16 *__restrict__ o,
-                          const __bf16 *__restrict__ dout, const float *__restrict__ lse,
-                          const int32_t *__restrict__ n_real, float *__restrict__ delta,
-                          float *__restrict__ lse2) {
-    constexpr int LPR = D / 8;
-    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t row = gid / LPR;                       // (r, i, h) in o's row order
-    const int part = int(gid % LPR);
-    if (row >= int64_t(R) * T * Hq) return;              // whole groups of LPR lanes
-    const int h = int(row % Hq);
-    const int64_t ri = row / Hq;
-    const int r = int(ri / T), i = int(ri % T);
-    float acc = 0.f;
-    if (i < n_real[r]) {
-        const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(o + row * D + part * 8);
-        const bf16x8_t y = *reinterpret_cast<const bf16x8_t *>(dout + row * D + part * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(float(x[e]), float(y[e]), acc);
-    }
-    acc = lanes::group_sum<LPR>(acc);
-    if (part == 0) {
-        const int64_t idx = (int64_t(r) * Hq + h) * T + i;
-        delta[idx] = acc;
-        lse2[idx] = lse[idx] * kLog2e;
-    }
 }
 
 // ------------------------------------------------------------------------------ dq_kernel
@@ -246,25 +212,45 @@ void dq_kernel(BwdArgs a) {
     const bool qreal = qpos < n_real;
 
     // Q and dO fragments of the wave's 32 queries (dO zero at pad queries: its contents never
-    // reach dK / dV / dQ); per-lane log2-domain LSE (+inf at pads so that P = 0) and D.
+    // reach dK / dV / dQ); per-lane log2-domain LSE (+inf at pads so that P = 0) and
+    // D = rowsum(dO * O) in fp32 (0 at pads), both also written to the workspace for the dK/dV
+    // kernel (every (row, position, head) belongs to exactly one dQ work item).
     bf16x8_t qf[TL::NDS], dof[TL::NDS];
+    float dsum = 0.f;
     {
         const int64_t row_off = ((int64_t(r) * T + qpos) * a.Hq + head) * D;
         const bf16x8_t *pq = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.q) + row_off);
         const bf16x8_t *pd = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.dout) + row_off);
+        const bf16x8_t *po = reinterpret_cast<const bf16x8_t *>(reinterpret_cast<const __bf16 *>(a.o) + row_off);
 #pragma unroll
         for (int ds = 0; ds < TL::NDS; ++ds) {
             qf[ds] = pq[2 * ds + h];
             const bf16x8_t x = pd[2 * ds + h];
+            const bf16x8_t ov = po[2 * ds + h];
             bf16x8_t z;
 #pragma unroll
             for (int e = 0; e < 8; ++e) z[e] = qreal ? x[e] : static_cast<__bf16>(0.f);
             dof[ds] = z;
+            static_for<4>([&](auto ec) __attribute__((always_inline)) {
+                constexpr int e = 2 * decltype(ec)::value;
+                dsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, e, e + 1),
+                                                       __builtin_shufflevector(ov, ov, e, e + 1), dsum, false);
+            });
         }
     }
-    const float lse2_raw = a.lse2[(int64_t(r) * a.Hq + head) * T + qpos];
+    const int64_t term = (int64_t(r) * a.Hq + head) * T + qpos;
+    const float lse2_raw = a.lse[term] * kLog2e;
     const float lse2 = (qreal && lse2_raw > -INFINITY) ? lse2_raw : INFINITY;
-    const float dlt = a.delta[(int64_t(r) * a.Hq + head) * T + qpos];
+    {
+        // the two lane halves hold the two halves of each 16-column chunk pair
+        const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(dsum), __float_as_uint(dsum), false, false);
+        dsum = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+    }
+    const float dlt = qreal ? dsum : 0.f;   // a select: pad O / dO contents (even NaN) stay out
+    if (h == 0) {
+        a.delta[term] = dlt;
+        a.lse2[term] = lse2_raw;
+    }
     const LaneOffsets<D> lo(lane);
 
     floatx16 acc[TL::NDB];
@@ -700,12 +686,6 @@ __global__ __launch_bounds__(256) void dkdv_reduce(BwdArgs a) {
 
 template <int D>
 hipError_t launch_d(const BwdArgs &a, int R, int n_items_q, int n_items_k, int n_units_k, hipStream_t s) {
-    const int64_t n_threads = int64_t(R) * a.T * a.Hq * (D / 8);
-    if (n_threads > 0) {
-        row_terms<D><<<int((n_threads + 255) / 256), 256, 0, s>>>(
-            R, a.T, a.Hq, reinterpret_cast<const __bf16 *>(a.o), reinterpret_cast<const __bf16 *>(a.dout), a.lse,
-            a.n_real, a.delta, a.lse2);
-    }
     if (n_items_q > 0) {
         const int smem = DqLds<D>::LIST_OFF + 4 * ((a.nK + 3) & ~3);
         if (smem > kLdsBytes) return hipErrorInvalidValue;
