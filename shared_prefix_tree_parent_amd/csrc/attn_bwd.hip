@@ -62,8 +62,8 @@ struct BwdArgs {
     const uint8_t *kt_kind;
     const int32_t *kp_ptr, *kp_list, *kwork;
     float *part;                   // per-slice dK^T / dV^T partials (BwdLayout::part)
-    const int2 *pslot;             // per pair: (query slices, first partial slot)
-    const int2 *units;             // (pair item, slice) of every dK/dV workgroup, work order
+    const int2 *pslot;             // per k-tile group: (query slices, first partial slot)
+    const int2 *units;             // (group item, slice) of every dK/dV workgroup, work order
     const int32_t *n_units;        // units in use; workgroups past them exit
     const int32_t *kend, *work, *n_real, *status;
     int32_t T, Hq, Hkv, G, HCH, nQ, nK, nP, L, BQ;
@@ -451,7 +451,7 @@ __device__ __forceinline__ void kv_block(const char *blk, const LaneOffsets<D> &
     });
 }
 
-// Position in a pair's sequence of 32-query blocks: list entry, query head of the group,
+// Position in a k-tile group's sequence of 32-query blocks: list entry, query head of the KV group,
 // 32-query chunk of the q-tile.
 struct BlockCursor {
     int e = 0, hd = 0, ch = 0;
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
 
 // Sum of a split group's slice partials, in slice order, to bf16 dK (times scale) and dV.
 // kRedParts workgroups per (group item, KV head), each over an equal part of the group's
-// accumulator elements (a single workgroup per pair left most CUs idle); unsplit groups return.
+// accumulator elements (a single workgroup per group left most CUs idle); unsplit groups return.
 constexpr int kRedParts = 4;
 template <int D>
 __global__ __launch_bounds__(256) void dkdv_reduce(BwdArgs a) {
