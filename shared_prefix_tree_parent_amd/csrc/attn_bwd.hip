@@ -154,7 +154,14 @@ __device__ __forceinline__ void dq_tile(const char *Kt, const char *Vt, const in
     };
     static_for<2>([&](auto kbc) __attribute__((always_inline)) {
         constexpr int kb = decltype(kbc)::value;
-        floatx16 s = zero16(), dp = zero16();
+        // dP^T starts from -D (every element of a lane is its query), so dS = P * that.  The
+        // empty asm keeps the splat inside the loop (hoisted, its 16 registers would stay live
+        // through the whole tile loop).
+        float nd = -dlt;
+        asm volatile("" : "+v"(nd));
+        floatx16 s = zero16(), dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dp[i] = nd;
         static_for<NA>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
             const bf16x8_t op = next(std::integral_constant<int, kb * PER + r>{});
@@ -177,7 +184,7 @@ __device__ __forceinline__ void dq_tile(const char *Kt, const char *Vt, const in
             }
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = s[i] * (dp[i] - dlt);
+        for (int i = 0; i < 16; ++i) s[i] = s[i] * dp[i];
         const bf16x8_t dsf[2] = {acc_frag(s, 0), acc_frag(s, 1)};
         static_for<2 * NDB>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value, ks = j / NDB, db = j % NDB;
@@ -353,14 +360,14 @@ struct KvLds {
 };
 
 // Softmax of one block for a wave's 32 keys: P and dS as bf16 operands (accumulator register
-// order).  Element i is query q0 + 8(i/4) + 4h + i%4 of the block (qh = q0 + 4h).
+// order), dp holding dP - D (its accumulator started from -D).  Element i is query
+// q0 + 8(i/4) + 4h + i%4 of the block (qh = q0 + 4h).
 template <int D>
 __device__ __forceinline__ void kv_softmax(const floatx16 &s, const floatx16 &dp, const char *blk, int h, float c,
                                            bool partial, int key, int kend_k, int qh, bf16x8_t (&pf)[2],
                                            bf16x8_t (&sf)[2]) {
     using LD = KvLds<D>;
     const float *LS = reinterpret_cast<const float *>(blk + LD::LSE_OFF) + 4 * h;
-    const float *DL = reinterpret_cast<const float *>(blk + LD::DL_OFF) + 4 * h;
     floatx16 pm, dsm;
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
@@ -379,12 +386,7 @@ __device__ __forceinline__ void kv_softmax(const floatx16 &s, const floatx16 &dp
             }
     }
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 d4 = *reinterpret_cast<const float4 *>(DL + 8 * i4);
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dsm[4 * i4 + e] = pm[4 * i4 + e] * (dp[4 * i4 + e] - dv4[e]);
-    }
+    for (int i = 0; i < 16; ++i) dsm[i] = pm[i] * dp[i];   // dp holds dP - D
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         pf[ks] = acc_frag(pm, ks);
@@ -423,7 +425,19 @@ __device__ __forceinline__ void kv_block(const char *blk, const LaneOffsets<D> &
     };
     bf16x8_t ring[RING];
     static_for<RING>([&](auto ic) __attribute__((always_inline)) { ring[decltype(ic)::value] = operand(ic); });
-    floatx16 s = zero16(), dp = zero16();
+    // dP starts from -D of each element's query (staged with the block), so dS = P * dP.
+    floatx16 s = zero16(), dp;
+    {
+        const float *DL = reinterpret_cast<const float *>(blk + LD::DL_OFF) + 4 * h;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const float4 d4 = *reinterpret_cast<const float4 *>(DL + 8 * i4);
+            dp[4 * i4 + 0] = -d4.x;
+            dp[4 * i4 + 1] = -d4.y;
+            dp[4 * i4 + 2] = -d4.z;
+            dp[4 * i4 + 3] = -d4.w;
+        }
+    }
     bf16x8_t dof;                            // the k-step's dO operand, until its V operand
     static_for<NP1>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
