@@ -406,7 +406,7 @@ def main() -> int:
                "mfma_flops_per_call": 3.5 * useful,
                "plan_us": round(bwd_plan_ms * 1e3, 2),
                "fwd_plus_bwd_ms": round(fwd_ms + bwd_ms, 4),
-               "calls": "tree_attn_bwd (row terms + dQ kernel + dK/dV kernel); plan once per batch"}
+               "calls": "tree_attn_bwd (dQ kernel with the row terms, dK/dV kernel, dK/dV slice reduce); plan once per batch"}
 
     rope = None
     if not args.no_rope:
