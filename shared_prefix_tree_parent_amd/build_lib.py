@@ -27,9 +27,10 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 HIP_SOURCES = ["classify.hip", "attn_fwd.hip", "attn_bwd.hip", "rope.hip", "gdn.hip", "capi.hip"]
-# Per-source device flags.  The backward keeps every MFMA result in ordinary VGPRs: its
-# dK/dV kernel runs one wave per SIMD, and with the default accumulator-register form the
-# score MFMAs' results are copied back to VGPRs for the softmax (one extra VALU op per value).
+# Per-source device flags.  The backward and the GDN scan keep every MFMA result in ordinary
+# VGPRs: their softmax or decay work reads the score MFMAs' results, and with the default
+# accumulator-register form each result is copied back to a VGPR first (one extra VALU op per
+# value).
 SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "gdn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 CXX_SOURCES = ["plan.cpp"]
 
