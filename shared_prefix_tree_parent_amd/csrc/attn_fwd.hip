@@ -409,7 +409,7 @@ void tree_attn_fwd_kernel(FwdArgs a) {
     static_assert(Tr::NDS == Tr::NDB * Tr::NKS, "S and PV fragments of a step must pair up");
     static_assert(NLOAD >= 8, "the softmax needs at least 8 load slots per step");
     constexpr int EPF = 16 / Tr::NKS;           // accumulator elements per P^T operand
-    constexpr int kAhead = 4;                   // LDS fragment reads issued this many slots early
+    constexpr int kAhead = 8;                   // LDS fragment reads issued this many slots early
     static_assert(NLOAD % kAhead == 0, "the ring carries over steps only when kAhead divides NLOAD");
     floatx16 sA[kNBlk], sB[kNBlk];
     frag pA[kNBlk][Tr::NKS], pB[kNBlk][Tr::NKS];
